@@ -1,0 +1,225 @@
+"""Throughput of the MoE layer forward pass on one MI355X.
+
+One step = one moe_forward over one batch of seeded synthetic input already
+resident in HBM: router GEMM + top-k + gates, histogram/scan/permutation and
+row gather, the two grouped expert GEMMs (and shared expert), and the
+gate-weighted combine.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                    [--no-cpu-baseline] [--copy-calib MiB]
+
+Prints one JSON line.  `value` is tokens/s of the whole layer; `roofline`
+reports the dominant kernel (the first grouped GEMM) against the bf16 MFMA
+peak, timed with HIP events recorded by the library around each of its
+launches inside the timed region; `cpu_baseline` times the CPU oracle on a
+bounded token sample of the same workload.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer tokens/sec + active TFLOP/s (prefill), GB/s (decode) at 1 GPU"
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_F32_TFLOPS = 157.3       # MI355X fp32 matrix
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+
+
+def algorithmic_work(w, counts):
+    """Algorithmic FLOPs and bytes of one forward, and of the first expert GEMM.
+
+    FLOPs: router 2 T d E; per kept routed row n_mat * 2 d d_ff (n_mat = 3 for
+    SwiGLU, 2 otherwise), of which the first GEMM is (n_mat - 1) * 2 d d_ff;
+    shared experts 3 * 2 T d d_ff_s each.  Bytes: x in + y out, the router
+    weights, the weights of every expert that receives a row, shared weights,
+    and 8 bytes of routing output per slot.  Padding rows and the round trips
+    of intermediates are not counted."""
+    b = 2 if w.dtype == "bf16" else 4
+    n_mat = 3 if w.act == "swiglu" else 2
+    kept = int(sum(counts))
+    active = sum(1 for c in counts if c > 0)
+    f_router = 2 * w.T * w.d * w.E
+    f_ffn1 = kept * (n_mat - 1) * 2 * w.d * w.d_ff
+    f_ffn2 = kept * 2 * w.d * w.d_ff
+    f_shared = w.num_shared * 3 * 2 * w.T * w.d * w.d_ff_shared
+    flops = f_router + f_ffn1 + f_ffn2 + f_shared
+    byt = (2 * w.T * w.d * b + w.E * w.d * b + active * n_mat * w.d * w.d_ff * b
+           + w.num_shared * 3 * w.d * w.d_ff_shared * b + 8 * w.T * w.k)
+    ffn1_bytes = active * (n_mat - 1) * w.d * w.d_ff * b + kept * (w.d + w.d_ff) * b
+    return dict(flops=flops, bytes=byt, ffn1_flops=f_ffn1, ffn1_bytes=ffn1_bytes,
+                kept=kept, active=active)
+
+
+def cpu_baseline(w, inp, budget_s=15.0):
+    """Time the CPU oracle (as it stands) on a bounded sample of tokens."""
+    import numpy as np
+    from oracle import moe_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = len(os.sched_getaffinity(0))
+
+    def host(t):
+        return None if t is None else t.float().cpu().numpy()
+
+    x = host(inp["x"])
+    wr = host(inp["w_router"])
+    w1, w2, w3 = host(inp["w1"]), host(inp["w2"]), host(inp["w3"])
+    sh = None
+    if w.num_shared:
+        sh = (host(inp["ws1"]), host(inp["ws3"]), host(inp["ws2"]))
+    off = host(inp["logit_offset"])
+    bias = host(inp["select_bias"])
+
+    def run(n):
+        t0 = time.perf_counter()
+        O.forward(x[:n], wr, w1, w2, w3, k=w.k, act=w.act, gating=w.gating,
+                  capacity_factor=float(np.float32(w.capacity_factor)), logit_offset=off,
+                  select_bias=bias, shared=sh)
+        return time.perf_counter() - t0
+
+    n = min(w.T, 64)
+    dt = run(n)
+    if dt < budget_s / 3 and n < w.T:
+        n = min(w.T, max(n + 1, int(n * budget_s / max(dt, 1e-3))))
+        dt = run(n)
+    return {"value": n / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"first {n} of the {w.T} tokens of {w.name}, numpy float64 oracle "
+                      f"forward (all routed experts touched by them), {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="mixtral_bf16")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calib", type=int, default=0,
+                    help="also run a plain device copy of this many MiB (counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}): the layer is "
+              "built and measured on a single MI355X; multi-GPU sharding is not part of "
+              "this build.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from sparse_mixture_experts_gates_amd import binding as B
+    from sparse_mixture_experts_gates_amd.workloads import WORKLOADS, make_inputs
+
+    w = WORKLOADS[args.workload]
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    inp = make_inputs(w, dev)
+    cfg = B.config_for(w)
+    ws = B.workspace(cfg, w.T, dev)
+    y = torch.empty((w.T, w.d), dtype=w.torch_dtype, device=dev)
+    idx = torch.empty((w.T, w.k), dtype=torch.int32, device=dev)
+    gate = torch.empty((w.T, w.k), dtype=torch.float32, device=dev)
+    counts = torch.empty(w.E, dtype=torch.int32, device=dev)
+    dropped = torch.empty(1, dtype=torch.int32, device=dev)
+
+    def step():
+        B.forward(cfg, inp["x"], inp["w_router"], inp["w1"], inp["w2"], inp["w3"],
+                  logit_offset=inp["logit_offset"], select_bias=inp["select_bias"],
+                  ws1=inp["ws1"], ws3=inp["ws3"], ws2=inp["ws2"], ws=ws, y=y, outputs=False)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    # routing statistics of this batch (for the algorithmic work)
+    B.forward(cfg, inp["x"], inp["w_router"], inp["w1"], inp["w2"], inp["w3"],
+              logit_offset=inp["logit_offset"], select_bias=inp["select_bias"],
+              ws1=inp["ws1"], ws3=inp["ws3"], ws2=inp["ws2"], ws=ws, y=y)
+    _, _, _, cnt, drp = B.forward_inputs(cfg, inp, ws=ws)
+    torch.cuda.synchronize()
+    cnt = cnt.cpu().tolist()
+    if w.capacity_factor > 0:
+        C = B.capacity(cfg, w.T)
+        kept_counts = [min(c, C) for c in cnt]
+    else:
+        kept_counts = cnt
+    work = algorithmic_work(w, kept_counts)
+
+    if args.copy_calib:
+        n = args.copy_calib * (1 << 20) // 4
+        a = torch.ones(n, dtype=torch.float32, device=dev)
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
+
+    B.profile_enable(True)
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(args.steps):
+        step()
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / args.steps
+    prof = B.profile_read()
+    B.profile_enable(False)
+
+    kern = {k: v[0] / max(v[1], 1) for k, v in prof.items()}
+    dom = "ffn1"
+    dom_ms = kern.get(dom, float("nan"))
+    peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
+    decode = w.T * w.k <= B.DECODE_MAX_ROWS
+    if decode:   # small batch: the expert GEMMs stream the active experts' weights
+        roof = {"kernel": dom, "bound": "hbm",
+                "achieved": work["ffn1_bytes"] / (dom_ms * 1e-3) / 1e9, "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "algorithmic_bytes_per_launch": work["ffn1_bytes"]}
+    else:
+        roof = {"kernel": dom, "bound": "mfma",
+                "achieved": work["ffn1_flops"] / (dom_ms * 1e-3) / 1e12, "peak": peak,
+                "unit": "TFLOP/s", "algorithmic_flops_per_launch": work["ffn1_flops"]}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = None
+    roof["avg_ms"] = dom_ms
+    tflops = work["flops"] / (ms * 1e-3) / 1e12
+    gbs = work["bytes"] / (ms * 1e-3) / 1e9
+    res = {
+        "metric": METRIC,
+        "value": w.T / (ms * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "T": w.T, "d": w.d, "E": w.E, "k": w.k,
+                   "d_ff": w.d_ff, "act": w.act, "gating": w.gating,
+                   "capacity_factor": w.capacity_factor, "num_shared": w.num_shared,
+                   "d_ff_shared": w.d_ff_shared, "parallelism": "none (1 GPU)"},
+        "active_tflops": tflops,
+        "active_tflops_frac_of_peak": tflops / peak,
+        "algorithmic_gbs": gbs,
+        "algorithmic_gbs_frac_of_hbm": gbs / PEAK_HBM_GBS,
+        "routing": {"kept_rows": work["kept"], "active_experts": work["active"],
+                    "dropped": int(drp.item())},
+        "kernels_ms": {k: round(v, 5) for k, v in sorted(kern.items())},
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(w, inp)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

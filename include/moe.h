@@ -1,0 +1,243 @@
+/*
+ * moe.h -- C ABI of libmoe_mi355x.so: the forward pass of a sparse
+ * mixture-of-experts feed-forward layer on AMD Instinct MI355X (gfx950).
+ *
+ * The layer (sources: "Mixture of experts", Inside the Model guide ch. 14,
+ * section "The computation", equation block; "Mixture of Experts", LLM
+ * tutorial ch. 11, sections "The mathematics" and "The routing decision"):
+ *
+ *     s   = W_r x (+ o)                    router scores, one per expert
+ *     S   = TopK(q, k),  q = a(s) + b      ordered top-k of the selection key
+ *     g_i = normalize(s)_i, i in S         gates over the kept experts
+ *     y   = sum_{i in S, kept} g_i Expert_i(x)  +  sum_shared Shared_j(x)
+ *
+ * with an optional Switch-style expert capacity (LLM tutorial ch. 11,
+ * "Expert capacity and dropped tokens"): a slot beyond its expert's capacity
+ * is dropped and contributes 0, so the token's residual carries it.  y is the
+ * MoE branch only; the caller adds the residual.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - All tensors are dense, row-major, contiguous, in device memory unless
+ *   stated otherwise, and 16-byte aligned.  "dtype" is cfg->dtype (fp32 or
+ *   bf16) and applies to x, all weights, y and the intermediate activations.
+ *   Scores, offsets, biases and gates are fp32; indices and counts are int32.
+ * - Weight layouts follow the pages' expert arrays ("Mixture of Experts", LLM
+ *   tutorial ch. 11, "The mathematics", numpy forward pass):
+ *     w_router [E, d];  w1, w3 [E, d_ff, d];  w2 [E, d, d_ff];
+ *     ws1, ws3 [S, d_ff_shared, d];  ws2 [S, d, d_ff_shared]
+ *   (S = cfg->num_shared).  Expert e computes
+ *     relu/gelu:  w2[e] . act(w1[e] . x)
+ *     swiglu:     w2[e] . (silu(w1[e] . x) * (w3[e] . x))
+ *   with no biases anywhere.
+ * - The caller owns every buffer.  The library never allocates device memory;
+ *   calls that need scratch space take a caller-provided workspace whose size
+ *   moe_workspace_size() returns.
+ * - Every call enqueues work on `stream` (a hipStream_t; NULL = the legacy
+ *   default stream) and returns without synchronising.  Errors detected on
+ *   the host are returned before anything is enqueued; a fault inside a kernel
+ *   surfaces at the caller's next synchronisation, as usual for HIP.
+ * - T = 0 is valid: the call validates cfg and enqueues nothing; pointer
+ *   arguments are not inspected (empty tensors may have NULL data).
+ * - Results are deterministic: no floating-point atomics; the same inputs give
+ *   the same bits on every run.
+ * - The library never prints and never aborts.
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* element types (cfg->dtype) */
+#define MOE_F32  0
+#define MOE_BF16 1
+
+/* expert nonlinearity (cfg->act).  GeLU is the exact erf form. */
+#define MOE_ACT_RELU   0
+#define MOE_ACT_GELU   1
+#define MOE_ACT_SWIGLU 2
+
+/* gating (cfg->gating)
+ *  SOFTMAX_TOPK : key q = s (+ b); gates = softmax over the k kept scores
+ *                 ("Mixture of Experts", LLM tutorial ch. 11, "The routing
+ *                 decision").
+ *  SIGMOID_TOPK : key q = sigmoid(s) (+ b); gates = sigmoid(s_i) divided by
+ *                 the sum over the kept experts ("Mixture of experts", Inside
+ *                 the Model ch. 14, "The computation" and "Auxiliary-loss-free
+ *                 balancing"; the bias b picks experts only).
+ *  SOFTMAX_FULL : key q = s (+ b); gate = the full-softmax probability of each
+ *                 kept expert (the Switch top-1 variant, LLM tutorial ch. 11,
+ *                 "Top-1 vs top-2"). */
+#define MOE_GATE_SOFTMAX_TOPK 0
+#define MOE_GATE_SIGMOID_TOPK 1
+#define MOE_GATE_SOFTMAX_FULL 2
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = 1,  /* null required pointer, misaligned pointer,
+                               k < 1, k > E, T < 0, bad enum value        */
+  MOE_ERR_UNSUPPORTED = 2,  /* valid but not built: see moe_config_t       */
+  MOE_ERR_WORKSPACE = 3,    /* ws_bytes below moe_workspace_size()         */
+  MOE_ERR_HIP = 4           /* a HIP runtime call or launch failed         */
+} moe_status_t;
+
+/* Problem statement ("Mixture of experts", Inside the Model ch. 14, "The
+ * computation": d, E, k; "Fine-grained and shared experts"; LLM tutorial
+ * ch. 11, "Expert capacity and dropped tokens": capacity factor).
+ *
+ * Supported: 1 <= k <= E <= 256, k <= 16; d and d_ff (and d_ff_shared when
+ * num_shared > 0) positive multiples of 64 for bf16, of 4 for fp32;
+ * num_shared in [0, 8], shared experts are SwiGLU and need dtype bf16 or fp32
+ * like the rest.  Enum fields are int32 so the struct has one layout in every
+ * language (40 bytes, no padding). */
+typedef struct moe_config {
+  int32_t d;                /* model width                                  */
+  int32_t num_experts;      /* E, routed experts                            */
+  int32_t top_k;            /* k, experts per token                         */
+  int32_t d_ff;             /* hidden width of a routed expert              */
+  int32_t act;              /* MOE_ACT_*                                    */
+  int32_t gating;           /* MOE_GATE_*                                   */
+  int32_t dtype;            /* MOE_F32 | MOE_BF16                           */
+  float   capacity_factor;  /* rho; <= 0 means no capacity limit            */
+  int32_t num_shared;       /* always-on shared SwiGLU experts (0 = none)   */
+  int32_t d_ff_shared;      /* their hidden width                           */
+} moe_config_t;
+
+/* Human-readable name of a status code (static storage; never NULL). */
+const char* moe_status_str(moe_status_t status);
+
+/* Validate cfg for T tokens without touching the GPU. */
+moe_status_t moe_check_config(const moe_config_t* cfg, int64_t T);
+
+/* Bytes of workspace moe_forward() needs for T tokens; the same amount
+ * suffices for moe_permute() and moe_expert_ffn().  Host only. */
+moe_status_t moe_workspace_size(const moe_config_t* cfg, int64_t T,
+                                size_t* bytes);
+
+/* Expert capacity C = floor(((rho * k) * T) / E), computed in IEEE double
+ * from the float rho ("Mixture of experts", Inside the Model ch. 14,
+ * "Auxiliary loss": tokens per batch / N x capacity factor; "Mixture of
+ * Experts", LLM tutorial ch. 11, Exercise 4 truncates it to an integer; with
+ * k slots per token the fair share is k T / E).  *capacity = -1 when rho <= 0
+ * (no limit).  Host only. */
+moe_status_t moe_capacity(const moe_config_t* cfg, int64_t T,
+                          int64_t* capacity);
+
+/* Router and gating ("Mixture of experts", Inside the Model ch. 14, "The
+ * computation"; LLM tutorial ch. 11, "The routing decision" and "Training
+ * instability": router math in FP32).
+ *   x            [T, d]     dtype
+ *   w_router     [E, d]     dtype
+ *   logit_offset [E] fp32 or NULL: added to every token's score (it enters
+ *                both the selection and the gates)
+ *   select_bias  [E] fp32 or NULL: added to the selection key only
+ *   logits       [T, E] fp32 out, or NULL: s = x . w_router^T (+ offset),
+ *                products exact, fp32 accumulation
+ *   topk_idx     [T, k] int32 out: experts in descending key order, ties to
+ *                the lower index, -0.0 == +0.0
+ *   topk_gate    [T, k] fp32 out: gates in the same order
+ * One fused kernel: MFMA score GEMM, then per-token top-k with wavefront
+ * shuffles and the gates, from the scores held in LDS. */
+moe_status_t moe_route(const moe_config_t* cfg, int64_t T, const void* x,
+                       const void* w_router, const float* logit_offset,
+                       const float* select_bias, float* logits,
+                       int32_t* topk_idx, float* topk_gate, void* stream);
+
+/* Capacity, histogram, scan and the stable permutation (LLM tutorial ch. 11,
+ * "Expert capacity and dropped tokens" and Exercise 4; "Chapter 33 -- Mixture
+ * of Experts (MoE)", "Simple MoE Layer Implementation": rows grouped per
+ * expert, replacing its per-expert mask loop with one gather).
+ *   topk_idx       [T, k] int32 in (from moe_route)
+ *   x              [T, d] dtype in; may be NULL when x_perm is NULL
+ *   expert_counts  [E] int32 out or NULL: slots per expert before capacity
+ *   expert_offsets [E+1] int32 out: exclusive scan of kept = min(count, C)
+ *   perm_src       [T*k] int32 out: flat slot t*k+j of permuted row p for
+ *                  p < expert_offsets[E]; -1 for the rows after that.  Rows of
+ *                  one expert are in ascending token order; experts ascend.
+ *   slot_pos       [T*k] int32 out: permuted row of slot t*k+j, -1 = dropped.
+ *                  Slots are kept first-come in token order.
+ *   num_dropped    [1] int32 out or NULL: sum_e max(0, count_e - C)
+ *   x_perm         [T*k, d] dtype out or NULL: x_perm[p] = x[perm_src[p]/k];
+ *                  rows past expert_offsets[E] are left untouched
+ *   workspace      device scratch of ws_bytes >= moe_workspace_size() */
+moe_status_t moe_permute(const moe_config_t* cfg, int64_t T,
+                         const int32_t* topk_idx, const void* x,
+                         int32_t* expert_counts, int32_t* expert_offsets,
+                         int32_t* perm_src, int32_t* slot_pos,
+                         int32_t* num_dropped, void* x_perm, void* workspace,
+                         size_t ws_bytes, void* stream);
+
+/* The experts on their routed rows, and the shared experts on all tokens
+ * ("Mixture of experts", Inside the Model ch. 14, "The computation": each
+ * expert a gated MLP, only the selected ones run; "Fine-grained and shared
+ * experts"; LLM tutorial ch. 11, "The mathematics").
+ *   x              [T, d] dtype, read only by the shared experts (NULL if none)
+ *   x_perm         [T*k, d] dtype: rows grouped per expert (moe_permute)
+ *   expert_offsets [E+1] int32 (device): rows of expert e are
+ *                  [expert_offsets[e], expert_offsets[e+1])
+ *   w1, w3, w2     routed expert weights (w3 only for SwiGLU, else NULL)
+ *   ws1, ws3, ws2  shared expert weights, or NULL when num_shared == 0
+ *   expert_out     [T*k, d] dtype out: Expert_e(x_perm[p]) for the kept rows
+ *   shared_out     [S, T, d] dtype out (NULL when num_shared == 0)
+ * Ragged grouped GEMMs on bf16 MFMA with fp32 accumulation and a fused
+ * activation / SwiGLU epilogue; the hidden activations are rounded to dtype.
+ * When T*k <= MOE_DECODE_MAX_ROWS a small-batch variant is used that reads
+ * each active expert's weights once and skips idle experts. */
+#define MOE_DECODE_MAX_ROWS 64
+moe_status_t moe_expert_ffn(const moe_config_t* cfg, int64_t T,
+                            const void* x, const void* x_perm,
+                            const int32_t* expert_offsets, const void* w1,
+                            const void* w3, const void* w2, const void* ws1,
+                            const void* ws3, const void* ws2, void* expert_out,
+                            void* shared_out, void* workspace,
+                            size_t ws_bytes, void* stream);
+
+/* Gate-weighted sum ("Mixture of experts", Inside the Model ch. 14, "The
+ * computation": y = sum g_i Expert_i(x); "Mixture-of-Experts", Neural
+ * Networks Visually ch. 15, "Show the math": unselected experts add exactly
+ * zero).  For each token, in slot order j = 0..k-1 and then shared expert
+ * s = 0..S-1, in fp32, rounded once to dtype:
+ *   y[t] = sum_{j: slot_pos[t*k+j] >= 0} topk_gate[t,j] * expert_out[slot_pos]
+ *          + sum_s shared_out[s, t]
+ * Dropped slots add 0 and the remaining gates are not renormalised.
+ *   shared_out may be NULL (then nothing is added). */
+moe_status_t moe_combine(const moe_config_t* cfg, int64_t T,
+                         const void* expert_out, const int32_t* slot_pos,
+                         const float* topk_gate, const void* shared_out,
+                         void* y, void* stream);
+
+/* The whole layer: moe_route, moe_permute, moe_expert_ffn, moe_combine.
+ *   y [T, d] dtype out.  topk_idx [T,k], topk_gate [T,k], expert_counts [E]
+ *   and num_dropped [1] are optional outputs (NULL = keep them in the
+ *   workspace).  The other arguments are as above. */
+moe_status_t moe_forward(const moe_config_t* cfg, int64_t T, const void* x,
+                         const void* w_router, const float* logit_offset,
+                         const float* select_bias, const void* w1,
+                         const void* w3, const void* w2, const void* ws1,
+                         const void* ws3, const void* ws2, void* y,
+                         int32_t* topk_idx, float* topk_gate,
+                         int32_t* expert_counts, int32_t* num_dropped,
+                         void* workspace, size_t ws_bytes, void* stream);
+
+/* Per-kernel timing with HIP events, for measurement tools.
+ * moe_profile_enable(1) clears the record and brackets every later launch by
+ * this library with a pair of events on the launch's stream;
+ * moe_profile_enable(0) stops recording.  moe_profile_read() waits for the
+ * recorded events and reports, per kernel name (at most max_names of them),
+ * the total elapsed milliseconds and the number of launches; it returns the
+ * number of names written, or -1 on a HIP error.  names[i] point to static
+ * strings.  Not meant for use from several threads at once. */
+moe_status_t moe_profile_enable(int32_t on);
+int32_t moe_profile_read(const char** names, double* total_ms,
+                         int32_t* launches, int32_t max_names);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_MI355X_H */

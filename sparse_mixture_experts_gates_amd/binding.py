@@ -1,0 +1,237 @@
+"""ctypes binding of libmoe_mi355x.so (C ABI in include/moe.h).
+
+Argument marshalling only: torch tensors (device memory) are checked and
+turned into pointers, outputs are allocated with torch.empty, and each call
+enqueues on torch's current HIP stream.  Every step of the layer runs in the
+library's HIP kernels.  If the library has not been built, the first call
+raises -- there is no fallback.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmoe_mi355x.so")
+
+MOE_F32, MOE_BF16 = 0, 1
+ACTS = {"relu": 0, "gelu": 1, "swiglu": 2}
+GATINGS = {"softmax_topk": 0, "sigmoid_topk": 1, "softmax_full": 2}
+DECODE_MAX_ROWS = 64
+STATUS = {0: "MOE_OK", 1: "MOE_ERR_INVALID_ARG", 2: "MOE_ERR_UNSUPPORTED",
+          3: "MOE_ERR_WORKSPACE", 4: "MOE_ERR_HIP"}
+
+EXPORTS = ("moe_status_str", "moe_check_config", "moe_workspace_size", "moe_capacity",
+           "moe_route", "moe_permute", "moe_expert_ffn", "moe_combine", "moe_forward",
+           "moe_profile_enable", "moe_profile_read")
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status, where):
+        self.status = status
+        super().__init__(f"{where}: {STATUS.get(status, status)}")
+
+
+class MoeConfig(ctypes.Structure):
+    _fields_ = [("d", ctypes.c_int32), ("num_experts", ctypes.c_int32),
+                ("top_k", ctypes.c_int32), ("d_ff", ctypes.c_int32),
+                ("act", ctypes.c_int32), ("gating", ctypes.c_int32),
+                ("dtype", ctypes.c_int32), ("capacity_factor", ctypes.c_float),
+                ("num_shared", ctypes.c_int32), ("d_ff_shared", ctypes.c_int32)]
+
+
+_lib_handle = None
+_vp, _i64, _sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t
+_cfgp = ctypes.POINTER(MoeConfig)
+
+
+def lib():
+    """Load the library (once).  Raises if it is missing."""
+    global _lib_handle
+    if _lib_handle is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it with "
+                "`python -m sparse_mixture_experts_gates_amd.build` (there is no fallback)")
+        L = ctypes.CDLL(LIB_PATH)
+        L.moe_status_str.restype = ctypes.c_char_p
+        L.moe_status_str.argtypes = [ctypes.c_int]
+        L.moe_check_config.argtypes = [_cfgp, _i64]
+        L.moe_workspace_size.argtypes = [_cfgp, _i64, ctypes.POINTER(_sz)]
+        L.moe_capacity.argtypes = [_cfgp, _i64, ctypes.POINTER(_i64)]
+        L.moe_route.argtypes = [_cfgp, _i64] + [_vp] * 7 + [_vp]
+        L.moe_permute.argtypes = [_cfgp, _i64] + [_vp] * 9 + [_sz, _vp]
+        L.moe_expert_ffn.argtypes = [_cfgp, _i64] + [_vp] * 12 + [_sz, _vp]
+        L.moe_combine.argtypes = [_cfgp, _i64] + [_vp] * 5 + [_vp]
+        L.moe_forward.argtypes = [_cfgp, _i64] + [_vp] * 16 + [_sz, _vp]
+        L.moe_profile_enable.argtypes = [ctypes.c_int32]
+        L.moe_profile_read.restype = ctypes.c_int32
+        L.moe_profile_read.argtypes = [ctypes.POINTER(ctypes.c_char_p),
+                                       ctypes.POINTER(ctypes.c_double),
+                                       ctypes.POINTER(ctypes.c_int32), ctypes.c_int32]
+        for fn in ("moe_check_config", "moe_workspace_size", "moe_capacity", "moe_route",
+                   "moe_permute", "moe_expert_ffn", "moe_combine", "moe_forward",
+                   "moe_profile_enable"):
+            getattr(L, fn).restype = ctypes.c_int
+        _lib_handle = L
+    return _lib_handle
+
+
+def config(d, num_experts, top_k, d_ff, act="swiglu", gating="softmax_topk",
+           dtype="bf16", capacity_factor=0.0, num_shared=0, d_ff_shared=0):
+    return MoeConfig(d, num_experts, top_k, d_ff, ACTS[act], GATINGS[gating],
+                     MOE_BF16 if dtype == "bf16" else MOE_F32, float(capacity_factor),
+                     num_shared, d_ff_shared)
+
+
+def config_for(w, T=None):
+    """MoeConfig of a workloads.Workload."""
+    return config(w.d, w.E, w.k, w.d_ff, w.act, w.gating, w.dtype, w.capacity_factor,
+                  w.num_shared, w.d_ff_shared)
+
+
+def _check(st, where):
+    if st != 0:
+        raise MoeError(st, where)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensor must be in device memory")
+    if not t.is_contiguous():
+        raise ValueError("tensor must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _dt(cfg):
+    return torch.bfloat16 if cfg.dtype == MOE_BF16 else torch.float32
+
+
+def check_config(cfg, T):
+    return lib().moe_check_config(ctypes.byref(cfg), T)
+
+
+def workspace_size(cfg, T):
+    n = _sz(0)
+    _check(lib().moe_workspace_size(ctypes.byref(cfg), T, ctypes.byref(n)), "moe_workspace_size")
+    return n.value
+
+
+def capacity(cfg, T):
+    c = _i64(0)
+    _check(lib().moe_capacity(ctypes.byref(cfg), T, ctypes.byref(c)), "moe_capacity")
+    return c.value
+
+
+def workspace(cfg, T, device="cuda"):
+    return torch.empty(max(workspace_size(cfg, T), 256), dtype=torch.uint8, device=device)
+
+
+def route(cfg, x, w_router, logit_offset=None, select_bias=None, want_logits=False):
+    T = x.shape[0]
+    k, E = cfg.top_k, cfg.num_experts
+    idx = torch.empty((T, k), dtype=torch.int32, device=x.device)
+    gate = torch.empty((T, k), dtype=torch.float32, device=x.device)
+    logits = torch.empty((T, E), dtype=torch.float32, device=x.device) if want_logits else None
+    _check(lib().moe_route(ctypes.byref(cfg), T, _ptr(x), _ptr(w_router), _ptr(logit_offset),
+                           _ptr(select_bias), _ptr(logits), _ptr(idx), _ptr(gate), _stream()),
+           "moe_route")
+    return idx, gate, logits
+
+
+def permute(cfg, topk_idx, x=None, gather=True, ws=None):
+    T = topk_idx.shape[0]
+    k, E, dev = cfg.top_k, cfg.num_experts, topk_idx.device
+    out = dict(
+        expert_counts=torch.empty(E, dtype=torch.int32, device=dev),
+        expert_offsets=torch.empty(E + 1, dtype=torch.int32, device=dev),
+        perm_src=torch.empty(T * k, dtype=torch.int32, device=dev),
+        slot_pos=torch.empty(T * k, dtype=torch.int32, device=dev),
+        num_dropped=torch.empty(1, dtype=torch.int32, device=dev),
+        x_perm=(torch.empty((T * k, cfg.d), dtype=_dt(cfg), device=dev) if gather else None))
+    if ws is None:
+        ws = workspace(cfg, T, dev)
+    _check(lib().moe_permute(ctypes.byref(cfg), T, _ptr(topk_idx), _ptr(x),
+                             _ptr(out["expert_counts"]), _ptr(out["expert_offsets"]),
+                             _ptr(out["perm_src"]), _ptr(out["slot_pos"]),
+                             _ptr(out["num_dropped"]), _ptr(out["x_perm"]), _ptr(ws),
+                             ws.numel(), _stream()), "moe_permute")
+    return out
+
+
+def expert_ffn(cfg, T, x_perm, expert_offsets, w1, w2, w3=None, x=None, ws1=None, ws3=None,
+               ws2=None, ws=None):
+    dev = x_perm.device
+    eout = torch.empty((T * cfg.top_k, cfg.d), dtype=_dt(cfg), device=dev)
+    sout = (torch.empty((cfg.num_shared, T, cfg.d), dtype=_dt(cfg), device=dev)
+            if cfg.num_shared > 0 else None)
+    if ws is None:
+        ws = workspace(cfg, T, dev)
+    _check(lib().moe_expert_ffn(ctypes.byref(cfg), T, _ptr(x), _ptr(x_perm), _ptr(expert_offsets),
+                                _ptr(w1), _ptr(w3), _ptr(w2), _ptr(ws1), _ptr(ws3), _ptr(ws2),
+                                _ptr(eout), _ptr(sout), _ptr(ws), ws.numel(), _stream()),
+           "moe_expert_ffn")
+    return eout, sout
+
+
+def combine(cfg, T, expert_out, slot_pos, topk_gate, shared_out=None):
+    y = torch.empty((T, cfg.d), dtype=_dt(cfg), device=expert_out.device)
+    _check(lib().moe_combine(ctypes.byref(cfg), T, _ptr(expert_out), _ptr(slot_pos),
+                             _ptr(topk_gate), _ptr(shared_out), _ptr(y), _stream()),
+           "moe_combine")
+    return y
+
+
+def forward(cfg, x, w_router, w1, w2, w3=None, *, logit_offset=None, select_bias=None,
+            ws1=None, ws3=None, ws2=None, ws=None, y=None, outputs=True):
+    """The whole layer.  Returns (y, topk_idx, topk_gate, expert_counts,
+    num_dropped); the last four are None when outputs=False."""
+    T = x.shape[0]
+    dev = x.device
+    if y is None:
+        y = torch.empty((T, cfg.d), dtype=_dt(cfg), device=dev)
+    idx = gate = counts = dropped = None
+    if outputs:
+        idx = torch.empty((T, cfg.top_k), dtype=torch.int32, device=dev)
+        gate = torch.empty((T, cfg.top_k), dtype=torch.float32, device=dev)
+        counts = torch.empty(cfg.num_experts, dtype=torch.int32, device=dev)
+        dropped = torch.empty(1, dtype=torch.int32, device=dev)
+    if ws is None:
+        ws = workspace(cfg, T, dev)
+    _check(lib().moe_forward(ctypes.byref(cfg), T, _ptr(x), _ptr(w_router), _ptr(logit_offset),
+                             _ptr(select_bias), _ptr(w1), _ptr(w3), _ptr(w2), _ptr(ws1),
+                             _ptr(ws3), _ptr(ws2), _ptr(y), _ptr(idx), _ptr(gate),
+                             _ptr(counts), _ptr(dropped), _ptr(ws), ws.numel(), _stream()),
+           "moe_forward")
+    return y, idx, gate, counts, dropped
+
+
+def forward_inputs(cfg, inp, **kw):
+    """forward() on a dict from workloads.make_inputs."""
+    return forward(cfg, inp["x"], inp["w_router"], inp["w1"], inp["w2"], inp.get("w3"),
+                   logit_offset=inp.get("logit_offset"), select_bias=inp.get("select_bias"),
+                   ws1=inp.get("ws1"), ws3=inp.get("ws3"), ws2=inp.get("ws2"), **kw)
+
+
+def profile_enable(on=True):
+    _check(lib().moe_profile_enable(1 if on else 0), "moe_profile_enable")
+
+
+def profile_read(max_names=64):
+    names = (ctypes.c_char_p * max_names)()
+    ms = (ctypes.c_double * max_names)()
+    cnt = (ctypes.c_int32 * max_names)()
+    n = lib().moe_profile_read(names, ms, cnt, max_names)
+    if n < 0:
+        raise MoeError(4, "moe_profile_read")
+    return {names[i].decode(): (ms[i], cnt[i]) for i in range(n)}

@@ -1,0 +1,54 @@
+// Shared device helpers for the MI355X (gfx950) kernels: bf16 bit handling,
+// MFMA operand types, sortable float keys and the internal launcher API.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/moe.h"
+
+namespace moe {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+// bf16 is carried as its 16-bit pattern in memory.
+__device__ __forceinline__ float bf16_to_f32(uint32_t h16) {
+  return __uint_as_float(h16 << 16);
+}
+
+// float -> bf16, round to nearest even; NaN stays NaN (quiet), Inf stays Inf.
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7f800000u) == 0x7f800000u)
+    return (u >> 16) | ((u & 0xffffu) ? 0x40u : 0u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
+}
+
+// Order-preserving map of a float to uint32 (larger float -> larger key).
+// -0.0 is folded into +0.0 first.
+__device__ __forceinline__ uint32_t sortable_key(float f) {
+  uint32_t u = __float_as_uint(f + 0.0f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ float sigmoidf_(float z) {
+  return 1.0f / (1.0f + expf(-z));
+}
+
+// Wavefront-wide shuffle of 64-bit values (wave64).
+__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int mask) {
+  uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);
+  lo = __shfl_xor(lo, mask, 64);
+  hi = __shfl_xor(hi, mask, 64);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+__host__ __device__ constexpr int cdiv(int a, int b) { return (a + b - 1) / b; }
+
+}  // namespace moe

@@ -1,0 +1,416 @@
+// Expert FFN: ragged grouped GEMMs over per-expert row segments.
+//
+// Each selected expert runs on the rows routed to it and nowhere else
+// ("Mixture of experts", Inside the Model ch. 14, "The computation": only the
+// selected experts run; LLM tutorial ch. 11, "The mathematics": FLOPs scale
+// with k).  An expert is W2 . act(W1 . x) or the SwiGLU gated MLP
+// W2 . (silu(W1 . x) * (W3 . x)) (LLM tutorial ch. 11, "Modern MoE variants",
+// gate W1 / up W3 / down W2), computed as two passes:
+//   pass 1: H = act(X_e . W1_e^T)  or  silu(X_e . W1_e^T) * (X_e . W3_e^T)
+//   pass 2: Y = H_e . W2_e^T
+//
+// A pass is a device-built tile plan plus one GEMM launch.  The plan kernel
+// turns the segment offsets into (segment, row range, column tile) entries,
+// expert-major, then column tile, then row tile, so the tiles that share a
+// weight slab are adjacent; the GEMM remaps block ids so that adjacent plan
+// entries land on the same XCD (blocks are dealt round-robin over the 8 XCDs),
+// which keeps each shared slab in one L2.  No host synchronisation: the grid
+// is sized for the worst case and surplus blocks return at once.
+//
+// bf16 GEMM: XOR-swizzled LDS tiles of 64-wide K slabs, double-buffered
+// through registers; v_mfma_f32_16x16x32_bf16 with weights on the MFMA row
+// side, so each lane ends with 4 adjacent output columns of one row (8-byte
+// stores).  SwiGLU interleaves W1 and W3 rows inside every wave's slab so the
+// gate and up accumulators of a column sit in the same lane and the epilogue
+// is elementwise.  The fp32 variant is a plain LDS-tiled FMA GEMM.
+#include "common.h"
+#include "launch.h"
+
+namespace moe {
+
+namespace {
+
+constexpr int MODE_PLAIN = 0, MODE_RELU = 1, MODE_GELU = 2, MODE_SWIGLU = 3;
+constexpr int BK = 64;
+
+struct PlanEntry {
+  int32_t g, m0, m1, nt;
+};
+
+struct KArgs {
+  const uint16_t* A;   // or float*
+  const uint16_t* W;
+  const uint16_t* Wu;
+  uint16_t* C;
+  const PlanEntry* plan;
+  const int32_t* count;
+  int K, N;
+  int64_t a_seg_rows, c_seg_rows;  // extra row offset per segment (shared experts)
+};
+
+// Plan: one workgroup; G <= 1024 segments.
+__global__ __launch_bounds__(1024) void ffn_plan_kernel(
+    const int32_t* __restrict__ seg, int G, int64_t dense_rows, int BM, int NT,
+    PlanEntry* __restrict__ plan, int32_t* __restrict__ count) {
+  __shared__ int mt[1024];
+  __shared__ int start[1024];
+  __shared__ int rows_s[1024];
+  __shared__ int base[1025];
+  const int tid = threadIdx.x;
+  for (int g = tid; g < G; g += 1024) {
+    const int r0 = seg ? seg[g] : 0;
+    const int r1 = seg ? seg[g + 1] : (int)dense_rows;
+    start[g] = r0;
+    rows_s[g] = r1 - r0;
+    mt[g] = (r1 - r0 + BM - 1) / BM;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    int acc = 0;
+    for (int g = 0; g < G; ++g) {
+      base[g] = acc;
+      acc += mt[g] * NT;
+    }
+    base[G] = acc;
+  }
+  __syncthreads();
+  const int V = base[G];
+  for (int L = tid; L < V; L += 1024) {
+    int lo = 0, hi = G - 1;  // last g with base[g] <= L
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (base[mid] <= L) lo = mid; else hi = mid - 1;
+    }
+    const int g = lo, rem = L - base[g], m = mt[g];
+    const int nt = rem / m, mi = rem - nt * m;
+    const int m0 = start[g] + mi * BM;
+    int m1 = m0 + BM;
+    if (m1 > start[g] + rows_s[g]) m1 = start[g] + rows_s[g];
+    plan[L] = PlanEntry{g, m0, m1, nt};
+  }
+  if (tid == 0) count[0] = V;
+}
+
+__device__ __forceinline__ int swz(int row, int chunk) {
+  return row * BK + ((chunk ^ (row & 7)) << 3);
+}
+
+// XCD-aware order: physical block P runs on XCD P % 8; give each XCD a
+// contiguous run of the V valid plan entries.
+__device__ __forceinline__ int xcd_remap(int P, int V) {
+  const int x = P & 7, i = P >> 3, q = V >> 3, r = V & 7;
+  return (x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q) + i;
+}
+
+__device__ __forceinline__ float gelu_erf(float z) {
+  return 0.5f * z * (1.0f + erff(z * 0.70710678118654752f));
+}
+__device__ __forceinline__ float silu_f(float z) { return z / (1.0f + __expf(-z)); }
+
+template <int MODE>
+__device__ __forceinline__ float act1(float v) {
+  if (MODE == MODE_RELU) return v > 0.f ? v : 0.f;
+  if (MODE == MODE_GELU) return gelu_erf(v);
+  return v;
+}
+
+template <int BM, int BN, int WM, int WN, int MODE>
+__global__ __launch_bounds__(64 * WM * WN) void ffn_bf16_kernel(KArgs a) {
+  constexpr int NTH = 64 * WM * WN;
+  constexpr int BMW = BM / WM, BNW = BN / WN;   // wave tile (tokens, weight rows)
+  constexpr int TM = BMW / 16, TN = BNW / 16;
+  constexpr int HALF = BNW / 2;                  // SwiGLU: gate rows per wave
+  constexpr int BNOUT = MODE == MODE_SWIGLU ? BN / 2 : BN;
+  constexpr int CHUNKS = (BM + BN) * 8;
+  constexpr int CPT = (CHUNKS + NTH - 1) / NTH;
+  constexpr int SA = BM * BK, SB = BN * BK;      // bf16 elements per stage
+  static_assert(MODE != MODE_SWIGLU || TN % 2 == 0, "SwiGLU needs paired tiles");
+
+  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * (SA + SB)];
+
+  const int V = a.count[0];
+  const int P = blockIdx.x;
+  if (P >= V) return;
+  const PlanEntry pe = a.plan[xcd_remap(P, V)];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / WN, wn = wave % WN;
+  const int K = a.K, N = a.N;
+  const int n0 = pe.nt * BNOUT;
+  const int64_t arow0 = (int64_t)pe.g * a.a_seg_rows;
+  const int64_t wbase = (int64_t)pe.g * N * K;
+
+  // per-thread copy slots: (global source, LDS destination)
+  const uint16_t* src[CPT];
+  int dst[CPT];
+#pragma unroll
+  for (int i = 0; i < CPT; ++i) {
+    const int c = tid + i * NTH;
+    dst[i] = -1;
+    src[i] = a.A;
+    if (c < CHUNKS) {
+      const int row = c >> 3, ch = c & 7;
+      if (row < BM) {
+        int r = pe.m0 + row;
+        if (r > pe.m1 - 1) r = pe.m1 - 1;
+        src[i] = a.A + (arow0 + r) * K + ch * 8;
+        dst[i] = swz(row, ch);
+      } else {
+        const int rho = row - BM;
+        int n;
+        const uint16_t* Wm = a.W;
+        if (MODE == MODE_SWIGLU) {
+          const int wq = rho / BNW, wi = rho - wq * BNW;
+          n = n0 + wq * HALF + (wi < HALF ? wi : wi - HALF);
+          if (wi >= HALF) Wm = a.Wu;
+        } else {
+          n = n0 + rho;
+        }
+        if (n > N - 1) n = N - 1;
+        src[i] = Wm + wbase + (int64_t)n * K + ch * 8;
+        dst[i] = SA + swz(rho, ch);
+      }
+    }
+  }
+  uint4 stg[CPT];
+  auto gload = [&](int k0) {
+#pragma unroll
+    for (int i = 0; i < CPT; ++i)
+      if (dst[i] >= 0) stg[i] = *reinterpret_cast<const uint4*>(src[i] + k0);
+  };
+  auto lstore = [&](int buf) {
+    uint16_t* b = smem + buf * (SA + SB);
+#pragma unroll
+    for (int i = 0; i < CPT; ++i)
+      if (dst[i] >= 0) *reinterpret_cast<uint4*>(b + dst[i]) = stg[i];
+  };
+
+  f32x4_t acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  const int nk = K / BK;
+  gload(0);
+  lstore(0);
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    const int buf = kt & 1;
+    if (kt + 1 < nk) gload((kt + 1) * BK);
+    const uint16_t* sa = smem + buf * (SA + SB);
+    const uint16_t* sb = sa + SA;
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      const int ch = kk * 4 + (lane >> 4);
+      bf16x8_t fw[TN];
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+        fw[j] = *reinterpret_cast<const bf16x8_t*>(sb + swz(wn * BNW + j * 16 + (lane & 15), ch));
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        const bf16x8_t fx =
+            *reinterpret_cast<const bf16x8_t*>(sa + swz(wm * BMW + i * 16 + (lane & 15), ch));
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fw[j], fx, acc[i][j], 0, 0, 0);
+      }
+    }
+    if (kt + 1 < nk) lstore(buf ^ 1);
+    __syncthreads();
+  }
+
+  // epilogue: lane holds columns 4*(lane/16)+r of tile j, row lane%16 of tile i
+  const int64_t crow0 = (int64_t)pe.g * a.c_seg_rows;
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+    const int r = pe.m0 + wm * BMW + i * 16 + (lane & 15);
+    if (r >= pe.m1) continue;
+    uint16_t* crow = a.C + (crow0 + r) * (int64_t)N;
+    constexpr int JOUT = MODE == MODE_SWIGLU ? TN / 2 : TN;
+#pragma unroll
+    for (int j = 0; j < JOUT; ++j) {
+      float v[4];
+      int col;
+      if (MODE == MODE_SWIGLU) {
+        col = n0 + wn * HALF + j * 16 + 4 * (lane >> 4);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) v[q] = silu_f(acc[i][j][q]) * acc[i][j + TN / 2][q];
+      } else {
+        col = n0 + wn * BNW + j * 16 + 4 * (lane >> 4);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) v[q] = act1<MODE>(acc[i][j][q]);
+      }
+      if (col + 3 < N) {
+        uint2 pk;
+        pk.x = pack_bf16x2(v[0], v[1]);
+        pk.y = pack_bf16x2(v[2], v[3]);
+        *reinterpret_cast<uint2*>(crow + col) = pk;
+      } else {
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          if (col + q < N) crow[col + q] = (uint16_t)f32_to_bf16(v[q]);
+      }
+    }
+  }
+}
+
+// fp32: 64 x 64 output tile, 16-deep K slabs, 4 x 4 outputs per thread
+// (x 2 accumulators for SwiGLU).
+template <int MODE>
+__global__ __launch_bounds__(256) void ffn_f32_kernel(KArgs a) {
+  constexpr int TB = 64, KS = 16, LDT = TB + 4;
+  __shared__ float As[KS][LDT];
+  __shared__ float Ws[KS][LDT];
+  __shared__ float Us[KS][LDT];
+  const int V = a.count[0];
+  const int P = blockIdx.x;
+  if (P >= V) return;
+  const PlanEntry pe = a.plan[P];
+  const float* A = reinterpret_cast<const float*>(a.A);
+  const float* W = reinterpret_cast<const float*>(a.W);
+  const float* Wu = reinterpret_cast<const float*>(a.Wu);
+  float* C = reinterpret_cast<float*>(a.C);
+  const int K = a.K, N = a.N;
+  const int n0 = pe.nt * TB;
+  const int64_t arow0 = (int64_t)pe.g * a.a_seg_rows;
+  const int64_t wbase = (int64_t)pe.g * N * K;
+  const int tid = threadIdx.x, tr = tid >> 4, tc = tid & 15;
+  float acc[4][4], accu[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = accu[i][j] = 0.f;
+  for (int k0 = 0; k0 < K; k0 += KS) {
+#pragma unroll
+    for (int l = 0; l < 4; ++l) {
+      const int idx = tid + l * 256, row = idx >> 4, kk = idx & 15;
+      const bool kin = k0 + kk < K;
+      int r = pe.m0 + row;
+      if (r > pe.m1 - 1) r = pe.m1 - 1;
+      As[kk][row] = kin ? A[(arow0 + r) * K + k0 + kk] : 0.f;
+      int n = n0 + row;
+      if (n > N - 1) n = N - 1;
+      Ws[kk][row] = kin ? W[wbase + (int64_t)n * K + k0 + kk] : 0.f;
+      if (MODE == MODE_SWIGLU) Us[kk][row] = kin ? Wu[wbase + (int64_t)n * K + k0 + kk] : 0.f;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) {
+      float av[4], wv[4], uv[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) av[i] = As[kk][tr * 4 + i];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) wv[j] = Ws[kk][tc * 4 + j];
+      if (MODE == MODE_SWIGLU) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) uv[j] = Us[kk][tc * 4 + j];
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          acc[i][j] = fmaf(av[i], wv[j], acc[i][j]);
+          if (MODE == MODE_SWIGLU) accu[i][j] = fmaf(av[i], uv[j], accu[i][j]);
+        }
+    }
+    __syncthreads();
+  }
+  const int64_t crow0 = (int64_t)pe.g * a.c_seg_rows;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = pe.m0 + tr * 4 + i;
+    if (r >= pe.m1) continue;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int col = n0 + tc * 4 + j;
+      if (col >= N) continue;
+      float v;
+      if (MODE == MODE_SWIGLU) {
+        const float z = acc[i][j];
+        v = z / (1.0f + expf(-z)) * accu[i][j];
+      } else {
+        v = act1<MODE>(acc[i][j]);
+      }
+      C[(crow0 + r) * N + col] = v;
+    }
+  }
+}
+
+struct Shape {
+  int BM, BNOUT;
+};
+
+Shape pick_shape(int dtype, bool small, int mode) {
+  if (dtype == MOE_F32) return {64, 64};
+  if (small) return {16, mode == MODE_SWIGLU ? 64 : 128};
+  return {256, mode == MODE_SWIGLU ? 128 : 256};
+}
+
+int64_t max_entries(int64_t max_rows, int G, int N, Shape sh) {
+  const int64_t nt = (N + sh.BNOUT - 1) / sh.BNOUT;
+  return ((max_rows + sh.BM - 1) / sh.BM + G) * nt;
+}
+
+template <int BM, int BN, int WM, int WN>
+void launch_bf16(int mode, unsigned grid, const KArgs& k, hipStream_t s) {
+  switch (mode) {
+    case MODE_PLAIN: ffn_bf16_kernel<BM, BN, WM, WN, MODE_PLAIN><<<grid, 64 * WM * WN, 0, s>>>(k); break;
+    case MODE_RELU: ffn_bf16_kernel<BM, BN, WM, WN, MODE_RELU><<<grid, 64 * WM * WN, 0, s>>>(k); break;
+    case MODE_GELU: ffn_bf16_kernel<BM, BN, WM, WN, MODE_GELU><<<grid, 64 * WM * WN, 0, s>>>(k); break;
+    default: ffn_bf16_kernel<BM, BN, WM, WN, MODE_SWIGLU><<<grid, 64 * WM * WN, 0, s>>>(k); break;
+  }
+}
+
+}  // namespace
+
+size_t ffn_plan_bytes(int64_t max_rows, int G, int N, bool small, int dtype) {
+  size_t best = 0;
+  for (int mode = 0; mode < 4; ++mode) {
+    const size_t b = 16 + 16 * (size_t)max_entries(max_rows, G, N, pick_shape(dtype, small, mode));
+    if (b > best) best = b;
+  }
+  return best;
+}
+
+hipError_t launch_ffn_pass(const FfnPassArgs& p, hipStream_t s) {
+  const Shape sh = pick_shape(p.dtype, p.small, p.mode);
+  const int NT = (p.N + sh.BNOUT - 1) / sh.BNOUT;
+  const int64_t grid = max_entries(p.max_rows, p.G, p.N, sh);
+  if (grid == 0) return hipSuccess;
+  int32_t* count = static_cast<int32_t*>(p.plan);
+  PlanEntry* plan = reinterpret_cast<PlanEntry*>(static_cast<char*>(p.plan) + 16);
+  const char* nm1 = p.seg_offsets ? "ffn_plan" : "ffn_plan_shared";
+  prof_before(nm1, s);
+  ffn_plan_kernel<<<1, 1024, 0, s>>>(p.seg_offsets, p.G, p.dense_rows, sh.BM, NT, plan, count);
+  prof_after(s);
+  KArgs k;
+  k.A = static_cast<const uint16_t*>(p.A);
+  k.W = static_cast<const uint16_t*>(p.w);
+  k.Wu = static_cast<const uint16_t*>(p.w_up ? p.w_up : p.w);
+  k.C = static_cast<uint16_t*>(p.C);
+  k.plan = plan;
+  k.count = count;
+  k.K = p.K;
+  k.N = p.N;
+  k.a_seg_rows = p.a_seg_rows;
+  k.c_seg_rows = p.c_seg_rows;
+  const char* nm = p.seg_offsets ? (p.mode == MODE_PLAIN ? "ffn2" : "ffn1")
+                                 : (p.mode == MODE_PLAIN ? "ffn2_shared" : "ffn1_shared");
+  prof_before(nm, s);
+  if (p.dtype == MOE_F32) {
+    switch (p.mode) {
+      case MODE_PLAIN: ffn_f32_kernel<MODE_PLAIN><<<(unsigned)grid, 256, 0, s>>>(k); break;
+      case MODE_RELU: ffn_f32_kernel<MODE_RELU><<<(unsigned)grid, 256, 0, s>>>(k); break;
+      case MODE_GELU: ffn_f32_kernel<MODE_GELU><<<(unsigned)grid, 256, 0, s>>>(k); break;
+      default: ffn_f32_kernel<MODE_SWIGLU><<<(unsigned)grid, 256, 0, s>>>(k); break;
+    }
+  } else if (p.small) {
+    launch_bf16<16, 128, 1, 4>(p.mode, (unsigned)grid, k, s);
+  } else {
+    launch_bf16<256, 256, 2, 4>(p.mode, (unsigned)grid, k, s);
+  }
+  prof_after(s);
+  return hipGetLastError();
+}
+
+}  // namespace moe

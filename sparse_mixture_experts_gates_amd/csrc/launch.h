@@ -1,0 +1,79 @@
+// Internal launcher API between the C-ABI host code (moe_api.hip) and the
+// kernel files.  Every launcher enqueues on `stream` and returns the result of
+// hipGetLastError() after its launches.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+// Named-kernel launch bracket for the optional event profiler (moe_api.hip).
+void prof_before(const char* name, hipStream_t s);
+void prof_after(hipStream_t s);
+
+struct RouteArgs {
+  const void* x;
+  const void* w;
+  const float* offset;  // [E] or null
+  const float* bias;    // [E] or null
+  float* logits;        // [T, E] or null
+  int32_t* topk_idx;    // [T, k]
+  float* topk_gate;     // [T, k]
+  int64_t T;
+  int d, E, k, gating, dtype;
+};
+hipError_t launch_route(const RouteArgs& a, hipStream_t s);
+
+struct PermuteArgs {
+  const int32_t* topk_idx;  // [T*k]
+  const void* x;            // [T, d] (may be null when x_perm is null)
+  int32_t* counts;          // [E] or null
+  int32_t* offsets;         // [E+1]
+  int32_t* perm_src;        // [T*k]
+  int32_t* slot_pos;        // [T*k]
+  int32_t* num_dropped;     // [1] or null
+  void* x_perm;             // [T*k, d] or null
+  int32_t* block_counts;    // workspace [nblocks * E]
+  int32_t* kept_total;      // workspace [1]: expert_offsets[E] copy for the gather
+  int64_t T;
+  int k, E, d, dtype;
+  int64_t capacity;         // < 0: unlimited
+};
+int permute_nblocks(int64_t rows);
+hipError_t launch_permute(const PermuteArgs& a, hipStream_t s);
+
+// One grouped GEMM pass over ragged row segments:
+//   C[r, n] = epilogue( sum_k A[r, k] * W_seg[n, k] )  for r in the segment.
+// mode: 0 = plain, 1 = relu, 2 = gelu, 3 = swiglu (W1 = w, W3 = w_up).
+struct FfnPassArgs {
+  const void* A;          // [rows, K] dtype
+  const void* w;          // [G, N_w, K] dtype (gate / only matrix)
+  const void* w_up;       // [G, N_w, K] dtype (SwiGLU up) or null
+  void* C;                // [rows, N] dtype
+  const int32_t* seg_offsets;  // [G+1] device row offsets, or null = one dense segment
+  int64_t dense_rows;     // rows when seg_offsets is null
+  int G;                  // number of segments (experts)
+  int K, N;               // N = output columns (d_ff for GEMM1, d for GEMM2)
+  int mode, dtype;
+  int64_t a_seg_rows;     // row offset of segment g in A is g * a_seg_rows (dense segments)
+  int64_t c_seg_rows;     // row offset of segment g in C is g * c_seg_rows
+  void* plan;             // workspace for the tile plan
+  int64_t max_rows;       // upper bound of rows over all segments (host)
+  bool small;             // small-batch (decode) tile shape
+};
+size_t ffn_plan_bytes(int64_t max_rows, int G, int N, bool small, int dtype);
+hipError_t launch_ffn_pass(const FfnPassArgs& a, hipStream_t s);
+
+struct CombineArgs {
+  const void* expert_out;   // [T*k, d]
+  const int32_t* slot_pos;  // [T*k]
+  const float* gate;        // [T*k]
+  const void* shared_out;   // [S, T, d] or null
+  void* y;                  // [T, d]
+  int64_t T;
+  int k, d, S, dtype;
+};
+hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
+
+}  // namespace moe

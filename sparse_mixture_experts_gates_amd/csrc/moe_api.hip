@@ -1,0 +1,472 @@
+// C ABI of libmoe_mi355x.so (declared in include/moe.h): argument validation,
+// capacity, workspace carving and the launch sequence of the forward pass.
+// All device work is enqueued on the caller's stream; nothing here
+// synchronises except moe_profile_read().
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "common.h"
+#include "launch.h"
+
+namespace moe {
+
+// ---------------------------------------------------------------- profiling
+namespace {
+struct ProfRec {
+  const char* name;
+  hipEvent_t e0, e1;
+};
+std::mutex g_prof_mu;
+bool g_prof_on = false;
+std::vector<ProfRec> g_prof_recs;
+std::vector<hipEvent_t> g_prof_pool;
+
+hipEvent_t prof_event() {
+  if (!g_prof_pool.empty()) {
+    hipEvent_t e = g_prof_pool.back();
+    g_prof_pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+}  // namespace
+
+void prof_before(const char* name, hipStream_t s) {
+  if (!g_prof_on) return;
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  ProfRec r{name, prof_event(), prof_event()};
+  if (!r.e0 || !r.e1) return;
+  hipEventRecord(r.e0, s);
+  g_prof_recs.push_back(r);
+}
+
+void prof_after(hipStream_t s) {
+  if (!g_prof_on) return;
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  if (!g_prof_recs.empty()) hipEventRecord(g_prof_recs.back().e1, s);
+}
+
+}  // namespace moe
+
+using namespace moe;
+
+namespace {
+
+constexpr size_t ALIGN = 256;
+size_t up(size_t v) { return (v + ALIGN - 1) / ALIGN * ALIGN; }
+
+bool al(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+size_t esize(const moe_config_t* c) { return c->dtype == MOE_BF16 ? 2 : 4; }
+
+moe_status_t check_cfg(const moe_config_t* c, int64_t T) {
+  if (!c || T < 0) return MOE_ERR_INVALID_ARG;
+  if (c->d <= 0 || c->num_experts < 1 || c->top_k < 1 || c->top_k > c->num_experts ||
+      c->d_ff <= 0 || c->num_shared < 0)
+    return MOE_ERR_INVALID_ARG;
+  if (c->act < MOE_ACT_RELU || c->act > MOE_ACT_SWIGLU) return MOE_ERR_INVALID_ARG;
+  if (c->gating < MOE_GATE_SOFTMAX_TOPK || c->gating > MOE_GATE_SOFTMAX_FULL)
+    return MOE_ERR_INVALID_ARG;
+  if (c->dtype != MOE_F32 && c->dtype != MOE_BF16) return MOE_ERR_INVALID_ARG;
+  if (isnan(c->capacity_factor)) return MOE_ERR_INVALID_ARG;
+  if (c->num_shared > 0 && c->d_ff_shared <= 0) return MOE_ERR_INVALID_ARG;
+  if (c->num_experts > 256 || c->top_k > 16 || c->num_shared > 8) return MOE_ERR_UNSUPPORTED;
+  const int q = c->dtype == MOE_BF16 ? 64 : 4;
+  if (c->d % q || c->d_ff % q || (c->num_shared > 0 && c->d_ff_shared % q))
+    return MOE_ERR_UNSUPPORTED;
+  if (T * (int64_t)c->top_k > (int64_t)1 << 30) return MOE_ERR_UNSUPPORTED;
+  if (c->num_shared > 0 && T * (int64_t)c->num_shared > (int64_t)1 << 30) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+int64_t capacity_of(const moe_config_t* c, int64_t T) {
+  const double rho = (double)c->capacity_factor;
+  if (!(rho > 0.0)) return -1;
+  return (int64_t)floor(((rho * (double)c->top_k) * (double)T) / (double)c->num_experts);
+}
+
+bool small_batch(int64_t rows) { return rows <= MOE_DECODE_MAX_ROWS; }
+
+struct PermWs {
+  size_t block_counts, kept_total, total;
+};
+PermWs perm_ws(const moe_config_t* c, int64_t T) {
+  PermWs w;
+  size_t o = 0;
+  w.block_counts = o;
+  o += up((size_t)permute_nblocks(T * c->top_k) * c->num_experts * 4);
+  w.kept_total = o;
+  o += up(4);
+  w.total = o;
+  return w;
+}
+
+struct FfnWs {
+  size_t H, Hs, plan, total;
+};
+FfnWs ffn_ws(const moe_config_t* c, int64_t T) {
+  FfnWs w;
+  const int64_t R = T * c->top_k;
+  const int S = c->num_shared;
+  size_t o = 0;
+  w.H = o;
+  o += up((size_t)R * c->d_ff * esize(c));
+  w.Hs = o;
+  o += up((size_t)S * T * (S ? c->d_ff_shared : 0) * esize(c));
+  size_t pb = ffn_plan_bytes(R, c->num_experts, c->d_ff, small_batch(R), c->dtype);
+  size_t p2 = ffn_plan_bytes(R, c->num_experts, c->d, small_batch(R), c->dtype);
+  if (p2 > pb) pb = p2;
+  if (S) {
+    const size_t p3 = ffn_plan_bytes((int64_t)S * T, S, c->d_ff_shared, small_batch(T), c->dtype);
+    const size_t p4 = ffn_plan_bytes((int64_t)S * T, S, c->d, small_batch(T), c->dtype);
+    if (p3 > pb) pb = p3;
+    if (p4 > pb) pb = p4;
+  }
+  w.plan = o;
+  o += up(pb);
+  w.total = o;
+  return w;
+}
+
+struct FwdWs {
+  size_t idx, gate, counts, dropped, offsets, perm_src, slot_pos, x_perm, eout, sout, perm, ffn,
+      total;
+};
+FwdWs fwd_ws(const moe_config_t* c, int64_t T) {
+  FwdWs w;
+  const int64_t R = T * c->top_k;
+  size_t o = 0;
+  w.idx = o; o += up((size_t)R * 4);
+  w.gate = o; o += up((size_t)R * 4);
+  w.counts = o; o += up((size_t)c->num_experts * 4);
+  w.dropped = o; o += up(4);
+  w.offsets = o; o += up((size_t)(c->num_experts + 1) * 4);
+  w.perm_src = o; o += up((size_t)R * 4);
+  w.slot_pos = o; o += up((size_t)R * 4);
+  w.x_perm = o; o += up((size_t)R * c->d * esize(c));
+  w.eout = o; o += up((size_t)R * c->d * esize(c));
+  w.sout = o; o += up((size_t)c->num_shared * T * c->d * esize(c));
+  w.perm = o; o += perm_ws(c, T).total;
+  w.ffn = o; o += ffn_ws(c, T).total;
+  w.total = o;
+  return w;
+}
+
+char* at(void* base, size_t off) { return static_cast<char*>(base) + off; }
+
+moe_status_t hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+moe_status_t do_route(const moe_config_t* c, int64_t T, const void* x, const void* wr,
+                      const float* off, const float* bias, float* logits, int32_t* idx,
+                      float* gate, hipStream_t s) {
+  RouteArgs a{x, wr, off, bias, logits, idx, gate, T, c->d, c->num_experts, c->top_k,
+              c->gating, c->dtype};
+  return hip_status(launch_route(a, s));
+}
+
+moe_status_t do_permute(const moe_config_t* c, int64_t T, const int32_t* idx, const void* x,
+                        int32_t* counts, int32_t* offsets, int32_t* perm_src,
+                        int32_t* slot_pos, int32_t* dropped, void* x_perm, void* ws,
+                        hipStream_t s) {
+  const PermWs w = perm_ws(c, T);
+  PermuteArgs a;
+  a.topk_idx = idx;
+  a.x = x;
+  a.counts = counts;
+  a.offsets = offsets;
+  a.perm_src = perm_src;
+  a.slot_pos = slot_pos;
+  a.num_dropped = dropped;
+  a.x_perm = x_perm;
+  a.block_counts = reinterpret_cast<int32_t*>(at(ws, w.block_counts));
+  a.kept_total = reinterpret_cast<int32_t*>(at(ws, w.kept_total));
+  a.T = T;
+  a.k = c->top_k;
+  a.E = c->num_experts;
+  a.d = c->d;
+  a.dtype = c->dtype;
+  a.capacity = capacity_of(c, T);
+  return hip_status(launch_permute(a, s));
+}
+
+moe_status_t do_ffn(const moe_config_t* c, int64_t T, const void* x, const void* x_perm,
+                    const int32_t* offsets, const void* w1, const void* w3, const void* w2,
+                    const void* ws1, const void* ws3, const void* ws2, void* eout, void* sout,
+                    void* ws, hipStream_t s) {
+  const FfnWs w = ffn_ws(c, T);
+  const int64_t R = T * c->top_k;
+  const int mode1 = c->act == MOE_ACT_SWIGLU ? 3 : (c->act == MOE_ACT_GELU ? 2 : 1);
+  FfnPassArgs p;
+  memset(&p, 0, sizeof(p));
+  p.A = x_perm;
+  p.w = w1;
+  p.w_up = c->act == MOE_ACT_SWIGLU ? w3 : nullptr;
+  p.C = at(ws, w.H);
+  p.seg_offsets = offsets;
+  p.G = c->num_experts;
+  p.K = c->d;
+  p.N = c->d_ff;
+  p.mode = mode1;
+  p.dtype = c->dtype;
+  p.plan = at(ws, w.plan);
+  p.max_rows = R;
+  p.small = small_batch(R);
+  hipError_t e = launch_ffn_pass(p, s);
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  p.A = at(ws, w.H);
+  p.w = w2;
+  p.w_up = nullptr;
+  p.C = eout;
+  p.K = c->d_ff;
+  p.N = c->d;
+  p.mode = 0;
+  e = launch_ffn_pass(p, s);
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  if (c->num_shared > 0) {
+    const int S = c->num_shared;
+    FfnPassArgs q;
+    memset(&q, 0, sizeof(q));
+    q.A = x;
+    q.w = ws1;
+    q.w_up = ws3;
+    q.C = at(ws, w.Hs);
+    q.seg_offsets = nullptr;
+    q.dense_rows = T;
+    q.G = S;
+    q.K = c->d;
+    q.N = c->d_ff_shared;
+    q.mode = 3;
+    q.dtype = c->dtype;
+    q.a_seg_rows = 0;
+    q.c_seg_rows = T;
+    q.plan = at(ws, w.plan);
+    q.max_rows = (int64_t)S * T;
+    q.small = small_batch(T);
+    e = launch_ffn_pass(q, s);
+    if (e != hipSuccess) return MOE_ERR_HIP;
+    q.A = at(ws, w.Hs);
+    q.w = ws2;
+    q.w_up = nullptr;
+    q.C = sout;
+    q.K = c->d_ff_shared;
+    q.N = c->d;
+    q.mode = 0;
+    q.a_seg_rows = T;
+    q.c_seg_rows = T;
+    e = launch_ffn_pass(q, s);
+    if (e != hipSuccess) return MOE_ERR_HIP;
+  }
+  return MOE_OK;
+}
+
+moe_status_t do_combine(const moe_config_t* c, int64_t T, const void* eout,
+                        const int32_t* slot_pos, const float* gate, const void* sout, void* y,
+                        hipStream_t s) {
+  CombineArgs a{eout, slot_pos, gate, sout, y, T, c->top_k, c->d,
+                sout ? c->num_shared : 0, c->dtype};
+  return hip_status(launch_combine(a, s));
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_str(moe_status_t st) {
+  switch (st) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_INVALID_ARG: return "MOE_ERR_INVALID_ARG: invalid argument";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED: configuration not supported";
+    case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE: workspace too small";
+    case MOE_ERR_HIP: return "MOE_ERR_HIP: HIP runtime or launch error";
+  }
+  return "unknown moe_status_t";
+}
+
+moe_status_t moe_check_config(const moe_config_t* cfg, int64_t T) { return check_cfg(cfg, T); }
+
+moe_status_t moe_workspace_size(const moe_config_t* cfg, int64_t T, size_t* bytes) {
+  moe_status_t st = check_cfg(cfg, T);
+  if (st != MOE_OK) return st;
+  if (!bytes) return MOE_ERR_INVALID_ARG;
+  *bytes = fwd_ws(cfg, T).total;
+  return MOE_OK;
+}
+
+moe_status_t moe_capacity(const moe_config_t* cfg, int64_t T, int64_t* capacity) {
+  moe_status_t st = check_cfg(cfg, T);
+  if (st != MOE_OK) return st;
+  if (!capacity) return MOE_ERR_INVALID_ARG;
+  *capacity = capacity_of(cfg, T);
+  return MOE_OK;
+}
+
+moe_status_t moe_route(const moe_config_t* cfg, int64_t T, const void* x, const void* w_router,
+                       const float* logit_offset, const float* select_bias, float* logits,
+                       int32_t* topk_idx, float* topk_gate, void* stream) {
+  moe_status_t st = check_cfg(cfg, T);
+  if (st != MOE_OK) return st;
+  if (T == 0) return MOE_OK;  // nothing to do; token-sized pointers may be null
+  if (!x || !w_router || !topk_idx || !topk_gate) return MOE_ERR_INVALID_ARG;
+  if (!al(x, 16) || !al(w_router, 16) || !al(topk_idx, 4) || !al(topk_gate, 4) ||
+      (logits && !al(logits, 4)) || (logit_offset && !al(logit_offset, 4)) ||
+      (select_bias && !al(select_bias, 4)))
+    return MOE_ERR_INVALID_ARG;
+  return do_route(cfg, T, x, w_router, logit_offset, select_bias, logits, topk_idx, topk_gate,
+                  static_cast<hipStream_t>(stream));
+}
+
+moe_status_t moe_permute(const moe_config_t* cfg, int64_t T, const int32_t* topk_idx,
+                         const void* x, int32_t* expert_counts, int32_t* expert_offsets,
+                         int32_t* perm_src, int32_t* slot_pos, int32_t* num_dropped,
+                         void* x_perm, void* workspace, size_t ws_bytes, void* stream) {
+  moe_status_t st = check_cfg(cfg, T);
+  if (st != MOE_OK) return st;
+  if (T == 0) return MOE_OK;  // nothing to do; token-sized pointers may be null
+  if (!topk_idx || !expert_offsets || !perm_src || !slot_pos) return MOE_ERR_INVALID_ARG;
+  if (x_perm && (!x || !al(x, 16) || !al(x_perm, 16))) return MOE_ERR_INVALID_ARG;
+  if (!al(topk_idx, 4) || !al(expert_offsets, 4) || !al(perm_src, 4) || !al(slot_pos, 4) ||
+      (expert_counts && !al(expert_counts, 4)) || (num_dropped && !al(num_dropped, 4)))
+    return MOE_ERR_INVALID_ARG;
+  if (!workspace || !al(workspace, ALIGN)) return MOE_ERR_INVALID_ARG;
+  if (ws_bytes < fwd_ws(cfg, T).total) return MOE_ERR_WORKSPACE;
+  return do_permute(cfg, T, topk_idx, x, expert_counts, expert_offsets, perm_src, slot_pos,
+                    num_dropped, x_perm, workspace, static_cast<hipStream_t>(stream));
+}
+
+moe_status_t moe_expert_ffn(const moe_config_t* cfg, int64_t T, const void* x,
+                            const void* x_perm, const int32_t* expert_offsets, const void* w1,
+                            const void* w3, const void* w2, const void* ws1, const void* ws3,
+                            const void* ws2, void* expert_out, void* shared_out,
+                            void* workspace, size_t ws_bytes, void* stream) {
+  moe_status_t st = check_cfg(cfg, T);
+  if (st != MOE_OK) return st;
+  if (T == 0) return MOE_OK;  // nothing to do; token-sized pointers may be null
+  if (!x_perm || !expert_offsets || !w1 || !w2 || !expert_out) return MOE_ERR_INVALID_ARG;
+  if (cfg->act == MOE_ACT_SWIGLU && !w3) return MOE_ERR_INVALID_ARG;
+  if (cfg->num_shared > 0 && (!x || !ws1 || !ws3 || !ws2 || !shared_out))
+    return MOE_ERR_INVALID_ARG;
+  const void* p16[] = {x_perm, w1, w2, expert_out, w3, x, ws1, ws3, ws2, shared_out};
+  for (const void* p : p16)
+    if (p && !al(p, 16)) return MOE_ERR_INVALID_ARG;
+  if (!al(expert_offsets, 4)) return MOE_ERR_INVALID_ARG;
+  if (!workspace || !al(workspace, ALIGN)) return MOE_ERR_INVALID_ARG;
+  if (ws_bytes < fwd_ws(cfg, T).total) return MOE_ERR_WORKSPACE;
+  return do_ffn(cfg, T, x, x_perm, expert_offsets, w1, w3, w2, ws1, ws3, ws2, expert_out,
+                shared_out, workspace, static_cast<hipStream_t>(stream));
+}
+
+moe_status_t moe_combine(const moe_config_t* cfg, int64_t T, const void* expert_out,
+                         const int32_t* slot_pos, const float* topk_gate, const void* shared_out,
+                         void* y, void* stream) {
+  moe_status_t st = check_cfg(cfg, T);
+  if (st != MOE_OK) return st;
+  if (T == 0) return MOE_OK;  // nothing to do; token-sized pointers may be null
+  if (!expert_out || !slot_pos || !topk_gate || !y) return MOE_ERR_INVALID_ARG;
+  if (!al(expert_out, 16) || !al(y, 16) || (shared_out && !al(shared_out, 16)) ||
+      !al(slot_pos, 4) || !al(topk_gate, 4))
+    return MOE_ERR_INVALID_ARG;
+  return do_combine(cfg, T, expert_out, slot_pos, topk_gate, shared_out, y,
+                    static_cast<hipStream_t>(stream));
+}
+
+moe_status_t moe_forward(const moe_config_t* cfg, int64_t T, const void* x, const void* w_router,
+                         const float* logit_offset, const float* select_bias, const void* w1,
+                         const void* w3, const void* w2, const void* ws1, const void* ws3,
+                         const void* ws2, void* y, int32_t* topk_idx, float* topk_gate,
+                         int32_t* expert_counts, int32_t* num_dropped, void* workspace,
+                         size_t ws_bytes, void* stream) {
+  moe_status_t st = check_cfg(cfg, T);
+  if (st != MOE_OK) return st;
+  if (T == 0) return MOE_OK;  // nothing to do; token-sized pointers may be null
+  if (!x || !w_router || !w1 || !w2 || !y) return MOE_ERR_INVALID_ARG;
+  if (cfg->act == MOE_ACT_SWIGLU && !w3) return MOE_ERR_INVALID_ARG;
+  if (cfg->num_shared > 0 && (!ws1 || !ws3 || !ws2)) return MOE_ERR_INVALID_ARG;
+  const void* p16[] = {x, w_router, w1, w2, y, w3, ws1, ws3, ws2};
+  for (const void* p : p16)
+    if (p && !al(p, 16)) return MOE_ERR_INVALID_ARG;
+  const void* p4[] = {logit_offset, select_bias, topk_idx, topk_gate, expert_counts, num_dropped};
+  for (const void* p : p4)
+    if (p && !al(p, 4)) return MOE_ERR_INVALID_ARG;
+  if (!workspace || !al(workspace, ALIGN)) return MOE_ERR_INVALID_ARG;
+  const FwdWs w = fwd_ws(cfg, T);
+  if (ws_bytes < w.total) return MOE_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int32_t* idx = topk_idx ? topk_idx : reinterpret_cast<int32_t*>(at(workspace, w.idx));
+  float* gate = topk_gate ? topk_gate : reinterpret_cast<float*>(at(workspace, w.gate));
+  int32_t* counts = expert_counts ? expert_counts : reinterpret_cast<int32_t*>(at(workspace, w.counts));
+  int32_t* dropped = num_dropped ? num_dropped : reinterpret_cast<int32_t*>(at(workspace, w.dropped));
+  int32_t* offsets = reinterpret_cast<int32_t*>(at(workspace, w.offsets));
+  int32_t* perm_src = reinterpret_cast<int32_t*>(at(workspace, w.perm_src));
+  int32_t* slot_pos = reinterpret_cast<int32_t*>(at(workspace, w.slot_pos));
+  void* x_perm = at(workspace, w.x_perm);
+  void* eout = at(workspace, w.eout);
+  void* sout = cfg->num_shared > 0 ? at(workspace, w.sout) : nullptr;
+  st = do_route(cfg, T, x, w_router, logit_offset, select_bias, nullptr, idx, gate, s);
+  if (st != MOE_OK) return st;
+  st = do_permute(cfg, T, idx, x, counts, offsets, perm_src, slot_pos, dropped, x_perm,
+                  at(workspace, w.perm), s);
+  if (st != MOE_OK) return st;
+  st = do_ffn(cfg, T, x, x_perm, offsets, w1, w3, w2, ws1, ws3, ws2, eout, sout,
+              at(workspace, w.ffn), s);
+  if (st != MOE_OK) return st;
+  return do_combine(cfg, T, eout, slot_pos, gate, sout, y, s);
+}
+
+moe_status_t moe_profile_enable(int32_t on) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  for (auto& r : g_prof_recs) {
+    g_prof_pool.push_back(r.e0);
+    g_prof_pool.push_back(r.e1);
+  }
+  g_prof_recs.clear();
+  g_prof_on = on != 0;
+  return MOE_OK;
+}
+
+int32_t moe_profile_read(const char** names, double* total_ms, int32_t* launches,
+                         int32_t max_names) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  std::vector<const char*> nm;
+  std::vector<double> tot;
+  std::vector<int32_t> cnt;
+  int32_t rc = 0;
+  for (auto& r : g_prof_recs) {
+    float ms = 0.f;
+    if (hipEventSynchronize(r.e1) != hipSuccess || hipEventElapsedTime(&ms, r.e0, r.e1) != hipSuccess) {
+      rc = -1;
+      continue;
+    }
+    size_t i = 0;
+    for (; i < nm.size(); ++i)
+      if (strcmp(nm[i], r.name) == 0) break;
+    if (i == nm.size()) {
+      nm.push_back(r.name);
+      tot.push_back(0.0);
+      cnt.push_back(0);
+    }
+    tot[i] += ms;
+    cnt[i] += 1;
+  }
+  for (auto& r : g_prof_recs) {
+    g_prof_pool.push_back(r.e0);
+    g_prof_pool.push_back(r.e1);
+  }
+  g_prof_recs.clear();
+  if (rc < 0) return -1;
+  int32_t n = 0;
+  for (size_t i = 0; i < nm.size() && n < max_names; ++i, ++n) {
+    if (names) names[n] = nm[i];
+    if (total_ms) total_ms[n] = tot[i];
+    if (launches) launches[n] = cnt[i];
+  }
+  return n;
+}
+
+}  // extern "C"

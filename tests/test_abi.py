@@ -1,0 +1,129 @@
+"""The C-ABI library: it loads, exports every symbol include/moe.h declares,
+and rejects bad arguments on the host before touching the GPU (no compute
+call is made here)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from sparse_mixture_experts_gates_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(B.LIB_PATH),
+                                reason="libmoe_mi355x.so not built (run __graft_entry__.build())")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", src)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("moe_route", "moe_permute", "moe_expert_ffn", "moe_combine", "moe_forward",
+              "moe_workspace_size", "moe_capacity", "moe_status_str"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    L = ctypes.CDLL(B.LIB_PATH)
+    for n in declared_functions():
+        assert hasattr(L, n), n
+    assert set(declared_functions()) == set(B.EXPORTS)
+
+
+def test_config_struct_layout():
+    assert ctypes.sizeof(B.MoeConfig) == 40
+
+
+def test_status_strings():
+    for s in range(5):
+        assert B.lib().moe_status_str(s).decode().startswith(B.STATUS[s])
+
+
+def cfg(**kw):
+    base = dict(d=256, num_experts=8, top_k=2, d_ff=512, act="swiglu",
+                gating="softmax_topk", dtype="bf16")
+    base.update(kw)
+    return B.config(**base)
+
+
+def test_config_validation():
+    ok = cfg()
+    assert B.check_config(ok, 100) == 0
+    assert B.check_config(ok, 0) == 0
+    assert B.check_config(ok, -1) == 1
+    assert B.check_config(cfg(top_k=9), 10) == 1           # k > E
+    assert B.check_config(cfg(top_k=0), 10) == 1
+    assert B.check_config(cfg(d=0), 10) == 1
+    c = cfg(); c.act = 7
+    assert B.check_config(c, 10) == 1
+    c = cfg(); c.gating = -1
+    assert B.check_config(c, 10) == 1
+    c = cfg(); c.dtype = 5
+    assert B.check_config(c, 10) == 1
+    c = cfg(); c.capacity_factor = float("nan")
+    assert B.check_config(c, 10) == 1
+    assert B.check_config(cfg(d=100), 10) == 2              # bf16 needs multiples of 64
+    assert B.check_config(cfg(d=102, dtype="f32"), 10) == 2
+    assert B.check_config(cfg(d=100, dtype="f32"), 10) == 0
+    assert B.check_config(cfg(d=64, d_ff=36, dtype="f32"), 10) == 0
+    assert B.check_config(cfg(num_experts=300, top_k=2), 10) == 2
+    assert B.check_config(cfg(num_experts=64, top_k=17), 10) == 2
+    assert B.check_config(cfg(num_shared=1, d_ff_shared=0), 10) == 1
+    assert B.check_config(cfg(num_shared=1, d_ff_shared=128), 10) == 0
+
+
+def test_capacity_and_workspace_on_host():
+    c = cfg(d=768, d_ff=3072, top_k=1, act="relu", capacity_factor=1.25)
+    assert B.capacity(c, 8192) == 1280
+    assert B.capacity(cfg(), 8192) == -1
+    assert B.capacity(cfg(capacity_factor=1.0, top_k=2), 10) == 2   # floor(1*2*10/8)
+    w = B.workspace_size(cfg(), 1000)
+    assert w > 2000 * 256 * 2
+    assert B.workspace_size(cfg(), 0) >= 0
+    with pytest.raises(B.MoeError):
+        B.workspace_size(cfg(top_k=9), 10)
+
+
+def test_entry_points_reject_bad_arguments_before_any_gpu_work():
+    L = B.lib()
+    c = cfg()
+    p = ctypes.c_void_p(4096)          # aligned, never dereferenced
+    mis = ctypes.c_void_p(4096 + 2)    # misaligned
+    n = None
+    # null required pointers
+    assert L.moe_route(ctypes.byref(c), 10, n, p, n, n, n, p, p, n) == 1
+    assert L.moe_route(ctypes.byref(c), 10, mis, p, n, n, n, p, p, n) == 1
+    bad = cfg(top_k=9)
+    assert L.moe_route(ctypes.byref(bad), 10, p, p, n, n, n, p, p, n) == 1
+    assert L.moe_permute(ctypes.byref(c), 10, n, n, n, p, p, p, n, n, p, 1 << 30, n) == 1
+    # workspace too small
+    assert L.moe_permute(ctypes.byref(c), 10, p, n, n, p, p, p, n, n, p, 16, n) == 3
+    assert L.moe_expert_ffn(ctypes.byref(c), 10, n, p, p, p, n, p, n, n, n, p, n, p, 1 << 30, n) == 1  # swiglu needs w3
+    assert L.moe_combine(ctypes.byref(c), 10, p, p, p, n, n, n) == 1
+    assert L.moe_forward(ctypes.byref(c), 10, p, p, n, n, p, p, p, n, n, n, p, n, n, n, n, p, 16, n) == 3
+    assert L.moe_forward(ctypes.byref(c), 10, p, p, n, n, p, n, p, n, n, n, p, n, n, n, n, p, 1 << 40, n) == 1
+    sh = cfg(num_shared=1, d_ff_shared=128)
+    assert L.moe_forward(ctypes.byref(sh), 10, p, p, n, n, p, p, p, n, n, n, p, n, n, n, n, p, 1 << 40, n) == 1
+    # T = 0 is a valid no-op for every entry point
+    assert L.moe_route(ctypes.byref(c), 0, p, p, n, n, n, p, p, n) == 0
+    assert L.moe_permute(ctypes.byref(c), 0, p, n, n, p, p, p, n, n, n, 0, n) == 0
+    assert L.moe_expert_ffn(ctypes.byref(c), 0, n, p, p, p, p, p, n, n, n, p, n, n, 0, n) == 0
+    assert L.moe_combine(ctypes.byref(c), 0, p, p, p, n, p, n) == 0
+    assert L.moe_forward(ctypes.byref(c), 0, p, p, n, n, p, p, p, n, n, n, p, n, n, n, n, n, 0, n) == 0
+    assert L.moe_forward(ctypes.byref(c), 0, n, n, n, n, n, n, n, n, n, n, n, n, n, n, n, n, 0, n) == 0
+    assert L.moe_forward(ctypes.byref(bad), 0, n, n, n, n, n, n, n, n, n, n, n, n, n, n, n, n, 0, n) == 1
+
+
+def test_binding_refuses_host_tensors():
+    import torch
+    c = cfg()
+    with pytest.raises(ValueError):
+        B.route(c, torch.zeros((4, 256), dtype=torch.bfloat16),
+                torch.zeros((8, 256), dtype=torch.bfloat16))
