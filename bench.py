@@ -58,6 +58,31 @@ def algorithmic_work(w, counts):
                 kept=kept, active=active)
 
 
+def kernel_source_digest():
+    """sha256 of the sources the expert GEMM kernels are built from."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in ("ffn.hip", "common.h"):
+        with open(os.path.join(ROOT, "sparse_mixture_experts_gates_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(kernel, workload):
+    """HBM bytes per launch of `kernel` from the committed counter summary
+    (profiles/<kernel>_<workload>_traffic.json: FETCH_SIZE and WRITE_SIZE in
+    KiB per dispatch, each scaled by the factor a plain copy of known size
+    gives), or None when there is none or the kernel source changed since."""
+    p = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.json")
+    if not os.path.exists(p):
+        return None
+    with open(p) as fh:
+        d = json.load(fh)
+    if d.get("source_sha256") != kernel_source_digest():
+        return None
+    return d["traffic_bytes"]
+
+
 def cpu_baseline(w, inp, budget_s=15.0):
     """Time the CPU oracle (as it stands) on a bounded sample of tokens."""
     import numpy as np
@@ -89,8 +114,8 @@ def cpu_baseline(w, inp, budget_s=15.0):
 
     n = min(w.T, 64)
     dt = run(n)
-    if dt < budget_s / 3 and n < w.T:
-        n = min(w.T, max(n + 1, int(n * budget_s / max(dt, 1e-3))))
+    while dt < budget_s * 0.66 and n < w.T:
+        n = min(w.T, max(2 * n, int(n * budget_s / max(dt, 1e-3))))
         dt = run(n)
     return {"value": n / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
             "sample": f"first {n} of the {w.T} tokens of {w.name}, numpy float64 oracle "
@@ -186,7 +211,7 @@ def main():
                 "achieved": work["ffn1_flops"] / (dom_ms * 1e-3) / 1e12, "peak": peak,
                 "unit": "TFLOP/s", "algorithmic_flops_per_launch": work["ffn1_flops"]}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = None
+    roof["traffic"] = measured_traffic(dom, w.name)
     roof["avg_ms"] = dom_ms
     tflops = work["flops"] / (ms * 1e-3) / 1e12
     gbs = work["bytes"] / (ms * 1e-3) / 1e9

@@ -11,6 +11,7 @@ namespace moe {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));  // 16-byte copy unit
 
 // bf16 is carried as its 16-bit pattern in memory.
 __device__ __forceinline__ float bf16_to_f32(uint32_t h16) {

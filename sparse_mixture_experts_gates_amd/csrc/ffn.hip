@@ -139,15 +139,18 @@ __global__ __launch_bounds__(64 * WM * WN) void ffn_bf16_kernel(KArgs a) {
   const int64_t arow0 = (int64_t)pe.g * a.a_seg_rows;
   const int64_t wbase = (int64_t)pe.g * N * K;
 
-  // per-thread copy slots: (global source, LDS destination)
+  // per-thread copy slots: (global source, LDS destination).  Slots below
+  // CPT_FULL exist for every thread; the last one only when CHUNKS is not a
+  // multiple of the thread count.
+  constexpr int CPT_FULL = CHUNKS / NTH;
   const uint16_t* src[CPT];
   int dst[CPT];
 #pragma unroll
   for (int i = 0; i < CPT; ++i) {
     const int c = tid + i * NTH;
-    dst[i] = -1;
+    dst[i] = 0;
     src[i] = a.A;
-    if (c < CHUNKS) {
+    if (i < CPT_FULL || c < CHUNKS) {
       const int row = c >> 3, ch = c & 7;
       if (row < BM) {
         int r = pe.m0 + row;
@@ -171,18 +174,7 @@ __global__ __launch_bounds__(64 * WM * WN) void ffn_bf16_kernel(KArgs a) {
       }
     }
   }
-  uint4 stg[CPT];
-  auto gload = [&](int k0) {
-#pragma unroll
-    for (int i = 0; i < CPT; ++i)
-      if (dst[i] >= 0) stg[i] = *reinterpret_cast<const uint4*>(src[i] + k0);
-  };
-  auto lstore = [&](int buf) {
-    uint16_t* b = smem + buf * (SA + SB);
-#pragma unroll
-    for (int i = 0; i < CPT; ++i)
-      if (dst[i] >= 0) *reinterpret_cast<uint4*>(b + dst[i]) = stg[i];
-  };
+  const bool tail_slot = (CPT > CPT_FULL) && (tid + CPT_FULL * NTH < CHUNKS);
 
   f32x4_t acc[TM][TN];
 #pragma unroll
@@ -191,12 +183,23 @@ __global__ __launch_bounds__(64 * WM * WN) void ffn_bf16_kernel(KArgs a) {
     for (int j = 0; j < TN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   const int nk = K / BK;
-  gload(0);
-  lstore(0);
+  u32x4_t stg[CPT];
+#pragma unroll
+  for (int i = 0; i < CPT; ++i)
+    if (i < CPT_FULL || tail_slot) stg[i] = *reinterpret_cast<const u32x4_t*>(src[i]);
+#pragma unroll
+  for (int i = 0; i < CPT; ++i)
+    if (i < CPT_FULL || tail_slot) *reinterpret_cast<u32x4_t*>(smem + dst[i]) = stg[i];
   __syncthreads();
   for (int kt = 0; kt < nk; ++kt) {
     const int buf = kt & 1;
-    if (kt + 1 < nk) gload((kt + 1) * BK);
+    const bool more = kt + 1 < nk;
+    if (more) {
+      const int k0 = (kt + 1) * BK;
+#pragma unroll
+      for (int i = 0; i < CPT; ++i)
+        if (i < CPT_FULL || tail_slot) stg[i] = *reinterpret_cast<const u32x4_t*>(src[i] + k0);
+    }
     const uint16_t* sa = smem + buf * (SA + SB);
     const uint16_t* sb = sa + SA;
 #pragma unroll
@@ -215,7 +218,12 @@ __global__ __launch_bounds__(64 * WM * WN) void ffn_bf16_kernel(KArgs a) {
           acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fw[j], fx, acc[i][j], 0, 0, 0);
       }
     }
-    if (kt + 1 < nk) lstore(buf ^ 1);
+    if (more) {
+      uint16_t* b = smem + (buf ^ 1) * (SA + SB);
+#pragma unroll
+      for (int i = 0; i < CPT; ++i)
+        if (i < CPT_FULL || tail_slot) *reinterpret_cast<u32x4_t*>(b + dst[i]) = stg[i];
+    }
     __syncthreads();
   }
 

@@ -193,11 +193,11 @@ __global__ __launch_bounds__(RT_THREADS) void route_bf16_kernel(RouteArgs a) {
       }
     }
   }
-  uint4 stage[CPT];
+  u32x4_t stage[CPT];
   auto gload = [&](int k0) {
 #pragma unroll
     for (int i = 0; i < CPT; ++i)
-      if (dst[i] >= 0) stage[i] = *reinterpret_cast<const uint4*>(src[i] + k0);
+      if (dst[i] >= 0) stage[i] = *reinterpret_cast<const u32x4_t*>(src[i] + k0);
   };
   auto lstore = [&](int buf) {
 #pragma unroll
@@ -207,7 +207,7 @@ __global__ __launch_bounds__(RT_THREADS) void route_bf16_kernel(RouteArgs a) {
       // x chunks live in sx[buf], w chunks in sw[buf]
       uint16_t* base = off >= L::SX * 2 ? sw + buf * L::SW + (off - L::SX * 2)
                                         : sx + buf * L::SX + off;
-      *reinterpret_cast<uint4*>(base) = stage[i];
+      *reinterpret_cast<u32x4_t*>(base) = stage[i];
     }
   };
 
