@@ -16,7 +16,7 @@ from typing import Optional
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libmoe_mi355x.so")
+LIB_PATH = os.environ.get("MOE_MI355X_LIB") or os.path.join(_HERE, "libmoe_mi355x.so")
 
 MOE_F32, MOE_BF16 = 0, 1
 ACTS = {"relu": 0, "gelu": 1, "swiglu": 2}

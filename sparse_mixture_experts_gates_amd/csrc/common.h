@@ -5,7 +5,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#include "../../include/moe.h"
+#include "moe.h"
 
 namespace moe {
 
@@ -18,18 +18,16 @@ __device__ __forceinline__ float bf16_to_f32(uint32_t h16) {
   return __uint_as_float(h16 << 16);
 }
 
-// float -> bf16, round to nearest even; NaN stays NaN (quiet), Inf stays Inf.
-__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7f800000u) == 0x7f800000u)
-    return (u >> 16) | ((u & 0xffffu) ? 0x40u : 0u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return u >> 16;
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// float -> bf16 with the hardware conversion (v_cvt_pk_bf16_f32: round to
+// nearest even, NaN stays NaN), two at a time.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  const bf16x2_t v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
 }
 
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
-}
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) { return pack_bf16x2(f, 0.f) & 0xffffu; }
 
 // Order-preserving map of a float to uint32 (larger float -> larger key).
 // -0.0 is folded into +0.0 first.

@@ -114,67 +114,83 @@ __device__ __forceinline__ float act1(float v) {
   return v;
 }
 
-template <int BM, int BN, int WM, int WN, int MODE>
-__global__ __launch_bounds__(64 * WM * WN) void ffn_bf16_kernel(KArgs a) {
-  constexpr int NTH = 64 * WM * WN;
+#define LDS_PTR(p) ((__attribute__((address_space(3))) void*)(p))
+
+// Workgroup barrier that orders LDS accesses in the compiler but does not wait
+// for outstanding global loads (the ring below waits for exactly the ones it
+// needs with wait_vm_lgkm0 first).
+__device__ __forceinline__ void ring_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+// s_waitcnt vmcnt(N) lgkmcnt(0) (gfx9 encoding: vmcnt[3:0], expcnt[6:4] = 7
+// i.e. no wait, lgkmcnt[11:8], vmcnt high bits [15:14]).
+template <int N>
+__device__ __forceinline__ void wait_vm_lgkm0() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | ((N >> 4) << 14));
+}
+
+// Grouped GEMM tile: BM rows of A (tokens) x BN rows of W (weights), K in
+// slabs of 64 through an NSTAGE-deep LDS ring filled by direct-to-LDS loads
+// (global_load_lds_dwordx4).  A slab row is 128 bytes (8 chunks of 16 B) and
+// chunk c of row r sits at chunk c ^ (r & 7), so the MFMA operand reads
+// (16 rows at one chunk) hit distinct banks.  One load instruction fills 8
+// whole rows (1 KB): lane l writes LDS bytes 16*l, i.e. row l/8, chunk l%8,
+// so it fetches logical chunk (l%8) ^ (l/8) of its row -- full 128-byte lines
+// per 8 lanes.  Slab kt+NSTAGE-1 is requested while slab kt is multiplied;
+// one barrier per slab.
+template <int BM, int BN, int WM, int WN, int NSTAGE, int MODE>
+__global__ __launch_bounds__(64 * WM * WN)
+void ffn_bf16_kernel(KArgs a) {
+  constexpr int NW = WM * WN;
   constexpr int BMW = BM / WM, BNW = BN / WN;   // wave tile (tokens, weight rows)
   constexpr int TM = BMW / 16, TN = BNW / 16;
   constexpr int HALF = BNW / 2;                  // SwiGLU: gate rows per wave
   constexpr int BNOUT = MODE == MODE_SWIGLU ? BN / 2 : BN;
-  constexpr int CHUNKS = (BM + BN) * 8;
-  constexpr int CPT = (CHUNKS + NTH - 1) / NTH;
-  constexpr int SA = BM * BK, SB = BN * BK;      // bf16 elements per stage
+  constexpr int NG = (BM + BN) / 8;              // 8-row load groups per slab
+  constexpr int DPW = NG / NW;                   // load instructions per wave per slab
+  static_assert(NG % NW == 0, "load groups must divide evenly over the waves");
+  constexpr int SEL = (BM + BN) * BK;            // bf16 elements per slab
   static_assert(MODE != MODE_SWIGLU || TN % 2 == 0, "SwiGLU needs paired tiles");
 
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * (SA + SB)];
+  __shared__ __attribute__((aligned(1024))) uint16_t ring[NSTAGE * SEL];
 
   const int V = a.count[0];
   const int P = blockIdx.x;
   if (P >= V) return;
   const PlanEntry pe = a.plan[xcd_remap(P, V)];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
   const int wm = wave / WN, wn = wave % WN;
   const int K = a.K, N = a.N;
   const int n0 = pe.nt * BNOUT;
   const int64_t arow0 = (int64_t)pe.g * a.a_seg_rows;
   const int64_t wbase = (int64_t)pe.g * N * K;
 
-  // per-thread copy slots: (global source, LDS destination).  Slots below
-  // CPT_FULL exist for every thread; the last one only when CHUNKS is not a
-  // multiple of the thread count.
-  constexpr int CPT_FULL = CHUNKS / NTH;
-  const uint16_t* src[CPT];
-  int dst[CPT];
+  // this lane's source (row, logical chunk) for each 8-row group the wave loads
+  const uint16_t* src[DPW];
 #pragma unroll
-  for (int i = 0; i < CPT; ++i) {
-    const int c = tid + i * NTH;
-    dst[i] = 0;
-    src[i] = a.A;
-    if (i < CPT_FULL || c < CHUNKS) {
-      const int row = c >> 3, ch = c & 7;
-      if (row < BM) {
-        int r = pe.m0 + row;
-        if (r > pe.m1 - 1) r = pe.m1 - 1;
-        src[i] = a.A + (arow0 + r) * K + ch * 8;
-        dst[i] = swz(row, ch);
+  for (int i = 0; i < DPW; ++i) {
+    const int row = (wave + i * NW) * 8 + (lane >> 3);
+    const int ch = (lane & 7) ^ (lane >> 3);
+    if (row < BM) {
+      int r = pe.m0 + row;
+      if (r > pe.m1 - 1) r = pe.m1 - 1;
+      src[i] = a.A + (arow0 + r) * K + ch * 8;
+    } else {
+      const int rho = row - BM;
+      int n;
+      const uint16_t* Wm = a.W;
+      if (MODE == MODE_SWIGLU) {
+        const int wq = rho / BNW, wi = rho - wq * BNW;
+        n = n0 + wq * HALF + (wi < HALF ? wi : wi - HALF);
+        if (wi >= HALF) Wm = a.Wu;
       } else {
-        const int rho = row - BM;
-        int n;
-        const uint16_t* Wm = a.W;
-        if (MODE == MODE_SWIGLU) {
-          const int wq = rho / BNW, wi = rho - wq * BNW;
-          n = n0 + wq * HALF + (wi < HALF ? wi : wi - HALF);
-          if (wi >= HALF) Wm = a.Wu;
-        } else {
-          n = n0 + rho;
-        }
-        if (n > N - 1) n = N - 1;
-        src[i] = Wm + wbase + (int64_t)n * K + ch * 8;
-        dst[i] = SA + swz(rho, ch);
+        n = n0 + rho;
       }
+      if (n > N - 1) n = N - 1;
+      src[i] = Wm + wbase + (int64_t)n * K + ch * 8;
     }
   }
-  const bool tail_slot = (CPT > CPT_FULL) && (tid + CPT_FULL * NTH < CHUNKS);
 
   f32x4_t acc[TM][TN];
 #pragma unroll
@@ -183,25 +199,30 @@ __global__ __launch_bounds__(64 * WM * WN) void ffn_bf16_kernel(KArgs a) {
     for (int j = 0; j < TN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   const int nk = K / BK;
-  u32x4_t stg[CPT];
 #pragma unroll
-  for (int i = 0; i < CPT; ++i)
-    if (i < CPT_FULL || tail_slot) stg[i] = *reinterpret_cast<const u32x4_t*>(src[i]);
+  for (int s = 0; s < NSTAGE - 1; ++s) {
+    const int kk = s < nk ? s : nk - 1;
 #pragma unroll
-  for (int i = 0; i < CPT; ++i)
-    if (i < CPT_FULL || tail_slot) *reinterpret_cast<u32x4_t*>(smem + dst[i]) = stg[i];
-  __syncthreads();
+    for (int i = 0; i < DPW; ++i)
+      __builtin_amdgcn_global_load_lds((const void*)(src[i] + kk * BK),
+                                       LDS_PTR(ring + s * SEL + (wave + i * NW) * 512), 16, 0, 0);
+  }
+  int cur_s = 0;                          // ring stage of slab kt
+  int nxt_s = NSTAGE - 1;                 // ring stage of slab kt + NSTAGE - 1
   for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt & 1;
-    const bool more = kt + 1 < nk;
-    if (more) {
-      const int k0 = (kt + 1) * BK;
+    // slab kt has landed for this wave once at most NSTAGE-2 younger slabs remain
+    wait_vm_lgkm0<(NSTAGE - 2) * DPW>();
+    ring_barrier();
+    // refill the stage consumed in step kt-1 (past the end: a harmless reload
+    // of the last slab, so every step has the same shape)
+    const int kn = kt + NSTAGE - 1 < nk ? kt + NSTAGE - 1 : nk - 1;
+    uint16_t* nxt = ring + nxt_s * SEL;
 #pragma unroll
-      for (int i = 0; i < CPT; ++i)
-        if (i < CPT_FULL || tail_slot) stg[i] = *reinterpret_cast<const u32x4_t*>(src[i] + k0);
-    }
-    const uint16_t* sa = smem + buf * (SA + SB);
-    const uint16_t* sb = sa + SA;
+    for (int i = 0; i < DPW; ++i)
+      __builtin_amdgcn_global_load_lds((const void*)(src[i] + kn * BK),
+                                       LDS_PTR(nxt + (wave + i * NW) * 512), 16, 0, 0);
+    const uint16_t* sa = ring + cur_s * SEL;
+    const uint16_t* sb = sa + BM * BK;
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
       const int ch = kk * 4 + (lane >> 4);
@@ -218,23 +239,21 @@ __global__ __launch_bounds__(64 * WM * WN) void ffn_bf16_kernel(KArgs a) {
           acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fw[j], fx, acc[i][j], 0, 0, 0);
       }
     }
-    if (more) {
-      uint16_t* b = smem + (buf ^ 1) * (SA + SB);
-#pragma unroll
-      for (int i = 0; i < CPT; ++i)
-        if (i < CPT_FULL || tail_slot) *reinterpret_cast<u32x4_t*>(b + dst[i]) = stg[i];
-    }
-    __syncthreads();
+    cur_s = cur_s + 1 == NSTAGE ? 0 : cur_s + 1;
+    nxt_s = nxt_s + 1 == NSTAGE ? 0 : nxt_s + 1;
   }
+  wait_vm_lgkm0<0>();   // the trailing reloads must land before the LDS is released
 
-  // epilogue: lane holds columns 4*(lane/16)+r of tile j, row lane%16 of tile i
+  // epilogue: lane holds columns 4*(lane/16)+q of tile j, row lane%16 of
+  // tile i.  N is a multiple of 64, so a 4-column group is either wholly in
+  // range or wholly out.
   const int64_t crow0 = (int64_t)pe.g * a.c_seg_rows;
+  constexpr int JOUT = MODE == MODE_SWIGLU ? TN / 2 : TN;
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
     const int r = pe.m0 + wm * BMW + i * 16 + (lane & 15);
-    if (r >= pe.m1) continue;
+    const bool row_ok = r < pe.m1;
     uint16_t* crow = a.C + (crow0 + r) * (int64_t)N;
-    constexpr int JOUT = MODE == MODE_SWIGLU ? TN / 2 : TN;
 #pragma unroll
     for (int j = 0; j < JOUT; ++j) {
       float v[4];
@@ -248,16 +267,10 @@ __global__ __launch_bounds__(64 * WM * WN) void ffn_bf16_kernel(KArgs a) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) v[q] = act1<MODE>(acc[i][j][q]);
       }
-      if (col + 3 < N) {
-        uint2 pk;
-        pk.x = pack_bf16x2(v[0], v[1]);
-        pk.y = pack_bf16x2(v[2], v[3]);
-        *reinterpret_cast<uint2*>(crow + col) = pk;
-      } else {
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-          if (col + q < N) crow[col + q] = (uint16_t)f32_to_bf16(v[q]);
-      }
+      uint2 pk;
+      pk.x = pack_bf16x2(v[0], v[1]);
+      pk.y = pack_bf16x2(v[2], v[3]);
+      if (row_ok && col < N) *reinterpret_cast<uint2*>(crow + col) = pk;
     }
   }
 }
@@ -350,7 +363,7 @@ struct Shape {
 
 Shape pick_shape(int dtype, bool small, int mode) {
   if (dtype == MOE_F32) return {64, 64};
-  if (small) return {16, mode == MODE_SWIGLU ? 64 : 128};
+  if (small) return {64, mode == MODE_SWIGLU ? 64 : 128};
   return {256, mode == MODE_SWIGLU ? 128 : 256};
 }
 
@@ -359,13 +372,13 @@ int64_t max_entries(int64_t max_rows, int G, int N, Shape sh) {
   return ((max_rows + sh.BM - 1) / sh.BM + G) * nt;
 }
 
-template <int BM, int BN, int WM, int WN>
+template <int BM, int BN, int WM, int WN, int NS>
 void launch_bf16(int mode, unsigned grid, const KArgs& k, hipStream_t s) {
   switch (mode) {
-    case MODE_PLAIN: ffn_bf16_kernel<BM, BN, WM, WN, MODE_PLAIN><<<grid, 64 * WM * WN, 0, s>>>(k); break;
-    case MODE_RELU: ffn_bf16_kernel<BM, BN, WM, WN, MODE_RELU><<<grid, 64 * WM * WN, 0, s>>>(k); break;
-    case MODE_GELU: ffn_bf16_kernel<BM, BN, WM, WN, MODE_GELU><<<grid, 64 * WM * WN, 0, s>>>(k); break;
-    default: ffn_bf16_kernel<BM, BN, WM, WN, MODE_SWIGLU><<<grid, 64 * WM * WN, 0, s>>>(k); break;
+    case MODE_PLAIN: ffn_bf16_kernel<BM, BN, WM, WN, NS, MODE_PLAIN><<<grid, 64 * WM * WN, 0, s>>>(k); break;
+    case MODE_RELU: ffn_bf16_kernel<BM, BN, WM, WN, NS, MODE_RELU><<<grid, 64 * WM * WN, 0, s>>>(k); break;
+    case MODE_GELU: ffn_bf16_kernel<BM, BN, WM, WN, NS, MODE_GELU><<<grid, 64 * WM * WN, 0, s>>>(k); break;
+    default: ffn_bf16_kernel<BM, BN, WM, WN, NS, MODE_SWIGLU><<<grid, 64 * WM * WN, 0, s>>>(k); break;
   }
 }
 
@@ -413,9 +426,9 @@ hipError_t launch_ffn_pass(const FfnPassArgs& p, hipStream_t s) {
       default: ffn_f32_kernel<MODE_SWIGLU><<<(unsigned)grid, 256, 0, s>>>(k); break;
     }
   } else if (p.small) {
-    launch_bf16<16, 128, 1, 4>(p.mode, (unsigned)grid, k, s);
+    launch_bf16<64, 128, 1, 4, 3>(p.mode, (unsigned)grid, k, s);
   } else {
-    launch_bf16<256, 256, 2, 4>(p.mode, (unsigned)grid, k, s);
+    launch_bf16<256, 256, 2, 4, 2>(p.mode, (unsigned)grid, k, s);
   }
   prof_after(s);
   return hipGetLastError();
