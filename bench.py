@@ -129,6 +129,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="mixtral_bf16")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--graph", action="store_true",
+                    help="capture one step in a HIP graph (torch.cuda.CUDAGraph) and time replays")
     ap.add_argument("--copy-calib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -184,16 +186,43 @@ def main():
         torch.cuda.synchronize()
         del a, b
 
-    B.profile_enable(True)
+    run = step
+    if args.graph:
+        # the library launches on torch's current stream, so a capture on a
+        # side stream records every kernel of the step; replays reuse the
+        # same buffers
+        g = torch.cuda.CUDAGraph()
+        cs = torch.cuda.Stream()
+        cs.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(cs):
+            step()
+            torch.cuda.synchronize()
+            with torch.cuda.graph(g, stream=cs):
+                step()
+        torch.cuda.current_stream().wait_stream(cs)
+        torch.cuda.synchronize()
+        run = g.replay
+        for _ in range(args.warmup):
+            run()
+
+    # timed region 1: whole steps (the throughput `value`)
     torch.cuda.synchronize()
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     t0.record()
     for _ in range(args.steps):
-        step()
+        run()
     t1.record()
     torch.cuda.synchronize()
     ms = t0.elapsed_time(t1) / args.steps
+
+    # timed region 2: the same steps with the library's per-launch HIP events
+    # (on the stream each kernel is launched on) for the per-kernel times
+    B.profile_enable(True)
+    torch.cuda.synchronize()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
     prof = B.profile_read()
     B.profile_enable(False)
 
@@ -228,6 +257,7 @@ def main():
         "vs_baseline": None,
         "dtype": w.dtype,
         "data": "synthetic",
+        "hip_graph": bool(args.graph),
         "config": {"workload": w.name, "T": w.T, "d": w.d, "E": w.E, "k": w.k,
                    "d_ff": w.d_ff, "act": w.act, "gating": w.gating,
                    "capacity_factor": w.capacity_factor, "num_shared": w.num_shared,

@@ -141,12 +141,18 @@ moe_status_t moe_capacity(const moe_config_t* cfg, int64_t T,
  *   topk_idx     [T, k] int32 out: experts in descending key order, ties to
  *                the lower index, -0.0 == +0.0
  *   topk_gate    [T, k] fp32 out: gates in the same order
+ *   workspace    optional device scratch (NULL allowed, 256-byte aligned).
+ *                With T <= 16 (bf16) and ws_bytes >= moe_workspace_size(),
+ *                the scores are computed split over K by many workgroups and
+ *                reduced in a fixed order; otherwise it is not used.
  * One fused kernel: MFMA score GEMM, then per-token top-k with wavefront
- * shuffles and the gates, from the scores held in LDS. */
+ * shuffles and the gates, from the scores held in LDS (small batches with a
+ * workspace: a split-K score kernel plus one reduce-and-select kernel). */
 moe_status_t moe_route(const moe_config_t* cfg, int64_t T, const void* x,
                        const void* w_router, const float* logit_offset,
                        const float* select_bias, float* logits,
-                       int32_t* topk_idx, float* topk_gate, void* stream);
+                       int32_t* topk_idx, float* topk_gate, void* workspace,
+                       size_t ws_bytes, void* stream);
 
 /* Capacity, histogram, scan and the stable permutation (LLM tutorial ch. 11,
  * "Expert capacity and dropped tokens" and Exercise 4; "Chapter 33 -- Mixture

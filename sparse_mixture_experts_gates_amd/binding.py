@@ -63,7 +63,7 @@ def lib():
         L.moe_check_config.argtypes = [_cfgp, _i64]
         L.moe_workspace_size.argtypes = [_cfgp, _i64, ctypes.POINTER(_sz)]
         L.moe_capacity.argtypes = [_cfgp, _i64, ctypes.POINTER(_i64)]
-        L.moe_route.argtypes = [_cfgp, _i64] + [_vp] * 7 + [_vp]
+        L.moe_route.argtypes = [_cfgp, _i64] + [_vp] * 8 + [_sz, _vp]
         L.moe_permute.argtypes = [_cfgp, _i64] + [_vp] * 9 + [_sz, _vp]
         L.moe_expert_ffn.argtypes = [_cfgp, _i64] + [_vp] * 12 + [_sz, _vp]
         L.moe_combine.argtypes = [_cfgp, _i64] + [_vp] * 5 + [_vp]
@@ -137,15 +137,15 @@ def workspace(cfg, T, device="cuda"):
     return torch.empty(max(workspace_size(cfg, T), 256), dtype=torch.uint8, device=device)
 
 
-def route(cfg, x, w_router, logit_offset=None, select_bias=None, want_logits=False):
+def route(cfg, x, w_router, logit_offset=None, select_bias=None, want_logits=False, ws=None):
     T = x.shape[0]
     k, E = cfg.top_k, cfg.num_experts
     idx = torch.empty((T, k), dtype=torch.int32, device=x.device)
     gate = torch.empty((T, k), dtype=torch.float32, device=x.device)
     logits = torch.empty((T, E), dtype=torch.float32, device=x.device) if want_logits else None
     _check(lib().moe_route(ctypes.byref(cfg), T, _ptr(x), _ptr(w_router), _ptr(logit_offset),
-                           _ptr(select_bias), _ptr(logits), _ptr(idx), _ptr(gate), _stream()),
-           "moe_route")
+                           _ptr(select_bias), _ptr(logits), _ptr(idx), _ptr(gate), _ptr(ws),
+                           0 if ws is None else ws.numel(), _stream()), "moe_route")
     return idx, gate, logits
 
 

@@ -50,4 +50,35 @@ __device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int mask) {
 
 __host__ __device__ constexpr int cdiv(int a, int b) { return (a + b - 1) / b; }
 
+// ---- LDS operand slabs shared by the MFMA kernels -------------------------
+// A slab row is 64 bf16 (128 bytes = 8 chunks of 16 B); chunk c of row r is
+// stored at chunk c ^ (r & 7), so 16 rows read at one logical chunk (the
+// operand of one v_mfma_f32_16x16x32_bf16) fall in distinct banks.
+__device__ __forceinline__ int swz(int row, int chunk) {  // bf16 element offset
+  return row * 64 + ((chunk ^ (row & 7)) << 3);
+}
+
+#define MOE_LDS_PTR(p) ((__attribute__((address_space(3))) void*)(p))
+
+// Workgroup barrier that orders LDS accesses in the compiler but does not wait
+// for outstanding global loads; callers wait for exactly what they need first.
+__device__ __forceinline__ void ring_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+// s_waitcnt vmcnt(N) lgkmcnt(0) (gfx9 encoding: vmcnt[3:0], expcnt[6:4] = 7
+// i.e. no wait, lgkmcnt[11:8], vmcnt high bits [15:14]).
+template <int N>
+__device__ __forceinline__ void wait_vm_lgkm0() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | ((N >> 4) << 14));
+}
+
+// One direct-to-LDS load of 8 whole slab rows (1 KB): lane l writes LDS bytes
+// 16*l (row l/8, stored chunk l%8), so it must fetch logical chunk
+// (l%8) ^ (l/8) of its row; 8 lanes cover one full 128-byte line.
+__device__ __forceinline__ int dma_row(int lane) { return lane >> 3; }
+__device__ __forceinline__ int dma_chunk(int lane) { return (lane & 7) ^ (lane >> 3); }
+__device__ __forceinline__ void dma_rows(const uint16_t* src, uint16_t* lds_group) {
+  __builtin_amdgcn_global_load_lds((const void*)src, MOE_LDS_PTR(lds_group), 16, 0, 0);
+}
+
 }  // namespace moe

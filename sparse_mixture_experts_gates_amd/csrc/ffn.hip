@@ -44,14 +44,19 @@ struct KArgs {
   uint16_t* C;
   const PlanEntry* plan;
   const int32_t* count;
+  const int32_t* a_rows;  // optional row indirection for A (row gather folded in)
+  int a_div;
   int K, N;
   int64_t a_seg_rows, c_seg_rows;  // extra row offset per segment (shared experts)
 };
 
-// Plan: one workgroup; G <= 1024 segments.
+// Plan: one workgroup; G <= 1024 segments.  Writes the entries of one pass
+// (NT column tiles) and, when NT2 > 0, of a second pass over the same row
+// tiles with NT2 column tiles (the two expert GEMMs share their row tiling).
 __global__ __launch_bounds__(1024) void ffn_plan_kernel(
     const int32_t* __restrict__ seg, int G, int64_t dense_rows, int BM, int NT,
-    PlanEntry* __restrict__ plan, int32_t* __restrict__ count) {
+    PlanEntry* __restrict__ plan, int32_t* __restrict__ count, int NT2,
+    PlanEntry* __restrict__ plan2, int32_t* __restrict__ count2) {
   __shared__ int mt[1024];
   __shared__ int start[1024];
   __shared__ int rows_s[1024];
@@ -69,30 +74,33 @@ __global__ __launch_bounds__(1024) void ffn_plan_kernel(
     int acc = 0;
     for (int g = 0; g < G; ++g) {
       base[g] = acc;
-      acc += mt[g] * NT;
+      acc += mt[g];
     }
     base[G] = acc;
   }
   __syncthreads();
-  const int V = base[G];
-  for (int L = tid; L < V; L += 1024) {
-    int lo = 0, hi = G - 1;  // last g with base[g] <= L
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (base[mid] <= L) lo = mid; else hi = mid - 1;
+  const int MT = base[G];   // row tiles over all segments
+  for (int pass = 0; pass < 2; ++pass) {
+    const int nt_all = pass == 0 ? NT : NT2;
+    PlanEntry* out = pass == 0 ? plan : plan2;
+    if (nt_all <= 0) break;
+    const int V = MT * nt_all;
+    for (int L = tid; L < V; L += 1024) {
+      // entry L: segment-major, then column tile, then row tile
+      int lo = 0, hi = G - 1;  // last g with base[g] * nt_all <= L
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (base[mid] * nt_all <= L) lo = mid; else hi = mid - 1;
+      }
+      const int g = lo, rem = L - base[g] * nt_all, m = mt[g];
+      const int nt = rem / m, mi = rem - nt * m;
+      const int m0 = start[g] + mi * BM;
+      int m1 = m0 + BM;
+      if (m1 > start[g] + rows_s[g]) m1 = start[g] + rows_s[g];
+      out[L] = PlanEntry{g, m0, m1, nt};
     }
-    const int g = lo, rem = L - base[g], m = mt[g];
-    const int nt = rem / m, mi = rem - nt * m;
-    const int m0 = start[g] + mi * BM;
-    int m1 = m0 + BM;
-    if (m1 > start[g] + rows_s[g]) m1 = start[g] + rows_s[g];
-    plan[L] = PlanEntry{g, m0, m1, nt};
+    if (tid == 0) (pass == 0 ? count : count2)[0] = V;
   }
-  if (tid == 0) count[0] = V;
-}
-
-__device__ __forceinline__ int swz(int row, int chunk) {
-  return row * BK + ((chunk ^ (row & 7)) << 3);
 }
 
 // XCD-aware order: physical block P runs on XCD P % 8; give each XCD a
@@ -112,21 +120,6 @@ __device__ __forceinline__ float act1(float v) {
   if (MODE == MODE_RELU) return v > 0.f ? v : 0.f;
   if (MODE == MODE_GELU) return gelu_erf(v);
   return v;
-}
-
-#define LDS_PTR(p) ((__attribute__((address_space(3))) void*)(p))
-
-// Workgroup barrier that orders LDS accesses in the compiler but does not wait
-// for outstanding global loads (the ring below waits for exactly the ones it
-// needs with wait_vm_lgkm0 first).
-__device__ __forceinline__ void ring_barrier() { asm volatile("s_barrier" ::: "memory"); }
-
-// s_waitcnt vmcnt(N) lgkmcnt(0) (gfx9 encoding: vmcnt[3:0], expcnt[6:4] = 7
-// i.e. no wait, lgkmcnt[11:8], vmcnt high bits [15:14]).
-template <int N>
-__device__ __forceinline__ void wait_vm_lgkm0() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | ((N >> 4) << 14));
 }
 
 // Grouped GEMM tile: BM rows of A (tokens) x BN rows of W (weights), K in
@@ -170,12 +163,13 @@ void ffn_bf16_kernel(KArgs a) {
   const uint16_t* src[DPW];
 #pragma unroll
   for (int i = 0; i < DPW; ++i) {
-    const int row = (wave + i * NW) * 8 + (lane >> 3);
-    const int ch = (lane & 7) ^ (lane >> 3);
+    const int row = (wave + i * NW) * 8 + dma_row(lane);
+    const int ch = dma_chunk(lane);
     if (row < BM) {
       int r = pe.m0 + row;
       if (r > pe.m1 - 1) r = pe.m1 - 1;
-      src[i] = a.A + (arow0 + r) * K + ch * 8;
+      const int64_t sr = a.a_rows ? (int64_t)(a.a_rows[r] / a.a_div) : arow0 + r;
+      src[i] = a.A + sr * K + ch * 8;
     } else {
       const int rho = row - BM;
       int n;
@@ -204,8 +198,7 @@ void ffn_bf16_kernel(KArgs a) {
     const int kk = s < nk ? s : nk - 1;
 #pragma unroll
     for (int i = 0; i < DPW; ++i)
-      __builtin_amdgcn_global_load_lds((const void*)(src[i] + kk * BK),
-                                       LDS_PTR(ring + s * SEL + (wave + i * NW) * 512), 16, 0, 0);
+      dma_rows(src[i] + kk * BK, ring + s * SEL + (wave + i * NW) * 512);
   }
   int cur_s = 0;                          // ring stage of slab kt
   int nxt_s = NSTAGE - 1;                 // ring stage of slab kt + NSTAGE - 1
@@ -219,8 +212,7 @@ void ffn_bf16_kernel(KArgs a) {
     uint16_t* nxt = ring + nxt_s * SEL;
 #pragma unroll
     for (int i = 0; i < DPW; ++i)
-      __builtin_amdgcn_global_load_lds((const void*)(src[i] + kn * BK),
-                                       LDS_PTR(nxt + (wave + i * NW) * 512), 16, 0, 0);
+      dma_rows(src[i] + kn * BK, nxt + (wave + i * NW) * 512);
     const uint16_t* sa = ring + cur_s * SEL;
     const uint16_t* sb = sa + BM * BK;
 #pragma unroll
@@ -308,7 +300,8 @@ __global__ __launch_bounds__(256) void ffn_f32_kernel(KArgs a) {
       const bool kin = k0 + kk < K;
       int r = pe.m0 + row;
       if (r > pe.m1 - 1) r = pe.m1 - 1;
-      As[kk][row] = kin ? A[(arow0 + r) * K + k0 + kk] : 0.f;
+      const int64_t sr = a.a_rows ? (int64_t)(a.a_rows[r] / a.a_div) : arow0 + r;
+      As[kk][row] = kin ? A[sr * K + k0 + kk] : 0.f;
       int n = n0 + row;
       if (n > N - 1) n = N - 1;
       Ws[kk][row] = kin ? W[wbase + (int64_t)n * K + k0 + kk] : 0.f;
@@ -363,7 +356,7 @@ struct Shape {
 
 Shape pick_shape(int dtype, bool small, int mode) {
   if (dtype == MOE_F32) return {64, 64};
-  if (small) return {64, mode == MODE_SWIGLU ? 64 : 128};
+  if (small) return {32, mode == MODE_SWIGLU ? 64 : 128};
   return {256, mode == MODE_SWIGLU ? 128 : 256};
 }
 
@@ -390,20 +383,38 @@ size_t ffn_plan_bytes(int64_t max_rows, int G, int N, bool small, int dtype) {
     const size_t b = 16 + 16 * (size_t)max_entries(max_rows, G, N, pick_shape(dtype, small, mode));
     if (b > best) best = b;
   }
-  return best;
+  return (best + 255) / 256 * 256;
+}
+
+namespace {
+int pass_nt(const FfnPassArgs& p) {
+  const Shape sh = pick_shape(p.dtype, p.small, p.mode);
+  return (p.N + sh.BNOUT - 1) / sh.BNOUT;
+}
+}  // namespace
+
+hipError_t launch_ffn_plans(const FfnPassArgs& p1, const FfnPassArgs& p2, hipStream_t s) {
+  const Shape sh1 = pick_shape(p1.dtype, p1.small, p1.mode);
+  const Shape sh2 = pick_shape(p2.dtype, p2.small, p2.mode);
+  if (sh1.BM != sh2.BM || p1.seg_offsets != p2.seg_offsets) return hipErrorInvalidValue;
+  if (max_entries(p1.max_rows, p1.G, p1.N, sh1) == 0) return hipSuccess;
+  int32_t* c1 = static_cast<int32_t*>(p1.plan);
+  int32_t* c2 = static_cast<int32_t*>(p2.plan);
+  PlanEntry* e1 = reinterpret_cast<PlanEntry*>(static_cast<char*>(p1.plan) + 16);
+  PlanEntry* e2 = reinterpret_cast<PlanEntry*>(static_cast<char*>(p2.plan) + 16);
+  prof_before(p1.seg_offsets ? "ffn_plan" : "ffn_plan_shared", s);
+  ffn_plan_kernel<<<1, 1024, 0, s>>>(p1.seg_offsets, p1.G, p1.dense_rows, sh1.BM, pass_nt(p1), e1, c1,
+                                     pass_nt(p2), e2, c2);
+  prof_after(s);
+  return hipGetLastError();
 }
 
 hipError_t launch_ffn_pass(const FfnPassArgs& p, hipStream_t s) {
   const Shape sh = pick_shape(p.dtype, p.small, p.mode);
-  const int NT = (p.N + sh.BNOUT - 1) / sh.BNOUT;
   const int64_t grid = max_entries(p.max_rows, p.G, p.N, sh);
   if (grid == 0) return hipSuccess;
   int32_t* count = static_cast<int32_t*>(p.plan);
   PlanEntry* plan = reinterpret_cast<PlanEntry*>(static_cast<char*>(p.plan) + 16);
-  const char* nm1 = p.seg_offsets ? "ffn_plan" : "ffn_plan_shared";
-  prof_before(nm1, s);
-  ffn_plan_kernel<<<1, 1024, 0, s>>>(p.seg_offsets, p.G, p.dense_rows, sh.BM, NT, plan, count);
-  prof_after(s);
   KArgs k;
   k.A = static_cast<const uint16_t*>(p.A);
   k.W = static_cast<const uint16_t*>(p.w);
@@ -411,6 +422,8 @@ hipError_t launch_ffn_pass(const FfnPassArgs& p, hipStream_t s) {
   k.C = static_cast<uint16_t*>(p.C);
   k.plan = plan;
   k.count = count;
+  k.a_rows = p.a_rows;
+  k.a_div = p.a_div > 0 ? p.a_div : 1;
   k.K = p.K;
   k.N = p.N;
   k.a_seg_rows = p.a_seg_rows;
@@ -426,7 +439,7 @@ hipError_t launch_ffn_pass(const FfnPassArgs& p, hipStream_t s) {
       default: ffn_f32_kernel<MODE_SWIGLU><<<(unsigned)grid, 256, 0, s>>>(k); break;
     }
   } else if (p.small) {
-    launch_bf16<64, 128, 1, 4, 3>(p.mode, (unsigned)grid, k, s);
+    launch_bf16<32, 128, 1, 4, 4>(p.mode, (unsigned)grid, k, s);
   } else {
     launch_bf16<256, 256, 2, 4, 2>(p.mode, (unsigned)grid, k, s);
   }

@@ -20,9 +20,11 @@ struct RouteArgs {
   float* logits;        // [T, E] or null
   int32_t* topk_idx;    // [T, k]
   float* topk_gate;     // [T, k]
+  float* partial;       // optional workspace for the split-K small-batch path
   int64_t T;
   int d, E, k, gating, dtype;
 };
+size_t route_ws_bytes(int64_t T, int E, int dtype);
 hipError_t launch_route(const RouteArgs& a, hipStream_t s);
 
 struct PermuteArgs {
@@ -47,7 +49,9 @@ hipError_t launch_permute(const PermuteArgs& a, hipStream_t s);
 //   C[r, n] = epilogue( sum_k A[r, k] * W_seg[n, k] )  for r in the segment.
 // mode: 0 = plain, 1 = relu, 2 = gelu, 3 = swiglu (W1 = w, W3 = w_up).
 struct FfnPassArgs {
-  const void* A;          // [rows, K] dtype
+  const void* A;          // [rows, K] dtype, or [T, K] read through a_rows
+  const int32_t* a_rows;  // optional: A row of permuted row p is a_rows[p] / a_div
+  int a_div;
   const void* w;          // [G, N_w, K] dtype (gate / only matrix)
   const void* w_up;       // [G, N_w, K] dtype (SwiGLU up) or null
   void* C;                // [rows, N] dtype
@@ -63,6 +67,9 @@ struct FfnPassArgs {
   bool small;             // small-batch (decode) tile shape
 };
 size_t ffn_plan_bytes(int64_t max_rows, int G, int N, bool small, int dtype);
+// One plan kernel for the two passes of an expert FFN (same row tiles; the
+// entries go to p1.plan and p2.plan), then one GEMM launch per pass.
+hipError_t launch_ffn_plans(const FfnPassArgs& p1, const FfnPassArgs& p2, hipStream_t s);
 hipError_t launch_ffn_pass(const FfnPassArgs& a, hipStream_t s);
 
 struct CombineArgs {

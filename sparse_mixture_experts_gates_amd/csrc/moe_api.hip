@@ -109,7 +109,7 @@ PermWs perm_ws(const moe_config_t* c, int64_t T) {
 }
 
 struct FfnWs {
-  size_t H, Hs, plan, total;
+  size_t H, Hs, plan1, plan2, plan3, plan4, total;
 };
 FfnWs ffn_ws(const moe_config_t* c, int64_t T) {
   FfnWs w;
@@ -120,23 +120,22 @@ FfnWs ffn_ws(const moe_config_t* c, int64_t T) {
   o += up((size_t)R * c->d_ff * esize(c));
   w.Hs = o;
   o += up((size_t)S * T * (S ? c->d_ff_shared : 0) * esize(c));
-  size_t pb = ffn_plan_bytes(R, c->num_experts, c->d_ff, small_batch(R), c->dtype);
-  size_t p2 = ffn_plan_bytes(R, c->num_experts, c->d, small_batch(R), c->dtype);
-  if (p2 > pb) pb = p2;
+  w.plan1 = o;
+  o += ffn_plan_bytes(R, c->num_experts, c->d_ff, small_batch(R), c->dtype);
+  w.plan2 = o;
+  o += ffn_plan_bytes(R, c->num_experts, c->d, small_batch(R), c->dtype);
+  w.plan3 = w.plan4 = o;
   if (S) {
-    const size_t p3 = ffn_plan_bytes((int64_t)S * T, S, c->d_ff_shared, small_batch(T), c->dtype);
-    const size_t p4 = ffn_plan_bytes((int64_t)S * T, S, c->d, small_batch(T), c->dtype);
-    if (p3 > pb) pb = p3;
-    if (p4 > pb) pb = p4;
+    o += ffn_plan_bytes((int64_t)S * T, S, c->d_ff_shared, small_batch(T), c->dtype);
+    w.plan4 = o;
+    o += ffn_plan_bytes((int64_t)S * T, S, c->d, small_batch(T), c->dtype);
   }
-  w.plan = o;
-  o += up(pb);
   w.total = o;
   return w;
 }
 
 struct FwdWs {
-  size_t idx, gate, counts, dropped, offsets, perm_src, slot_pos, x_perm, eout, sout, perm, ffn,
+  size_t idx, gate, counts, dropped, offsets, perm_src, slot_pos, eout, sout, route, perm, ffn,
       total;
 };
 FwdWs fwd_ws(const moe_config_t* c, int64_t T) {
@@ -150,9 +149,9 @@ FwdWs fwd_ws(const moe_config_t* c, int64_t T) {
   w.offsets = o; o += up((size_t)(c->num_experts + 1) * 4);
   w.perm_src = o; o += up((size_t)R * 4);
   w.slot_pos = o; o += up((size_t)R * 4);
-  w.x_perm = o; o += up((size_t)R * c->d * esize(c));
   w.eout = o; o += up((size_t)R * c->d * esize(c));
   w.sout = o; o += up((size_t)c->num_shared * T * c->d * esize(c));
+  w.route = o; o += up(route_ws_bytes(T, c->num_experts, c->dtype));
   w.perm = o; o += perm_ws(c, T).total;
   w.ffn = o; o += ffn_ws(c, T).total;
   w.total = o;
@@ -165,9 +164,9 @@ moe_status_t hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ER
 
 moe_status_t do_route(const moe_config_t* c, int64_t T, const void* x, const void* wr,
                       const float* off, const float* bias, float* logits, int32_t* idx,
-                      float* gate, hipStream_t s) {
-  RouteArgs a{x, wr, off, bias, logits, idx, gate, T, c->d, c->num_experts, c->top_k,
-              c->gating, c->dtype};
+                      float* gate, void* ws, hipStream_t s) {
+  RouteArgs a{x, wr, off, bias, logits, idx, gate, static_cast<float*>(ws), T, c->d,
+              c->num_experts, c->top_k, c->gating, c->dtype};
   return hip_status(launch_route(a, s));
 }
 
@@ -196,16 +195,20 @@ moe_status_t do_permute(const moe_config_t* c, int64_t T, const int32_t* idx, co
   return hip_status(launch_permute(a, s));
 }
 
+// x_perm may be null when perm_src is given: the first GEMM then reads the
+// rows of x through perm_src (row gather folded into its operand loads).
 moe_status_t do_ffn(const moe_config_t* c, int64_t T, const void* x, const void* x_perm,
-                    const int32_t* offsets, const void* w1, const void* w3, const void* w2,
-                    const void* ws1, const void* ws3, const void* ws2, void* eout, void* sout,
-                    void* ws, hipStream_t s) {
+                    const int32_t* perm_src, const int32_t* offsets, const void* w1,
+                    const void* w3, const void* w2, const void* ws1, const void* ws3,
+                    const void* ws2, void* eout, void* sout, void* ws, hipStream_t s) {
   const FfnWs w = ffn_ws(c, T);
   const int64_t R = T * c->top_k;
   const int mode1 = c->act == MOE_ACT_SWIGLU ? 3 : (c->act == MOE_ACT_GELU ? 2 : 1);
   FfnPassArgs p;
   memset(&p, 0, sizeof(p));
-  p.A = x_perm;
+  p.A = x_perm ? x_perm : x;
+  p.a_rows = x_perm ? nullptr : perm_src;
+  p.a_div = c->top_k;
   p.w = w1;
   p.w_up = c->act == MOE_ACT_SWIGLU ? w3 : nullptr;
   p.C = at(ws, w.H);
@@ -215,20 +218,22 @@ moe_status_t do_ffn(const moe_config_t* c, int64_t T, const void* x, const void*
   p.N = c->d_ff;
   p.mode = mode1;
   p.dtype = c->dtype;
-  p.plan = at(ws, w.plan);
+  p.plan = at(ws, w.plan1);
   p.max_rows = R;
   p.small = small_batch(R);
-  hipError_t e = launch_ffn_pass(p, s);
-  if (e != hipSuccess) return MOE_ERR_HIP;
-  p.A = at(ws, w.H);
-  p.w = w2;
-  p.w_up = nullptr;
-  p.C = eout;
-  p.K = c->d_ff;
-  p.N = c->d;
-  p.mode = 0;
-  e = launch_ffn_pass(p, s);
-  if (e != hipSuccess) return MOE_ERR_HIP;
+  FfnPassArgs p2 = p;
+  p2.A = at(ws, w.H);
+  p2.a_rows = nullptr;
+  p2.w = w2;
+  p2.w_up = nullptr;
+  p2.C = eout;
+  p2.K = c->d_ff;
+  p2.N = c->d;
+  p2.mode = 0;
+  p2.plan = at(ws, w.plan2);
+  if (launch_ffn_plans(p, p2, s) != hipSuccess) return MOE_ERR_HIP;
+  if (launch_ffn_pass(p, s) != hipSuccess) return MOE_ERR_HIP;
+  if (launch_ffn_pass(p2, s) != hipSuccess) return MOE_ERR_HIP;
   if (c->num_shared > 0) {
     const int S = c->num_shared;
     FfnPassArgs q;
@@ -246,22 +251,22 @@ moe_status_t do_ffn(const moe_config_t* c, int64_t T, const void* x, const void*
     q.dtype = c->dtype;
     q.a_seg_rows = 0;
     q.c_seg_rows = T;
-    q.plan = at(ws, w.plan);
+    q.plan = at(ws, w.plan3);
     q.max_rows = (int64_t)S * T;
     q.small = small_batch(T);
-    e = launch_ffn_pass(q, s);
-    if (e != hipSuccess) return MOE_ERR_HIP;
-    q.A = at(ws, w.Hs);
-    q.w = ws2;
-    q.w_up = nullptr;
-    q.C = sout;
-    q.K = c->d_ff_shared;
-    q.N = c->d;
-    q.mode = 0;
-    q.a_seg_rows = T;
-    q.c_seg_rows = T;
-    e = launch_ffn_pass(q, s);
-    if (e != hipSuccess) return MOE_ERR_HIP;
+    FfnPassArgs q2 = q;
+    q2.A = at(ws, w.Hs);
+    q2.w = ws2;
+    q2.w_up = nullptr;
+    q2.C = sout;
+    q2.K = c->d_ff_shared;
+    q2.N = c->d;
+    q2.mode = 0;
+    q2.a_seg_rows = T;
+    q2.plan = at(ws, w.plan4);
+    if (launch_ffn_plans(q, q2, s) != hipSuccess) return MOE_ERR_HIP;
+    if (launch_ffn_pass(q, s) != hipSuccess) return MOE_ERR_HIP;
+    if (launch_ffn_pass(q2, s) != hipSuccess) return MOE_ERR_HIP;
   }
   return MOE_OK;
 }
@@ -309,7 +314,8 @@ moe_status_t moe_capacity(const moe_config_t* cfg, int64_t T, int64_t* capacity)
 
 moe_status_t moe_route(const moe_config_t* cfg, int64_t T, const void* x, const void* w_router,
                        const float* logit_offset, const float* select_bias, float* logits,
-                       int32_t* topk_idx, float* topk_gate, void* stream) {
+                       int32_t* topk_idx, float* topk_gate, void* workspace, size_t ws_bytes,
+                       void* stream) {
   moe_status_t st = check_cfg(cfg, T);
   if (st != MOE_OK) return st;
   if (T == 0) return MOE_OK;  // nothing to do; token-sized pointers may be null
@@ -318,8 +324,11 @@ moe_status_t moe_route(const moe_config_t* cfg, int64_t T, const void* x, const 
       (logits && !al(logits, 4)) || (logit_offset && !al(logit_offset, 4)) ||
       (select_bias && !al(select_bias, 4)))
     return MOE_ERR_INVALID_ARG;
+  if (workspace && !al(workspace, ALIGN)) return MOE_ERR_INVALID_ARG;
+  const size_t need = route_ws_bytes(T, cfg->num_experts, cfg->dtype);
+  void* part = (workspace && ws_bytes >= need && need > 0) ? workspace : nullptr;
   return do_route(cfg, T, x, w_router, logit_offset, select_bias, logits, topk_idx, topk_gate,
-                  static_cast<hipStream_t>(stream));
+                  part, static_cast<hipStream_t>(stream));
 }
 
 moe_status_t moe_permute(const moe_config_t* cfg, int64_t T, const int32_t* topk_idx,
@@ -358,8 +367,8 @@ moe_status_t moe_expert_ffn(const moe_config_t* cfg, int64_t T, const void* x,
   if (!al(expert_offsets, 4)) return MOE_ERR_INVALID_ARG;
   if (!workspace || !al(workspace, ALIGN)) return MOE_ERR_INVALID_ARG;
   if (ws_bytes < fwd_ws(cfg, T).total) return MOE_ERR_WORKSPACE;
-  return do_ffn(cfg, T, x, x_perm, expert_offsets, w1, w3, w2, ws1, ws3, ws2, expert_out,
-                shared_out, workspace, static_cast<hipStream_t>(stream));
+  return do_ffn(cfg, T, x, x_perm, nullptr, expert_offsets, w1, w3, w2, ws1, ws3, ws2,
+                expert_out, shared_out, workspace, static_cast<hipStream_t>(stream));
 }
 
 moe_status_t moe_combine(const moe_config_t* cfg, int64_t T, const void* expert_out,
@@ -405,15 +414,15 @@ moe_status_t moe_forward(const moe_config_t* cfg, int64_t T, const void* x, cons
   int32_t* offsets = reinterpret_cast<int32_t*>(at(workspace, w.offsets));
   int32_t* perm_src = reinterpret_cast<int32_t*>(at(workspace, w.perm_src));
   int32_t* slot_pos = reinterpret_cast<int32_t*>(at(workspace, w.slot_pos));
-  void* x_perm = at(workspace, w.x_perm);
   void* eout = at(workspace, w.eout);
   void* sout = cfg->num_shared > 0 ? at(workspace, w.sout) : nullptr;
-  st = do_route(cfg, T, x, w_router, logit_offset, select_bias, nullptr, idx, gate, s);
+  st = do_route(cfg, T, x, w_router, logit_offset, select_bias, nullptr, idx, gate,
+                route_ws_bytes(T, cfg->num_experts, cfg->dtype) ? at(workspace, w.route) : nullptr, s);
   if (st != MOE_OK) return st;
-  st = do_permute(cfg, T, idx, x, counts, offsets, perm_src, slot_pos, dropped, x_perm,
+  st = do_permute(cfg, T, idx, x, counts, offsets, perm_src, slot_pos, dropped, nullptr,
                   at(workspace, w.perm), s);
   if (st != MOE_OK) return st;
-  st = do_ffn(cfg, T, x, x_perm, offsets, w1, w3, w2, ws1, ws3, ws2, eout, sout,
+  st = do_ffn(cfg, T, x, nullptr, perm_src, offsets, w1, w3, w2, ws1, ws3, ws2, eout, sout,
               at(workspace, w.ffn), s);
   if (st != MOE_OK) return st;
   return do_combine(cfg, T, eout, slot_pos, gate, sout, y, s);

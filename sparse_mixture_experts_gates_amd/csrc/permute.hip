@@ -140,6 +140,117 @@ __global__ __launch_bounds__(64) void permute_scatter_kernel(
   }
 }
 
+// All of the above in one workgroup of 16 waves, for up to FUSED_MAX slots:
+// wave w owns a contiguous run of the slots; pass 1 counts its run per expert
+// (ballot groups, no atomics), the per-expert prefix over waves gives each
+// wave's starting ranks and the counts, capacity and offsets, and pass 2
+// re-walks the run to place every slot.  Same results as the three kernels.
+constexpr int FUSED_MAX = 2048;
+constexpr int FUSED_WAVES = 16;
+
+__device__ __forceinline__ uint64_t expert_peers(int e, bool valid) {
+  uint64_t peers = __ballot(valid);
+#pragma unroll
+  for (int b = 0; b < 8; ++b) {
+    const bool bit = (e >> b) & 1;
+    const uint64_t bb = __ballot(bit);
+    peers &= bit ? bb : ~bb;
+  }
+  return peers;
+}
+
+__global__ __launch_bounds__(1024) void permute_fused_kernel(
+    const int32_t* __restrict__ idx, int n, int E, int64_t cap, int32_t* __restrict__ counts,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ perm_src,
+    int32_t* __restrict__ slot_pos, int32_t* __restrict__ num_dropped,
+    int32_t* __restrict__ kept_total) {
+  __shared__ int run[FUSED_WAVES][256];
+  __shared__ int sk[256];
+  __shared__ int sdrop[256];
+  __shared__ int soff[256];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int per = ((n + FUSED_WAVES * 64 - 1) / (FUSED_WAVES * 64)) * 64;  // slots per wave
+  const int lo = w * per;
+  const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  for (int e = lane; e < 256; e += 64) run[w][e] = 0;
+  __syncthreads();
+  // pass 1: per-wave counts
+  for (int st = 0; st < per; st += 64) {
+    const int a = lo + st + lane;
+    int e = -1;
+    bool valid = a < n;
+    if (valid) {
+      e = idx[a];
+      valid = e >= 0 && e < E;
+    }
+    const uint64_t peers = expert_peers(e, valid);
+    if (valid && (peers & lt) == 0) run[w][e] += __popcll(peers);
+  }
+  __syncthreads();
+  // per expert: exclusive prefix over waves, counts, capacity
+  if (tid < 256) {
+    const int e = tid;
+    int tot = 0;
+    for (int v = 0; v < FUSED_WAVES; ++v) {
+      const int c = run[v][e];
+      run[v][e] = tot;
+      tot += c;
+    }
+    const int kept = e < E ? (cap < 0 ? tot : (int)(tot < cap ? tot : cap)) : 0;
+    sk[e] = kept;
+    sdrop[e] = e < E ? tot - kept : 0;
+    if (e < E && counts) counts[e] = tot;
+  }
+  __syncthreads();
+  for (int off = 1; off < 256; off <<= 1) {
+    int v = 0, u = 0;
+    if (tid < 256 && tid >= off) {
+      v = sk[tid - off];
+      u = sdrop[tid - off];
+    }
+    __syncthreads();
+    if (tid < 256) {
+      sk[tid] += v;
+      sdrop[tid] += u;
+    }
+    __syncthreads();
+  }
+  if (tid < 256) soff[tid] = tid == 0 ? 0 : sk[tid - 1];
+  if (tid < E) offsets[tid + 1] = sk[tid];
+  if (tid == 0) {
+    offsets[0] = 0;
+    if (num_dropped) num_dropped[0] = sdrop[255];
+    kept_total[0] = sk[255];
+  }
+  __syncthreads();
+  const int total = sk[255];
+  // pass 2: place every slot of this wave's run
+  for (int st = 0; st < per; st += 64) {
+    const int a = lo + st + lane;
+    int e = -1;
+    bool valid = a < n;
+    if (valid) {
+      e = idx[a];
+      valid = e >= 0 && e < E;
+    }
+    const uint64_t peers = expert_peers(e, valid);
+    int r = 0;
+    if (valid) r = run[w][e] + __popcll(peers & lt);
+    __builtin_amdgcn_wave_barrier();
+    if (valid && (peers & lt) == 0) run[w][e] += __popcll(peers);
+    if (a < n) {
+      if (valid && (cap < 0 || r < cap)) {
+        const int p = soff[e] + r;
+        slot_pos[a] = p;
+        perm_src[p] = a;
+      } else {
+        slot_pos[a] = -1;
+      }
+      if (a >= total) perm_src[a] = -1;
+    }
+  }
+}
+
 // x_perm[p] = x[perm_src[p] / k] for p < kept_total; one wave per row.
 template <typename VT, int EPV>
 __global__ __launch_bounds__(256) void gather_rows_kernel(
@@ -160,6 +271,13 @@ int permute_nblocks(int64_t rows) { return (int)((rows + CH - 1) / CH); }
 hipError_t launch_permute(const PermuteArgs& a, hipStream_t s) {
   const int64_t n = a.T * a.k;
   if (n == 0) return hipSuccess;
+  if (n <= FUSED_MAX) {
+    prof_before("permute", s);
+    permute_fused_kernel<<<1, 1024, 0, s>>>(a.topk_idx, (int)n, a.E, a.capacity, a.counts,
+                                            a.offsets, a.perm_src, a.slot_pos, a.num_dropped,
+                                            a.kept_total);
+    prof_after(s);
+  } else {
   const int nb = permute_nblocks(n);
   prof_before("permute_count", s);
   permute_count_kernel<<<nb, 256, 0, s>>>(a.topk_idx, n, a.E, a.block_counts);
@@ -172,6 +290,7 @@ hipError_t launch_permute(const PermuteArgs& a, hipStream_t s) {
   permute_scatter_kernel<<<nb, 64, 0, s>>>(a.topk_idx, n, a.E, a.capacity, a.block_counts,
                                            a.offsets, a.kept_total, a.perm_src, a.slot_pos);
   prof_after(s);
+  }
   if (a.x_perm) {
     const unsigned grid = (unsigned)((n + 3) / 4);
     prof_before("gather", s);

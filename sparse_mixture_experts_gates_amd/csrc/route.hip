@@ -6,13 +6,14 @@
 // Inside the Model ch. 14, "Auxiliary-loss-free balancing"], all in FP32 as
 // the LLM tutorial's "Training instability" section requires of the router.
 //
-// One workgroup (4 waves) owns 64 tokens and all E (<= 256) experts.  The
-// K loop stages 64-wide slabs of x and W_r in LDS (XOR-swizzled 16-byte
-// chunks, double-buffered through registers) and runs v_mfma_f32_16x16x32_bf16
-// with experts on the MFMA row side and tokens on the column side.  The fp32
-// scores of the tile then go to LDS, and each wave selects the top-k of its
-// tokens with 64-bit (key, ~index) maxima reduced by cross-lane shuffles, so
-// ties resolve to the lower expert index.
+// One workgroup (4 waves) owns BT tokens (16..64, fewer for small E so the
+// grid covers the chip) and all E (<= 256) experts.  The K loop streams
+// 64-wide slabs of x and W_r into an LDS ring with direct-to-LDS loads (whole
+// 128-byte lines, XOR-swizzled chunks, several slabs in flight) and runs
+// v_mfma_f32_16x16x32_bf16 with experts on the MFMA row side and tokens on the
+// column side.  The fp32 scores of the tile then go to LDS, and each wave
+// selects the top-k of its tokens with 64-bit (key, ~index) maxima reduced by
+// cross-lane shuffles, so ties resolve to the lower expert index.
 #include "common.h"
 #include "launch.h"
 
@@ -20,16 +21,12 @@ namespace moe {
 
 namespace {
 
-constexpr int RT_BT = 64;       // tokens per workgroup
-constexpr int RT_BK = 64;       // K slab (elements)
+constexpr int RT_BT = 64;       // tokens per workgroup (fp32 path)
 constexpr int RT_THREADS = 256;
 
-__device__ __forceinline__ int swz(int row, int chunk) {  // bf16 element offset
-  return row * RT_BK + ((chunk ^ (row & 7)) << 3);
-}
-
-// Top-k and gates for the 64 tokens whose scores sit in lg[64][ld].
-template <int EP>
+// Top-k and gates for the BT tokens whose scores sit in lg[BT][ld]; each of
+// the 4 waves handles BT/4 tokens.
+template <int EP, int BT>
 __device__ void topk_from_lds(const float* lg, int ld, const RouteArgs& a,
                               int64_t t0) {
   constexpr int TPW = EP <= 16 ? 4 : (EP <= 32 ? 2 : 1);  // tokens per wave pass
@@ -38,8 +35,9 @@ __device__ void topk_from_lds(const float* lg, int ld, const RouteArgs& a,
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int sl = lane % LPT;
   const int E = a.E, k = a.k;
-  for (int tg = 0; tg < 16 / TPW; ++tg) {
-    const int tl = wave * 16 + tg * TPW + lane / LPT;
+  static_assert((BT / 4) % TPW == 0, "tokens per wave");
+  for (int tg = 0; tg < (BT / 4) / TPW; ++tg) {
+    const int tl = wave * (BT / 4) + tg * TPW + lane / LPT;
     const int64_t t = t0 + tl;
     const float* row = lg + tl * ld;
     uint64_t key[KPL];
@@ -140,76 +138,47 @@ __device__ void topk_from_lds(const float* lg, int ld, const RouteArgs& a,
   }
 }
 
-template <int EP>
-struct RouteLds {
-  static constexpr int SX = RT_BT * RT_BK;   // bf16 elements per x stage
-  static constexpr int SW = EP * RT_BK;      // bf16 elements per w stage
-  static constexpr int STAGE_BYTES = 2 * (SX + SW) * 2;
-  static constexpr int LD = EP + 4;
-  static constexpr int LOGIT_BYTES = RT_BT * LD * 4;
-  static constexpr int BYTES = STAGE_BYTES > LOGIT_BYTES ? STAGE_BYTES : LOGIT_BYTES;
-};
-
-template <int EP>
+template <int EP, int BT, int NSTAGE>
 __global__ __launch_bounds__(RT_THREADS) void route_bf16_kernel(RouteArgs a) {
-  using L = RouteLds<EP>;
-  __shared__ __attribute__((aligned(16))) unsigned char smem[L::BYTES];
-  uint16_t* sx = reinterpret_cast<uint16_t*>(smem);        // [2][SX]
-  uint16_t* sw = sx + 2 * L::SX;                           // [2][SW]
-  float* lg = reinterpret_cast<float*>(smem);              // aliased after the K loop
+  constexpr int ROWS = BT + EP;                  // x rows then W_r rows per slab
+  constexpr int NG = ROWS / 8, DPW = NG / 4;     // 8-row load groups; per wave
+  static_assert(NG % 4 == 0, "load groups must divide over the 4 waves");
+  constexpr int SEL = ROWS * 64;                 // bf16 elements per slab
+  constexpr int LD = EP + 4;
+  constexpr int RING_BYTES = NSTAGE * SEL * 2;
+  constexpr int LOGIT_BYTES = BT * LD * 4;
+  __shared__ __attribute__((aligned(1024)))
+  unsigned char smem[RING_BYTES > LOGIT_BYTES ? RING_BYTES : LOGIT_BYTES];
+  uint16_t* ring = reinterpret_cast<uint16_t*>(smem);
+  float* lg = reinterpret_cast<float*>(smem);    // aliased after the K loop
 
-  constexpr int ET = EP / 16, TT = RT_BT / 16;
+  constexpr int ET = EP / 16, TT = BT / 16;
   constexpr int WE = ET < 4 ? ET : 4, WT = 4 / WE;
-  constexpr int NE = ET / WE, NT = TT / WT;
-  constexpr int CHUNKS = (RT_BT + EP) * 8;
-  constexpr int CPT = (CHUNKS + RT_THREADS - 1) / RT_THREADS;
+  constexpr int NE = ET / WE, NT = (TT + WT - 1) / WT;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int we = wave % WE, wt = wave / WE;
-  const int64_t t0 = (int64_t)blockIdx.x * RT_BT;
+  const int64_t t0 = (int64_t)blockIdx.x * BT;
   const int d = a.d, E = a.E;
   const uint16_t* X = static_cast<const uint16_t*>(a.x);
   const uint16_t* W = static_cast<const uint16_t*>(a.w);
 
-  const uint16_t* src[CPT];
-  int dst[CPT];
+  const uint16_t* src[DPW];
 #pragma unroll
-  for (int i = 0; i < CPT; ++i) {
-    const int c = tid + i * RT_THREADS;
-    src[i] = nullptr;
-    dst[i] = -1;
-    if (c < CHUNKS) {
-      const int row = c >> 3, ch = c & 7;
-      if (row < RT_BT) {
-        int64_t t = t0 + row;
-        if (t > a.T - 1) t = a.T - 1;
-        src[i] = X + t * d + ch * 8;
-        dst[i] = swz(row, ch);
-      } else {
-        int e = row - RT_BT;
-        if (e > E - 1) e = E - 1;
-        src[i] = W + (int64_t)e * d + ch * 8;
-        dst[i] = L::SX * 2 + swz(row - RT_BT, ch);   // offset into sw region of stage 0
-      }
+  for (int i = 0; i < DPW; ++i) {
+    const int row = (wave + i * 4) * 8 + dma_row(lane);
+    const int ch = dma_chunk(lane);
+    if (row < BT) {
+      int64_t t = t0 + row;
+      if (t > a.T - 1) t = a.T - 1;
+      src[i] = X + t * d + ch * 8;
+    } else {
+      int e = row - BT;
+      if (e > E - 1) e = E - 1;
+      src[i] = W + (int64_t)e * d + ch * 8;
     }
   }
-  u32x4_t stage[CPT];
-  auto gload = [&](int k0) {
-#pragma unroll
-    for (int i = 0; i < CPT; ++i)
-      if (dst[i] >= 0) stage[i] = *reinterpret_cast<const u32x4_t*>(src[i] + k0);
-  };
-  auto lstore = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-      if (dst[i] < 0) continue;
-      int off = dst[i];
-      // x chunks live in sx[buf], w chunks in sw[buf]
-      uint16_t* base = off >= L::SX * 2 ? sw + buf * L::SW + (off - L::SX * 2)
-                                        : sx + buf * L::SX + off;
-      *reinterpret_cast<u32x4_t*>(base) = stage[i];
-    }
-  };
 
   f32x4_t acc[NE][NT];
 #pragma unroll
@@ -217,59 +186,239 @@ __global__ __launch_bounds__(RT_THREADS) void route_bf16_kernel(RouteArgs a) {
 #pragma unroll
     for (int j = 0; j < NT; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  const int nk = d / RT_BK;
-  gload(0);
-  lstore(0);
-  __syncthreads();
+  const int nk = d / 64;
+#pragma unroll
+  for (int s = 0; s < NSTAGE - 1; ++s) {
+    const int kk = s < nk ? s : nk - 1;
+#pragma unroll
+    for (int i = 0; i < DPW; ++i) dma_rows(src[i] + kk * 64, ring + s * SEL + (wave + i * 4) * 512);
+  }
+  int cur_s = 0, nxt_s = NSTAGE - 1;
   for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < nk) gload((kt + 1) * RT_BK);
-    const uint16_t* bx = sx + buf * L::SX;
-    const uint16_t* bw = sw + buf * L::SW;
+    wait_vm_lgkm0<(NSTAGE - 2) * DPW>();
+    ring_barrier();
+    const int kn = kt + NSTAGE - 1 < nk ? kt + NSTAGE - 1 : nk - 1;
+#pragma unroll
+    for (int i = 0; i < DPW; ++i) dma_rows(src[i] + kn * 64, ring + nxt_s * SEL + (wave + i * 4) * 512);
+    const uint16_t* bx = ring + cur_s * SEL;
+    const uint16_t* bw = bx + BT * 64;
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
       const int ch = kk * 4 + (lane >> 4);
       bf16x8_t fx[NT], fw[NE];
 #pragma unroll
       for (int j = 0; j < NT; ++j) {
-        const int row = (wt + j * WT) * 16 + (lane & 15);
-        fx[j] = *reinterpret_cast<const bf16x8_t*>(bx + swz(row, ch));
+        const int tt = wt + j * WT;
+        fx[j] = *reinterpret_cast<const bf16x8_t*>(bx + swz((tt < TT ? tt : 0) * 16 + (lane & 15), ch));
       }
 #pragma unroll
-      for (int i = 0; i < NE; ++i) {
-        const int row = (we + i * WE) * 16 + (lane & 15);
-        fw[i] = *reinterpret_cast<const bf16x8_t*>(bw + swz(row, ch));
-      }
+      for (int i = 0; i < NE; ++i)
+        fw[i] = *reinterpret_cast<const bf16x8_t*>(bw + swz((we + i * WE) * 16 + (lane & 15), ch));
 #pragma unroll
       for (int i = 0; i < NE; ++i)
 #pragma unroll
         for (int j = 0; j < NT; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fw[i], fx[j], acc[i][j], 0, 0, 0);
     }
-    if (kt + 1 < nk) lstore(buf ^ 1);
-    __syncthreads();
+    cur_s = cur_s + 1 == NSTAGE ? 0 : cur_s + 1;
+    nxt_s = nxt_s + 1 == NSTAGE ? 0 : nxt_s + 1;
   }
+  wait_vm_lgkm0<0>();
+  ring_barrier();   // every wave is done with the ring before it becomes the score tile
   // scores -> LDS: lane holds experts 4*(lane/16)+r of tile i, token lane%16 of tile j
 #pragma unroll
   for (int i = 0; i < NE; ++i)
 #pragma unroll
-    for (int j = 0; j < NT; ++j)
+    for (int j = 0; j < NT; ++j) {
+      const int tt = wt + j * WT;
+      if (tt >= TT) continue;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int e = (we + i * WE) * 16 + 4 * (lane >> 4) + r;
-        const int tl = (wt + j * WT) * 16 + (lane & 15);
+        const int tl = tt * 16 + (lane & 15);
         float v = acc[i][j][r];
         if (a.offset && e < E) v += a.offset[e];
-        lg[tl * L::LD + e] = v;
+        lg[tl * LD + e] = v;
       }
+    }
   __syncthreads();
   if (a.logits) {
-    for (int idx = tid; idx < RT_BT * E; idx += RT_THREADS) {
+    for (int idx = tid; idx < BT * E; idx += RT_THREADS) {
       const int tl = idx / E, e = idx - tl * E;
-      if (t0 + tl < a.T) a.logits[(t0 + tl) * E + e] = lg[tl * L::LD + e];
+      if (t0 + tl < a.T) a.logits[(t0 + tl) * E + e] = lg[tl * LD + e];
     }
   }
-  topk_from_lds<EP>(lg, L::LD, a, t0);
+  topk_from_lds<EP, BT>(lg, LD, a, t0);
+}
+
+// Small batches (T <= 16, bf16): one workgroup of 8 waves splits the K
+// dimension instead of the tokens.  Wave w takes the 32-wide k steps
+// s = w, w+8, ...; its operands come straight from global memory into the
+// MFMA operand registers (16 bytes per lane: token or expert row l%16, k
+// chunk l/16), two steps in flight.  The 8 partial score tiles are summed in
+// LDS in wave order (deterministic), then the usual top-k runs.
+constexpr int RS_WAVES = 8;
+constexpr int RS_THREADS = 64 * RS_WAVES;
+
+template <int EP>
+__global__ __launch_bounds__(RS_THREADS) void route_small_kernel(RouteArgs a) {
+  constexpr int ET = EP / 16, LD = EP + 4;
+  __shared__ float lg[16 * LD];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int d = a.d, E = a.E;
+  const uint16_t* X = static_cast<const uint16_t*>(a.x);
+  const uint16_t* W = static_cast<const uint16_t*>(a.w);
+  int t = lane & 15;
+  if (t > a.T - 1) t = (int)a.T - 1;
+  const uint16_t* xrow = X + (int64_t)t * d + 8 * (lane >> 4);
+  const uint16_t* wrow[ET];
+#pragma unroll
+  for (int i = 0; i < ET; ++i) {
+    int e = i * 16 + (lane & 15);
+    if (e > E - 1) e = E - 1;
+    wrow[i] = W + (int64_t)e * d + 8 * (lane >> 4);
+  }
+  f32x4_t acc[ET];
+#pragma unroll
+  for (int i = 0; i < ET; ++i) acc[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  const int ns = d / 32;
+  constexpr int STEP = EP <= 128 ? 2 : 1;   // k steps in flight per wave
+  for (int st = wave; st < ns; st += STEP * RS_WAVES) {
+    const int st2 = st + RS_WAVES;
+    const bool two = STEP == 2 && st2 < ns;
+    const bf16x8_t x0 = *reinterpret_cast<const bf16x8_t*>(xrow + st * 32);
+    bf16x8_t w0[ET], w1[ET], x1 = x0;
+#pragma unroll
+    for (int i = 0; i < ET; ++i) w0[i] = *reinterpret_cast<const bf16x8_t*>(wrow[i] + st * 32);
+    if (two) {
+      x1 = *reinterpret_cast<const bf16x8_t*>(xrow + st2 * 32);
+#pragma unroll
+      for (int i = 0; i < ET; ++i) w1[i] = *reinterpret_cast<const bf16x8_t*>(wrow[i] + st2 * 32);
+    }
+#pragma unroll
+    for (int i = 0; i < ET; ++i) acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w0[i], x0, acc[i], 0, 0, 0);
+    if (two) {
+#pragma unroll
+      for (int i = 0; i < ET; ++i) acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w1[i], x1, acc[i], 0, 0, 0);
+    }
+  }
+  // sum the partial tiles in wave order
+  for (int w = 0; w < RS_WAVES; ++w) {
+    if (wave == w) {
+#pragma unroll
+      for (int i = 0; i < ET; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int e = i * 16 + 4 * (lane >> 4) + r;
+          float* dst = &lg[(lane & 15) * LD + e];
+          *dst = (w == 0 ? 0.f : *dst) + acc[i][r];
+        }
+    }
+    __syncthreads();
+  }
+  if (a.offset) {
+    for (int idx = tid; idx < 16 * E; idx += RS_THREADS) {
+      const int tl = idx / E, e = idx - tl * E;
+      lg[tl * LD + e] += a.offset[e];
+    }
+    __syncthreads();
+  }
+  if (a.logits) {
+    for (int idx = tid; idx < (int)a.T * E; idx += RS_THREADS) {
+      const int tl = idx / E, e = idx - tl * E;
+      a.logits[tl * E + e] = lg[tl * LD + e];
+    }
+  }
+  if (wave < 4) topk_from_lds<EP, 16>(lg, LD, a, 0);
+}
+
+// Small batches with a workspace: the same scores from many workgroups.
+// Workgroup (e, s) computes the 16-expert x 16-token tile e over the s-th
+// part of K (4 waves, operands straight from global memory), sums its waves
+// in LDS in wave order and stores the partial tile; one more workgroup adds
+// the parts in order and runs the top-k.  Deterministic, and the weights are
+// read by the whole chip instead of one CU.
+constexpr int RP_MAX_SPLIT = 64;
+
+template <int EP>
+__global__ __launch_bounds__(256) void route_partial_kernel(RouteArgs a, int nsplit) {
+  __shared__ float red[16 * 17];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int et = blockIdx.x, ks = blockIdx.y;
+  const int d = a.d, E = a.E;
+  const uint16_t* X = static_cast<const uint16_t*>(a.x);
+  const uint16_t* W = static_cast<const uint16_t*>(a.w);
+  int t = lane & 15;
+  if (t > a.T - 1) t = (int)a.T - 1;
+  int e = et * 16 + (lane & 15);
+  if (e > E - 1) e = E - 1;
+  const uint16_t* xrow = X + (int64_t)t * d + 8 * (lane >> 4);
+  const uint16_t* wrow = W + (int64_t)e * d + 8 * (lane >> 4);
+  const int ns = d / 32;
+  const int per = (ns + nsplit - 1) / nsplit;
+  const int s0 = ks * per, s1 = s0 + per < ns ? s0 + per : ns;
+  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+  for (int st = s0 + wave; st < s1; st += 4) {
+    const bf16x8_t xv = *reinterpret_cast<const bf16x8_t*>(xrow + st * 32);
+    const bf16x8_t wv = *reinterpret_cast<const bf16x8_t*>(wrow + st * 32);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wv, xv, acc, 0, 0, 0);
+  }
+  for (int w = 0; w < 4; ++w) {
+    if (wave == w) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        float* dst = &red[(lane & 15) * 17 + 4 * (lane >> 4) + r];
+        *dst = (w == 0 ? 0.f : *dst) + acc[r];
+      }
+    }
+    __syncthreads();
+  }
+  // partial[ks][token][EP]
+  float* out = a.partial + (int64_t)ks * 16 * EP;
+  const int tl = tid >> 4, ei = tid & 15;
+  out[tl * EP + et * 16 + ei] = red[tl * 17 + ei];
+}
+
+template <int EP>
+__global__ __launch_bounds__(1024) void route_reduce_topk_kernel(RouteArgs a, int nsplit) {
+  constexpr int LD = EP + 4;
+  __shared__ float lg[16 * LD];
+  const int tid = threadIdx.x, E = a.E;
+  for (int idx = tid; idx < 16 * EP; idx += 1024) {
+    const int tl = idx / EP, e = idx - tl * EP;
+    // parts added in order; eight loads in flight at a time
+    float v = 0.f;
+    int ks = 0;
+    for (; ks + 8 <= nsplit; ks += 8) {
+      float p[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) p[q] = a.partial[(int64_t)(ks + q) * 16 * EP + idx];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) v += p[q];
+    }
+    for (; ks < nsplit; ++ks) v += a.partial[(int64_t)ks * 16 * EP + idx];
+    if (a.offset && e < E) v += a.offset[e];
+    lg[tl * LD + e] = v;
+  }
+  __syncthreads();
+  if (a.logits) {
+    for (int idx = tid; idx < (int)a.T * E; idx += 1024) {
+      const int tl = idx / E, e = idx - tl * E;
+      a.logits[tl * E + e] = lg[tl * LD + e];
+    }
+  }
+  if (tid < 256) topk_from_lds<EP, 16>(lg, LD, a, 0);
+}
+
+int route_split(int d, int E) {
+  const int et = (E + 15) / 16;
+  int ns = d / 32;
+  int sp = 128 / et;
+  if (sp > ns / 2) sp = ns / 2;
+  if (sp > RP_MAX_SPLIT) sp = RP_MAX_SPLIT;
+  return sp < 1 ? 1 : sp;
 }
 
 // fp32 inputs: the same tile and top-k, scores by fp32 FMA from LDS slabs.
@@ -335,30 +484,43 @@ __global__ __launch_bounds__(RT_THREADS) void route_f32_kernel(RouteArgs a) {
       if (t0 + t < a.T) a.logits[(t0 + t) * E + e] = lg[t * LD + e];
     }
   }
-  topk_from_lds<EP>(lg, LD, a, t0);
+  topk_from_lds<EP, RT_BT>(lg, LD, a, t0);
 }
 
-template <int EP>
+template <int EP, int BT, int NS>
 hipError_t launch_ep(const RouteArgs& a, hipStream_t s) {
-  const unsigned grid = (unsigned)((a.T + RT_BT - 1) / RT_BT);
   prof_before("route", s);
-  if (a.dtype == MOE_BF16)
-    route_bf16_kernel<EP><<<grid, RT_THREADS, 0, s>>>(a);
+  if (a.dtype == MOE_BF16 && a.T <= 16 && a.partial) {
+    const int sp = route_split(a.d, a.E);
+    route_partial_kernel<EP><<<dim3(EP / 16, sp), 256, 0, s>>>(a, sp);
+    route_reduce_topk_kernel<EP><<<1, 1024, 0, s>>>(a, sp);
+  } else if (a.dtype == MOE_BF16 && a.T <= 16)
+    route_small_kernel<EP><<<1, RS_THREADS, 0, s>>>(a);
+  else if (a.dtype == MOE_BF16)
+    route_bf16_kernel<EP, BT, NS><<<(unsigned)((a.T + BT - 1) / BT), RT_THREADS, 0, s>>>(a);
   else
-    route_f32_kernel<EP><<<grid, RT_THREADS, 0, s>>>(a);
+    route_f32_kernel<EP><<<(unsigned)((a.T + RT_BT - 1) / RT_BT), RT_THREADS, 0, s>>>(a);
   prof_after(s);
   return hipGetLastError();
 }
 
 }  // namespace
 
+size_t route_ws_bytes(int64_t T, int E, int dtype) {
+  if (dtype != MOE_BF16 || T > 16) return 0;
+  const int ep = E <= 16 ? 16 : E <= 32 ? 32 : E <= 64 ? 64 : E <= 128 ? 128 : 256;
+  return (size_t)RP_MAX_SPLIT * 16 * ep * 4;
+}
+
 hipError_t launch_route(const RouteArgs& a, hipStream_t s) {
   if (a.T == 0) return hipSuccess;
-  if (a.E <= 16) return launch_ep<16>(a, s);
-  if (a.E <= 32) return launch_ep<32>(a, s);
-  if (a.E <= 64) return launch_ep<64>(a, s);
-  if (a.E <= 128) return launch_ep<128>(a, s);
-  return launch_ep<256>(a, s);
+  // (padded E, tokens per workgroup, ring depth): fewer tokens per workgroup
+  // for small E so that the grid covers the chip
+  if (a.E <= 16) return launch_ep<16, 16, 4>(a, s);
+  if (a.E <= 32) return launch_ep<32, 32, 4>(a, s);
+  if (a.E <= 64) return launch_ep<64, 32, 4>(a, s);
+  if (a.E <= 128) return launch_ep<128, 64, 4>(a, s);
+  return launch_ep<256, 64, 3>(a, s);
 }
 
 }  // namespace moe

@@ -53,7 +53,7 @@ def run_gpu(w, inp):
     T = w.T
     ws = B.workspace(cfg, T)
     idx, gate, logits = B.route(cfg, inp["x"], inp["w_router"], inp["logit_offset"],
-                                inp["select_bias"], want_logits=True)
+                                inp["select_bias"], want_logits=True, ws=ws)
     p = B.permute(cfg, idx, inp["x"], ws=ws)
     eout, sout = B.expert_ffn(cfg, T, p["x_perm"], p["expert_offsets"], inp["w1"], inp["w2"],
                               inp["w3"], x=inp["x"], ws1=inp["ws1"], ws3=inp["ws3"],

@@ -98,10 +98,10 @@ def test_entry_points_reject_bad_arguments_before_any_gpu_work():
     mis = ctypes.c_void_p(4096 + 2)    # misaligned
     n = None
     # null required pointers
-    assert L.moe_route(ctypes.byref(c), 10, n, p, n, n, n, p, p, n) == 1
-    assert L.moe_route(ctypes.byref(c), 10, mis, p, n, n, n, p, p, n) == 1
+    assert L.moe_route(ctypes.byref(c), 10, n, p, n, n, n, p, p, n, 0, n) == 1
+    assert L.moe_route(ctypes.byref(c), 10, mis, p, n, n, n, p, p, n, 0, n) == 1
     bad = cfg(top_k=9)
-    assert L.moe_route(ctypes.byref(bad), 10, p, p, n, n, n, p, p, n) == 1
+    assert L.moe_route(ctypes.byref(bad), 10, p, p, n, n, n, p, p, n, 0, n) == 1
     assert L.moe_permute(ctypes.byref(c), 10, n, n, n, p, p, p, n, n, p, 1 << 30, n) == 1
     # workspace too small
     assert L.moe_permute(ctypes.byref(c), 10, p, n, n, p, p, p, n, n, p, 16, n) == 3
@@ -112,7 +112,7 @@ def test_entry_points_reject_bad_arguments_before_any_gpu_work():
     sh = cfg(num_shared=1, d_ff_shared=128)
     assert L.moe_forward(ctypes.byref(sh), 10, p, p, n, n, p, p, p, n, n, n, p, n, n, n, n, p, 1 << 40, n) == 1
     # T = 0 is a valid no-op for every entry point
-    assert L.moe_route(ctypes.byref(c), 0, p, p, n, n, n, p, p, n) == 0
+    assert L.moe_route(ctypes.byref(c), 0, p, p, n, n, n, p, p, n, 0, n) == 0
     assert L.moe_permute(ctypes.byref(c), 0, p, n, n, p, p, p, n, n, n, 0, n) == 0
     assert L.moe_expert_ffn(ctypes.byref(c), 0, n, p, p, p, p, p, n, n, n, p, n, n, 0, n) == 0
     assert L.moe_combine(ctypes.byref(c), 0, p, p, p, n, p, n) == 0

@@ -1,0 +1,71 @@
+"""moe_forward inside a captured HIP graph (torch.cuda.CUDAGraph): every
+replay must give the eager result bit for bit, with eager work and
+synchronisations between the replays, also after the inputs are overwritten
+in place.  The library records no memset or allocation, so its launches are
+all it puts into the graph."""
+
+import pytest
+import torch
+
+from sparse_mixture_experts_gates_amd import binding as B
+from sparse_mixture_experts_gates_amd.workloads import WORKLOADS, make_inputs
+
+from tests.moe_check import bits
+
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():
+    pytest.skip("no GPU", allow_module_level=True)
+
+
+@pytest.mark.parametrize("name,kw", [
+    ("mixtral_small", dict(T=300, d=256, d_ff=320)),
+    ("decode_small", dict(T=8, d=192, E=32, d_ff=192)),
+    ("deepseek_small", dict(T=200, d=192, E=64, d_ff=128, d_ff_shared=192)),
+])
+def test_forward_replays_match_eager(name, kw):
+    base = {"mixtral_small": "mixtral_bf16", "decode_small": "gptoss_decode_bf16",
+            "deepseek_small": "deepseek_v3_bf16"}[name]
+    w = WORKLOADS[base].scaled(**kw)
+    print(f"[graph] {name}", flush=True)
+    inp = make_inputs(w, "cuda")
+    cfg = B.config_for(w)
+    ws = B.workspace(cfg, w.T)
+    y = torch.empty((w.T, w.d), dtype=w.torch_dtype, device="cuda")
+
+    def step():
+        B.forward_inputs(cfg, inp, ws=ws, y=y, outputs=False)
+
+    step()
+    torch.cuda.synchronize()
+    y_eager = y.clone()
+
+    g = torch.cuda.CUDAGraph()
+    cs = torch.cuda.Stream()
+    cs.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(cs):
+        step()
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=cs):
+            step()
+    torch.cuda.current_stream().wait_stream(cs)
+    torch.cuda.synchronize()
+
+    other = B.forward_inputs(cfg, inp)[0]          # eager work with its own buffers
+    for i in range(4):
+        y.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(bits(y), bits(y_eager)), f"replay {i} differs from eager"
+        other = B.forward_inputs(cfg, inp)[0]
+        torch.cuda.synchronize()
+        assert torch.equal(bits(other), bits(y_eager))
+
+    # new inputs written in place: replay == eager on the new inputs
+    inp["x"].copy_(torch.flip(inp["x"], dims=[0]))
+    g.replay()
+    torch.cuda.synchronize()
+    ref = B.forward_inputs(cfg, inp)[0]
+    torch.cuda.synchronize()
+    assert torch.equal(bits(y), bits(ref))
+    print(f"[graph] {name} ok", flush=True)

@@ -152,3 +152,27 @@ def test_capacity_drops_depend_on_the_batch():
         g = MC.run_gpu(ww, ii)
         MC.check_routing(ww, ii, g, {})
         MC.check_outputs(ww, ii, g)
+
+
+@pytest.mark.parametrize("E,d", [(8, 256), (128, 192), (256, 128)])
+def test_small_batch_router_paths_agree(E, d):
+    """T <= 16 has two router paths: split-K over many workgroups (with a
+    workspace) and a single-workgroup one (without).  Both must route like the
+    oracle from their own scores."""
+    w = small(T=11, E=E, d=d, k=min(4, E), act="swiglu")
+    inp = make_inputs(w, "cuda")
+    cfg = B.config_for(w)
+    ws = B.workspace(cfg, w.T)
+    for use_ws in (True, False):
+        idx, gate, logits = B.route(cfg, inp["x"], inp["w_router"], want_logits=True,
+                                    ws=ws if use_ws else None)
+        torch.cuda.synchronize()
+        g = dict(idx=idx.cpu().numpy().astype(np.int64), gate=gate.cpu().numpy(),
+                 logits=logits.cpu().numpy())
+        from oracle import moe_oracle as O
+        s_ref = O.router_logits(MC.np64(inp["x"]), MC.np64(inp["w_router"]))
+        assert np.abs(g["logits"] - s_ref).max() <= 1e-4
+        r = O.route_from_logits(g["logits"], k=w.k, gating=w.gating)
+        ok = ~r["near_tie"]
+        assert (r["topk_idx"][ok] == g["idx"][ok]).all()
+        assert np.abs(O.gate_values(g["logits"].astype(np.float64), g["idx"], w.gating) - g["gate"]).max() <= 1e-6
