@@ -159,32 +159,32 @@ void ffn_bf16_kernel(KArgs a) {
   const int64_t arow0 = (int64_t)pe.g * a.a_seg_rows;
   const int64_t wbase = (int64_t)pe.g * N * K;
 
-  // this lane's source (row, logical chunk) for each 8-row group the wave loads
-  const uint16_t* src[DPW];
-#pragma unroll
-  for (int i = 0; i < DPW; ++i) {
-    const int row = (wave + i * NW) * 8 + dma_row(lane);
-    const int ch = dma_chunk(lane);
+  // slab row `row` (tokens first, then weight rows) -> its global row start
+  auto row_ptr = [&](int row) -> const uint16_t* {
     if (row < BM) {
       int r = pe.m0 + row;
       if (r > pe.m1 - 1) r = pe.m1 - 1;
       const int64_t sr = a.a_rows ? (int64_t)(a.a_rows[r] / a.a_div) : arow0 + r;
-      src[i] = a.A + sr * K + ch * 8;
-    } else {
-      const int rho = row - BM;
-      int n;
-      const uint16_t* Wm = a.W;
-      if (MODE == MODE_SWIGLU) {
-        const int wq = rho / BNW, wi = rho - wq * BNW;
-        n = n0 + wq * HALF + (wi < HALF ? wi : wi - HALF);
-        if (wi >= HALF) Wm = a.Wu;
-      } else {
-        n = n0 + rho;
-      }
-      if (n > N - 1) n = N - 1;
-      src[i] = Wm + wbase + (int64_t)n * K + ch * 8;
+      return a.A + sr * K;
     }
-  }
+    const int rho = row - BM;
+    int n;
+    const uint16_t* Wm = a.W;
+    if (MODE == MODE_SWIGLU) {
+      const int wq = rho / BNW, wi = rho - wq * BNW;
+      n = n0 + wq * HALF + (wi < HALF ? wi : wi - HALF);
+      if (wi >= HALF) Wm = a.Wu;
+    } else {
+      n = n0 + rho;
+    }
+    if (n > N - 1) n = N - 1;
+    return Wm + wbase + (int64_t)n * K;
+  };
+  // this lane's source (row, logical chunk) for each 8-row group the wave loads
+  const uint16_t* src[DPW];
+#pragma unroll
+  for (int i = 0; i < DPW; ++i)
+    src[i] = row_ptr((wave + i * NW) * 8 + dma_row(lane)) + dma_chunk(lane) * 8;
 
   f32x4_t acc[TM][TN];
 #pragma unroll
@@ -193,6 +193,77 @@ void ffn_bf16_kernel(KArgs a) {
     for (int j = 0; j < TN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   const int nk = K / BK;
+  if constexpr (NSTAGE == 2) {
+    // Two-stage ring, software-pipelined across slabs.  Each slab is used in
+    // two halves of 32 k.  Step kt: (A) MFMAs of half 0 of slab kt, with the
+    // reads of half 1 spread between them; (B) wait for slab kt+1, barrier,
+    // request slab kt+2 into the stage slab kt occupied; (C) MFMAs of half 1
+    // of slab kt, with the reads of half 0 of slab kt+1 spread between them.
+    // LDS reads never wait at the start of a slab.
+    constexpr int NR = TN + TM, NM = TM * TN, PER = NM / NR > 0 ? NM / NR : 1;
+    auto read_half = [&](const uint16_t* st, int half, bf16x8_t* fw, bf16x8_t* fx) {
+      const uint16_t* sb = st + BM * BK;
+      const int ch = half * 4 + (lane >> 4);
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+        fw[j] = *reinterpret_cast<const bf16x8_t*>(sb + swz(wn * BNW + j * 16 + (lane & 15), ch));
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+        fx[i] = *reinterpret_cast<const bf16x8_t*>(st + swz(wm * BMW + i * 16 + (lane & 15), ch));
+    };
+#pragma unroll
+    for (int i = 0; i < DPW; ++i) dma_rows(src[i], ring + (wave + i * NW) * 512);
+    {
+      const int k1 = nk > 1 ? 1 : 0;
+#pragma unroll
+      for (int i = 0; i < DPW; ++i) dma_rows(src[i] + k1 * BK, ring + SEL + (wave + i * NW) * 512);
+    }
+    wait_vm_lgkm0<DPW>();
+    ring_barrier();
+    bf16x8_t w0[TN], x0[TM], w1[TN], x1[TM];
+    read_half(ring, 0, w0, x0);
+    for (int kt = 0; kt < nk; ++kt) {
+      const uint16_t* cur = ring + (kt & 1) * SEL;
+      const uint16_t* nxt = ring + ((kt + 1) & 1) * SEL;
+      // (A)
+      read_half(cur, 1, w1, x1);
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w0[j], x0[i], acc[i][j], 0, 0, 0);
+#pragma unroll
+      for (int r = 0; r < NR; ++r) {
+        __builtin_amdgcn_sched_group_barrier(0x008, PER, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, NM - NR * PER, 0);
+      // (B)
+      wait_vm_lgkm0<0>();
+      ring_barrier();
+      const int kn = kt + 2 < nk ? kt + 2 : nk - 1;
+#pragma unroll
+      for (int i = 0; i < DPW; ++i)
+        dma_rows(src[i] + kn * BK, const_cast<uint16_t*>(cur) + (wave + i * NW) * 512);
+      // (C)
+      read_half(nxt, 0, w0, x0);
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w1[j], x1[i], acc[i][j], 0, 0, 0);
+      // spread the slab loads over the MFMAs so the address path never
+      // backs up into the instruction stream
+#pragma unroll
+      for (int r = 0; r < NR; ++r) {
+        if (r < DPW) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, PER, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      if (DPW > NR) __builtin_amdgcn_sched_group_barrier(0x020, DPW > NR ? DPW - NR : 0, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, NM - NR * PER, 0);
+    }
+  } else {
 #pragma unroll
   for (int s = 0; s < NSTAGE - 1; ++s) {
     const int kk = s < nk ? s : nk - 1;
@@ -215,24 +286,40 @@ void ffn_bf16_kernel(KArgs a) {
       dma_rows(src[i] + kn * BK, nxt + (wave + i * NW) * 512);
     const uint16_t* sa = ring + cur_s * SEL;
     const uint16_t* sb = sa + BM * BK;
+    // operand reads of the first 32 k, then its MFMAs with the reads of the
+    // second 32 k spread between them, then the second half's MFMAs
+    bf16x8_t fw[2][TN], fx[2][TM];
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
       const int ch = kk * 4 + (lane >> 4);
-      bf16x8_t fw[TN];
 #pragma unroll
       for (int j = 0; j < TN; ++j)
-        fw[j] = *reinterpret_cast<const bf16x8_t*>(sb + swz(wn * BNW + j * 16 + (lane & 15), ch));
+        fw[kk][j] = *reinterpret_cast<const bf16x8_t*>(sb + swz(wn * BNW + j * 16 + (lane & 15), ch));
 #pragma unroll
-      for (int i = 0; i < TM; ++i) {
-        const bf16x8_t fx =
-            *reinterpret_cast<const bf16x8_t*>(sa + swz(wm * BMW + i * 16 + (lane & 15), ch));
+      for (int i = 0; i < TM; ++i)
+        fx[kk][i] = *reinterpret_cast<const bf16x8_t*>(sa + swz(wm * BMW + i * 16 + (lane & 15), ch));
+    }
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
 #pragma unroll
         for (int j = 0; j < TN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fw[j], fx, acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fw[kk][j], fx[kk][i], acc[i][j], 0, 0, 0);
+    {
+      constexpr int NR = TN + TM, NM = TM * TN, PER = NM / NR > 0 ? NM / NR : 1;
+      __builtin_amdgcn_sched_group_barrier(0x020, DPW, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);
+#pragma unroll
+      for (int r = 0; r < NR; ++r) {
+        __builtin_amdgcn_sched_group_barrier(0x008, PER, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       }
+      __builtin_amdgcn_sched_group_barrier(0x008, 2 * NM - NR * PER, 0);
     }
     cur_s = cur_s + 1 == NSTAGE ? 0 : cur_s + 1;
     nxt_s = nxt_s + 1 == NSTAGE ? 0 : nxt_s + 1;
+  }
   }
   wait_vm_lgkm0<0>();   // the trailing reloads must land before the LDS is released
 
@@ -351,13 +438,21 @@ __global__ __launch_bounds__(256) void ffn_f32_kernel(KArgs a) {
 }
 
 struct Shape {
-  int BM, BNOUT;
+  int BM, BNOUT, id;   // id: 0 fp32, 1 small batch, 2 big 256x256, 3 256x128
 };
 
-Shape pick_shape(int dtype, bool small, int mode) {
-  if (dtype == MOE_F32) return {64, 64};
-  if (small) return {32, mode == MODE_SWIGLU ? 64 : 128};
-  return {256, mode == MODE_SWIGLU ? 128 : 256};
+constexpr int kCUs = 256;
+
+// Tile shape of one pass.  Prefill passes use 256 x 256 tiles unless that
+// leaves fewer than four rounds of tiles over the CUs (e.g. the second expert
+// GEMM with a short N), where 256 x 128 tiles trim the last, partial round.
+Shape pick_shape(int dtype, bool small, int mode, int64_t max_rows, int N) {
+  if (dtype == MOE_F32) return {64, 64, 0};
+  const bool glu = mode == MODE_SWIGLU;
+  if (small) return {32, glu ? 64 : 128, 1};
+  const int64_t big_tiles = ((max_rows + 255) / 256) * ((N + (glu ? 127 : 255)) / (glu ? 128 : 256));
+  if (big_tiles < 4 * kCUs) return {256, glu ? 64 : 128, 3};
+  return {256, glu ? 128 : 256, 2};
 }
 
 int64_t max_entries(int64_t max_rows, int G, int N, Shape sh) {
@@ -380,7 +475,7 @@ void launch_bf16(int mode, unsigned grid, const KArgs& k, hipStream_t s) {
 size_t ffn_plan_bytes(int64_t max_rows, int G, int N, bool small, int dtype) {
   size_t best = 0;
   for (int mode = 0; mode < 4; ++mode) {
-    const size_t b = 16 + 16 * (size_t)max_entries(max_rows, G, N, pick_shape(dtype, small, mode));
+    const size_t b = 16 + 16 * (size_t)max_entries(max_rows, G, N, pick_shape(dtype, small, mode, max_rows, N));
     if (b > best) best = b;
   }
   return (best + 255) / 256 * 256;
@@ -388,14 +483,14 @@ size_t ffn_plan_bytes(int64_t max_rows, int G, int N, bool small, int dtype) {
 
 namespace {
 int pass_nt(const FfnPassArgs& p) {
-  const Shape sh = pick_shape(p.dtype, p.small, p.mode);
+  const Shape sh = pick_shape(p.dtype, p.small, p.mode, p.max_rows, p.N);
   return (p.N + sh.BNOUT - 1) / sh.BNOUT;
 }
 }  // namespace
 
 hipError_t launch_ffn_plans(const FfnPassArgs& p1, const FfnPassArgs& p2, hipStream_t s) {
-  const Shape sh1 = pick_shape(p1.dtype, p1.small, p1.mode);
-  const Shape sh2 = pick_shape(p2.dtype, p2.small, p2.mode);
+  const Shape sh1 = pick_shape(p1.dtype, p1.small, p1.mode, p1.max_rows, p1.N);
+  const Shape sh2 = pick_shape(p2.dtype, p2.small, p2.mode, p2.max_rows, p2.N);
   if (sh1.BM != sh2.BM || p1.seg_offsets != p2.seg_offsets) return hipErrorInvalidValue;
   if (max_entries(p1.max_rows, p1.G, p1.N, sh1) == 0) return hipSuccess;
   int32_t* c1 = static_cast<int32_t*>(p1.plan);
@@ -410,7 +505,7 @@ hipError_t launch_ffn_plans(const FfnPassArgs& p1, const FfnPassArgs& p2, hipStr
 }
 
 hipError_t launch_ffn_pass(const FfnPassArgs& p, hipStream_t s) {
-  const Shape sh = pick_shape(p.dtype, p.small, p.mode);
+  const Shape sh = pick_shape(p.dtype, p.small, p.mode, p.max_rows, p.N);
   const int64_t grid = max_entries(p.max_rows, p.G, p.N, sh);
   if (grid == 0) return hipSuccess;
   int32_t* count = static_cast<int32_t*>(p.plan);
@@ -438,8 +533,10 @@ hipError_t launch_ffn_pass(const FfnPassArgs& p, hipStream_t s) {
       case MODE_GELU: ffn_f32_kernel<MODE_GELU><<<(unsigned)grid, 256, 0, s>>>(k); break;
       default: ffn_f32_kernel<MODE_SWIGLU><<<(unsigned)grid, 256, 0, s>>>(k); break;
     }
-  } else if (p.small) {
+  } else if (sh.id == 1) {
     launch_bf16<32, 128, 1, 4, 4>(p.mode, (unsigned)grid, k, s);
+  } else if (sh.id == 3) {
+    launch_bf16<256, 128, 4, 2, 3>(p.mode, (unsigned)grid, k, s);
   } else {
     launch_bf16<256, 256, 2, 4, 2>(p.mode, (unsigned)grid, k, s);
   }
