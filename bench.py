@@ -117,8 +117,13 @@ def cpu_baseline(w, inp, budget_s=15.0):
     while dt < budget_s * 0.66 and n < w.T:
         n = min(w.T, max(2 * n, int(n * budget_s / max(dt, 1e-3))))
         dt = run(n)
-    return {"value": n / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"first {n} of the {w.T} tokens of {w.name}, numpy float64 oracle "
+    reps = 1
+    while dt < budget_s * 0.66:   # the whole batch is quick: repeat it
+        dt += run(n)
+        reps += 1
+    what = f"first {n} of the {w.T} tokens" if n < w.T else f"all {w.T} tokens"
+    return {"value": reps * n / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{what} of {w.name}, {reps} pass(es) of the numpy float64 oracle "
                       f"forward (all routed experts touched by them), {dt:.1f} s"}
 
 

@@ -12,17 +12,24 @@
 // A pass is a device-built tile plan plus one GEMM launch.  The plan kernel
 // turns the segment offsets into (segment, row range, column tile) entries,
 // expert-major, then column tile, then row tile, so the tiles that share a
-// weight slab are adjacent; the GEMM remaps block ids so that adjacent plan
-// entries land on the same XCD (blocks are dealt round-robin over the 8 XCDs),
-// which keeps each shared slab in one L2.  No host synchronisation: the grid
-// is sized for the worst case and surplus blocks return at once.
+// weight slab are adjacent, and splits them into 8 contiguous queues, one
+// per XCD (blocks are dealt round-robin over the 8 XCDs), which keeps each
+// shared slab in one L2.  The prefill GEMMs are persistent: one block per CU
+// drains its XCD's queue, then helps the others, so XCDs whose tiles are
+// cheaper (ragged segment ends) do not finish early and idle.  No host
+// synchronisation: the queue words live in the plan and the plan kernel
+// resets them.
 //
-// bf16 GEMM: XOR-swizzled LDS tiles of 64-wide K slabs, double-buffered
-// through registers; v_mfma_f32_16x16x32_bf16 with weights on the MFMA row
-// side, so each lane ends with 4 adjacent output columns of one row (8-byte
-// stores).  SwiGLU interleaves W1 and W3 rows inside every wave's slab so the
-// gate and up accumulators of a column sit in the same lane and the epilogue
-// is elementwise.  The fp32 variant is a plain LDS-tiled FMA GEMM.
+// bf16 GEMM: K in 64-wide slabs brought into XOR-swizzled LDS rings by
+// direct-to-LDS loads and software-pipelined across slabs;
+// v_mfma_f32_16x16x32_bf16 with weights on the MFMA row side, so each lane
+// ends with 4 adjacent output columns of one row (8-byte stores).  SwiGLU
+// interleaves W1 and W3 rows inside every wave's slab so the gate and up
+// accumulators of a column sit in the same lane and the epilogue is
+// elementwise.  Row sub-tiles past the end of a segment skip their MFMAs.
+// The fp32 variant is a plain LDS-tiled FMA GEMM.
+#include <type_traits>
+
 #include "common.h"
 #include "launch.h"
 
@@ -37,6 +44,10 @@ struct PlanEntry {
   int32_t g, m0, m1, nt;
 };
 
+// Plan buffer: a 128-byte header (int32 entry count, then at int32 index
+// kPlanHeads the 8 per-XCD queue words, 64-bit each), then the entries.
+constexpr int kPlanHeader = 128, kPlanHeads = 4;
+
 struct KArgs {
   const uint16_t* A;   // or float*
   const uint16_t* W;
@@ -44,6 +55,7 @@ struct KArgs {
   uint16_t* C;
   const PlanEntry* plan;
   const int32_t* count;
+  unsigned long long* queues;   // 8 per-XCD queue words (persistent launches)
   const int32_t* a_rows;  // optional row indirection for A (row gather folded in)
   int a_div;
   int K, N;
@@ -100,6 +112,7 @@ __global__ __launch_bounds__(1024) void ffn_plan_kernel(
       out[L] = PlanEntry{g, m0, m1, nt};
     }
     if (tid == 0) (pass == 0 ? count : count2)[0] = V;
+    if (tid < 16) (pass == 0 ? count : count2)[kPlanHeads + tid] = 0;   // queue words
   }
 }
 
@@ -108,6 +121,35 @@ __global__ __launch_bounds__(1024) void ffn_plan_kernel(
 __device__ __forceinline__ int xcd_remap(int P, int V) {
   const int x = P & 7, i = P >> 3, q = V >> 3, r = V & 7;
   return (x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q) + i;
+}
+
+// Start of XCD x's share of the V entries (the split xcd_remap uses).
+__device__ __forceinline__ int xcd_start(int x, int V) {
+  const int q = V >> 3, r = V & 7;
+  return x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q;
+}
+
+// Persistent launches: a block on XCD x takes the next entry of XCD x's
+// queue, and once that is drained, steals from the other XCDs' queues.  A
+// queue word holds the entries taken from its front (low 32 bits, by its own
+// XCD) and from its back (high 32 bits, by thieves): one atomic add claims
+// an entry from either end, and the entry exists while front + back < len.
+// Thieves take the last entries, whose weight slabs the owner XCD has not
+// fetched yet, so a slab is not pulled into two L2s.  Returns -1 when every
+// queue is drained.  Called by one lane.
+__device__ int next_tile(unsigned long long* queues, int V, int x) {
+#pragma unroll 1
+  for (int s = 0; s < 8; ++s) {
+    const int y = (x + s) & 7;
+    const unsigned len = (unsigned)(xcd_start(y + 1, V) - xcd_start(y, V));
+    const unsigned long long q0 = __hip_atomic_load(queues + y, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if ((unsigned)q0 + (unsigned)(q0 >> 32) >= len) continue;
+    const bool back = s > 0;
+    const unsigned long long q = atomicAdd(queues + y, back ? (1ull << 32) : 1ull);
+    const unsigned f = (unsigned)q, b = (unsigned)(q >> 32);
+    if (f + b < len) return xcd_start(y, V) + (int)(back ? len - 1 - b : f);
+  }
+  return -1;
 }
 
 __device__ __forceinline__ float gelu_erf(float z) {
@@ -131,7 +173,7 @@ __device__ __forceinline__ float act1(float v) {
 // so it fetches logical chunk (l%8) ^ (l/8) of its row -- full 128-byte lines
 // per 8 lanes.  Slab kt+NSTAGE-1 is requested while slab kt is multiplied;
 // one barrier per slab.
-template <int BM, int BN, int WM, int WN, int NSTAGE, int MODE>
+template <int BM, int BN, int WM, int WN, int NSTAGE, int NSB, int MODE, bool PERSIST>
 __global__ __launch_bounds__(64 * WM * WN)
 void ffn_bf16_kernel(KArgs a) {
   constexpr int NW = WM * WN;
@@ -145,16 +187,41 @@ void ffn_bf16_kernel(KArgs a) {
   constexpr int SEL = (BM + BN) * BK;            // bf16 elements per slab
   static_assert(MODE != MODE_SWIGLU || TN % 2 == 0, "SwiGLU needs paired tiles");
 
-  __shared__ __attribute__((aligned(1024))) uint16_t ring[NSTAGE * SEL];
+  // NSTAGE == 2: token ring [2][BM*BK] then weight ring [NSB][BN*BK];
+  // otherwise NSTAGE stages of [BM*BK tokens | BN*BK weights]
+  constexpr int LDS_ELEMS = NSTAGE == 2 ? 2 * BM * BK + NSB * BN * BK : NSTAGE * SEL;
+  // One LDS object only (a second one makes the compiler assume the operand
+  // reads may alias the in-flight direct-to-LDS writes and wait for them);
+  // the two int slots after the ring pass the next tile id to every wave.
+  __shared__ __attribute__((aligned(1024))) uint16_t ring[LDS_ELEMS + 4];
+  int* const tile_slot = reinterpret_cast<int*>(ring + LDS_ELEMS);
 
   const int V = a.count[0];
   const int P = blockIdx.x;
-  if (P >= V) return;
-  const PlanEntry pe = a.plan[xcd_remap(P, V)];
-  const int tid = threadIdx.x, lane = tid & 63;
+  const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
   const int wm = wave / WN, wn = wave % WN;
   const int K = a.K, N = a.N;
+  for (int it = 0;; ++it) {
+  int e;
+  if constexpr (PERSIST) {
+    // claimed when needed, not ahead: a claim held through a whole tile
+    // would keep that entry from an idle block at the end of the pass
+    if (tid == 0) tile_slot[it & 1] = next_tile(a.queues, V, P & 7);
+    // also: every wave is done with the previous tile's LDS
+    wait_vm_lgkm0<0>();
+    ring_barrier();
+    e = __builtin_amdgcn_readfirstlane(tile_slot[it & 1]);
+    if (e < 0) break;
+  } else {
+    if (it > 0 || P >= V) break;
+    e = xcd_remap(P, V);
+  }
+  // lane id, opaque to the optimiser so that nothing derived from it is
+  // hoisted out of the tile loop (it would stay live across every slab)
+  int lane = tid & 63;
+  asm volatile("" : "+v"(lane));
+  const PlanEntry pe = a.plan[e];
   const int n0 = pe.nt * BNOUT;
   const int64_t arow0 = (int64_t)pe.g * a.a_seg_rows;
   const int64_t wbase = (int64_t)pe.g * N * K;
@@ -194,75 +261,113 @@ void ffn_bf16_kernel(KArgs a) {
 
   const int nk = K / BK;
   if constexpr (NSTAGE == 2) {
-    // Two-stage ring, software-pipelined across slabs.  Each slab is used in
-    // two halves of 32 k.  Step kt: (A) MFMAs of half 0 of slab kt, with the
+    // Software pipeline across slabs: the token slabs sit in a 2-stage ring,
+    // the weight slabs in an NSB-stage ring (weights mostly come from HBM,
+    // so they are requested NSB-1 slabs ahead).  Each slab is used in two
+    // halves of 32 k.  Step kt: (A) MFMAs of half 0 of slab kt, with the
     // reads of half 1 spread between them; (B) wait for slab kt+1, barrier,
-    // request slab kt+2 into the stage slab kt occupied; (C) MFMAs of half 1
-    // of slab kt, with the reads of half 0 of slab kt+1 spread between them.
-    // LDS reads never wait at the start of a slab.
-    constexpr int NR = TN + TM, NM = TM * TN, PER = NM / NR > 0 ? NM / NR : 1;
-    auto read_half = [&](const uint16_t* st, int half, bf16x8_t* fw, bf16x8_t* fx) {
-      const uint16_t* sb = st + BM * BK;
-      const int ch = half * 4 + (lane >> 4);
+    // request token slab kt+2 and weight slab kt+NSB into the stages slab kt
+    // occupied; (C) MFMAs of half 1 of slab kt, with the reads of half 0 of
+    // slab kt+1 spread between them.  LDS reads never wait at a slab start.
+    constexpr int SA = BM * BK, SB = BN * BK;
+    constexpr int DPA = BM / 8 / NW, DPB = DPW - DPA;
+    static_assert((BM / 8) % NW == 0, "token load groups must divide over the waves");
+    uint16_t* const ring_a = ring;
+    uint16_t* const ring_b = ring + 2 * SA;
+    auto issue = [&](int kta, int stage_a, int ktb, int stage_b) {
+      const int ka = kta < nk ? kta : nk - 1;   // past the end: a harmless reload
+      const int kb = ktb < nk ? ktb : nk - 1;
 #pragma unroll
-      for (int j = 0; j < TN; ++j)
-        fw[j] = *reinterpret_cast<const bf16x8_t*>(sb + swz(wn * BNW + j * 16 + (lane & 15), ch));
+      for (int i = 0; i < DPA; ++i)
+        dma_rows(src[i] + ka * BK, ring_a + stage_a * SA + (wave + i * NW) * 512);
 #pragma unroll
-      for (int i = 0; i < TM; ++i)
-        fx[i] = *reinterpret_cast<const bf16x8_t*>(st + swz(wm * BMW + i * 16 + (lane & 15), ch));
+      for (int i = DPA; i < DPW; ++i)
+        dma_rows(src[i] + kb * BK, ring_b + stage_b * SB + (wave + i * NW - BM / 8) * 512);
     };
-#pragma unroll
-    for (int i = 0; i < DPW; ++i) dma_rows(src[i], ring + (wave + i * NW) * 512);
-    {
-      const int k1 = nk > 1 ? 1 : 0;
-#pragma unroll
-      for (int i = 0; i < DPW; ++i) dma_rows(src[i] + k1 * BK, ring + SEL + (wave + i * NW) * 512);
-    }
-    wait_vm_lgkm0<DPW>();
-    ring_barrier();
-    bf16x8_t w0[TN], x0[TM], w1[TN], x1[TM];
-    read_half(ring, 0, w0, x0);
-    for (int kt = 0; kt < nk; ++kt) {
-      const uint16_t* cur = ring + (kt & 1) * SEL;
-      const uint16_t* nxt = ring + ((kt + 1) & 1) * SEL;
-      // (A)
-      read_half(cur, 1, w1, x1);
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
+    // Rows of this wave's tile that hold tokens: a tile at the ragged end of
+    // a segment multiplies only its live 16-row sub-tiles.
+    const int rows_left = pe.m1 - pe.m0 - wm * BMW;
+    const int nlive = rows_left >= BMW ? TM : (rows_left <= 0 ? 0 : (rows_left + 15) >> 4);
+    // KIND 2: every sub-tile live; 1: some; 0: none (loads and barriers only)
+    auto pipeline = [&](auto kind_tag) {
+      constexpr int KIND = decltype(kind_tag)::value;
+      constexpr bool FULL = KIND == 2;
+      constexpr int NR = TN + TM, NM = TM * TN, PER = NM / NR > 0 ? NM / NR : 1;
+      auto read_half = [&](const uint16_t* sa, const uint16_t* sb, int half, bf16x8_t* fw,
+                           bf16x8_t* fx) {
+        const int ch = half * 4 + (lane >> 4);
 #pragma unroll
         for (int j = 0; j < TN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w0[j], x0[i], acc[i][j], 0, 0, 0);
+          fw[j] = *reinterpret_cast<const bf16x8_t*>(sb + swz(wn * BNW + j * 16 + (lane & 15), ch));
 #pragma unroll
-      for (int r = 0; r < NR; ++r) {
-        __builtin_amdgcn_sched_group_barrier(0x008, PER, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        for (int i = 0; i < TM; ++i)
+          fx[i] = *reinterpret_cast<const bf16x8_t*>(sa + swz(wm * BMW + i * 16 + (lane & 15), ch));
+      };
+      auto mfma_half = [&](const bf16x8_t* fw, const bf16x8_t* fx) {
+        if constexpr (KIND == 0) return;
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+          if (FULL || i < nlive)
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+              acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fw[j], fx[i], acc[i][j], 0, 0, 0);
+      };
+      issue(0, 0, 0, 0);
+      issue(1, 1, 1, 1);
+#pragma unroll
+      for (int st = 2; st < NSB; ++st) {
+        const int kb = st < nk ? st : nk - 1;
+#pragma unroll
+        for (int i = DPA; i < DPW; ++i)
+          dma_rows(src[i] + kb * BK, ring_b + st * SB + (wave + i * NW - BM / 8) * 512);
       }
-      __builtin_amdgcn_sched_group_barrier(0x008, NM - NR * PER, 0);
-      // (B)
-      wait_vm_lgkm0<0>();
+      wait_vm_lgkm0<DPW + (NSB - 2) * DPB>();
       ring_barrier();
-      const int kn = kt + 2 < nk ? kt + 2 : nk - 1;
+      bf16x8_t w0[TN], x0[TM], w1[TN], x1[TM];
+      read_half(ring_a, ring_b, 0, w0, x0);
+      int sb_cur = 0, sb_nxt = 1;   // weight ring stages of slabs kt and kt+1
+      for (int kt = 0; kt < nk; ++kt) {
+        const uint16_t* cur_a = ring_a + (kt & 1) * SA;
+        const uint16_t* nxt_a = ring_a + ((kt + 1) & 1) * SA;
+        const uint16_t* cur_b = ring_b + sb_cur * SB;
+        const uint16_t* nxt_b = ring_b + sb_nxt * SB;
+        // (A)
+        read_half(cur_a, cur_b, 1, w1, x1);
+        mfma_half(w0, x0);
+        if constexpr (FULL) {
 #pragma unroll
-      for (int i = 0; i < DPW; ++i)
-        dma_rows(src[i] + kn * BK, const_cast<uint16_t*>(cur) + (wave + i * NW) * 512);
-      // (C)
-      read_half(nxt, 0, w0, x0);
+          for (int r = 0; r < NR; ++r) {
+            __builtin_amdgcn_sched_group_barrier(0x008, PER, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          }
+          __builtin_amdgcn_sched_group_barrier(0x008, NM - NR * PER, 0);
+        }
+        // (B) slab kt+1 has landed once only weight slabs kt+2.. remain
+        wait_vm_lgkm0<(NSB - 2) * DPB>();
+        ring_barrier();
+        issue(kt + 2, kt & 1, kt + NSB, sb_cur);
+        // (C)
+        read_half(nxt_a, nxt_b, 0, w0, x0);
+        mfma_half(w1, x1);
+        if constexpr (FULL) {
+          // spread the slab loads over the MFMAs so the address path never
+          // backs up into the instruction stream
 #pragma unroll
-      for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w1[j], x1[i], acc[i][j], 0, 0, 0);
-      // spread the slab loads over the MFMAs so the address path never
-      // backs up into the instruction stream
-#pragma unroll
-      for (int r = 0; r < NR; ++r) {
-        if (r < DPW) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, PER, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          for (int r = 0; r < NR; ++r) {
+            if (r < DPW) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, PER, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          }
+          if (DPW > NR) __builtin_amdgcn_sched_group_barrier(0x020, DPW > NR ? DPW - NR : 0, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, NM - NR * PER, 0);
+        }
+        sb_cur = sb_nxt;
+        sb_nxt = sb_nxt + 1 == NSB ? 0 : sb_nxt + 1;
       }
-      if (DPW > NR) __builtin_amdgcn_sched_group_barrier(0x020, DPW > NR ? DPW - NR : 0, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, NM - NR * PER, 0);
-    }
+    };
+    if (nlive == TM) pipeline(std::integral_constant<int, 2>{});
+    else if (nlive == 0) pipeline(std::integral_constant<int, 0>{});
+    else pipeline(std::integral_constant<int, 1>{});
   } else {
 #pragma unroll
   for (int s = 0; s < NSTAGE - 1; ++s) {
@@ -352,6 +457,7 @@ void ffn_bf16_kernel(KArgs a) {
       if (row_ok && col < N) *reinterpret_cast<uint2*>(crow + col) = pk;
     }
   }
+  }  // tiles
 }
 
 // fp32: 64 x 64 output tile, 16-deep K slabs, 4 x 4 outputs per thread
@@ -460,14 +566,29 @@ int64_t max_entries(int64_t max_rows, int G, int N, Shape sh) {
   return ((max_rows + sh.BM - 1) / sh.BM + G) * nt;
 }
 
-template <int BM, int BN, int WM, int WN, int NS>
+template <int BM, int BN, int WM, int WN, int NS, int NSB, bool PERSIST>
 void launch_bf16(int mode, unsigned grid, const KArgs& k, hipStream_t s) {
+  constexpr int T = 64 * WM * WN;
   switch (mode) {
-    case MODE_PLAIN: ffn_bf16_kernel<BM, BN, WM, WN, NS, MODE_PLAIN><<<grid, 64 * WM * WN, 0, s>>>(k); break;
-    case MODE_RELU: ffn_bf16_kernel<BM, BN, WM, WN, NS, MODE_RELU><<<grid, 64 * WM * WN, 0, s>>>(k); break;
-    case MODE_GELU: ffn_bf16_kernel<BM, BN, WM, WN, NS, MODE_GELU><<<grid, 64 * WM * WN, 0, s>>>(k); break;
-    default: ffn_bf16_kernel<BM, BN, WM, WN, NS, MODE_SWIGLU><<<grid, 64 * WM * WN, 0, s>>>(k); break;
+    case MODE_PLAIN: ffn_bf16_kernel<BM, BN, WM, WN, NS, NSB, MODE_PLAIN, PERSIST><<<grid, T, 0, s>>>(k); break;
+    case MODE_RELU: ffn_bf16_kernel<BM, BN, WM, WN, NS, NSB, MODE_RELU, PERSIST><<<grid, T, 0, s>>>(k); break;
+    case MODE_GELU: ffn_bf16_kernel<BM, BN, WM, WN, NS, NSB, MODE_GELU, PERSIST><<<grid, T, 0, s>>>(k); break;
+    default: ffn_bf16_kernel<BM, BN, WM, WN, NS, NSB, MODE_SWIGLU, PERSIST><<<grid, T, 0, s>>>(k); break;
   }
+}
+
+// Compute units of the current device (one persistent block each).
+int device_cus() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return kCUs;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = kCUs;
+    cached[dev] = n;
+  }
+  return cached[dev];
 }
 
 }  // namespace
@@ -475,7 +596,7 @@ void launch_bf16(int mode, unsigned grid, const KArgs& k, hipStream_t s) {
 size_t ffn_plan_bytes(int64_t max_rows, int G, int N, bool small, int dtype) {
   size_t best = 0;
   for (int mode = 0; mode < 4; ++mode) {
-    const size_t b = 16 + 16 * (size_t)max_entries(max_rows, G, N, pick_shape(dtype, small, mode, max_rows, N));
+    const size_t b = kPlanHeader + 16 * (size_t)max_entries(max_rows, G, N, pick_shape(dtype, small, mode, max_rows, N));
     if (b > best) best = b;
   }
   return (best + 255) / 256 * 256;
@@ -495,8 +616,8 @@ hipError_t launch_ffn_plans(const FfnPassArgs& p1, const FfnPassArgs& p2, hipStr
   if (max_entries(p1.max_rows, p1.G, p1.N, sh1) == 0) return hipSuccess;
   int32_t* c1 = static_cast<int32_t*>(p1.plan);
   int32_t* c2 = static_cast<int32_t*>(p2.plan);
-  PlanEntry* e1 = reinterpret_cast<PlanEntry*>(static_cast<char*>(p1.plan) + 16);
-  PlanEntry* e2 = reinterpret_cast<PlanEntry*>(static_cast<char*>(p2.plan) + 16);
+  PlanEntry* e1 = reinterpret_cast<PlanEntry*>(static_cast<char*>(p1.plan) + kPlanHeader);
+  PlanEntry* e2 = reinterpret_cast<PlanEntry*>(static_cast<char*>(p2.plan) + kPlanHeader);
   prof_before(p1.seg_offsets ? "ffn_plan" : "ffn_plan_shared", s);
   ffn_plan_kernel<<<1, 1024, 0, s>>>(p1.seg_offsets, p1.G, p1.dense_rows, sh1.BM, pass_nt(p1), e1, c1,
                                      pass_nt(p2), e2, c2);
@@ -509,7 +630,7 @@ hipError_t launch_ffn_pass(const FfnPassArgs& p, hipStream_t s) {
   const int64_t grid = max_entries(p.max_rows, p.G, p.N, sh);
   if (grid == 0) return hipSuccess;
   int32_t* count = static_cast<int32_t*>(p.plan);
-  PlanEntry* plan = reinterpret_cast<PlanEntry*>(static_cast<char*>(p.plan) + 16);
+  PlanEntry* plan = reinterpret_cast<PlanEntry*>(static_cast<char*>(p.plan) + kPlanHeader);
   KArgs k;
   k.A = static_cast<const uint16_t*>(p.A);
   k.W = static_cast<const uint16_t*>(p.w);
@@ -517,6 +638,7 @@ hipError_t launch_ffn_pass(const FfnPassArgs& p, hipStream_t s) {
   k.C = static_cast<uint16_t*>(p.C);
   k.plan = plan;
   k.count = count;
+  k.queues = reinterpret_cast<unsigned long long*>(count + kPlanHeads);
   k.a_rows = p.a_rows;
   k.a_div = p.a_div > 0 ? p.a_div : 1;
   k.K = p.K;
@@ -534,11 +656,18 @@ hipError_t launch_ffn_pass(const FfnPassArgs& p, hipStream_t s) {
       default: ffn_f32_kernel<MODE_SWIGLU><<<(unsigned)grid, 256, 0, s>>>(k); break;
     }
   } else if (sh.id == 1) {
-    launch_bf16<32, 128, 1, 4, 4>(p.mode, (unsigned)grid, k, s);
-  } else if (sh.id == 3) {
-    launch_bf16<256, 128, 4, 2, 3>(p.mode, (unsigned)grid, k, s);
+    launch_bf16<32, 128, 1, 4, 4, 4, false>(p.mode, (unsigned)grid, k, s);
   } else {
-    launch_bf16<256, 256, 2, 4, 2>(p.mode, (unsigned)grid, k, s);
+    // With at least two rounds of tiles: one persistent block per CU (the
+    // LDS ring fills a CU).  Fewer, short tiles do not repay the queue.
+    const int cus = device_cus();
+    if (grid >= 2 * (int64_t)cus) {
+      if (sh.id == 3) launch_bf16<256, 128, 4, 2, 3, 3, true>(p.mode, (unsigned)cus, k, s);
+      else launch_bf16<256, 256, 2, 4, 2, 2, true>(p.mode, (unsigned)cus, k, s);
+    } else {
+      if (sh.id == 3) launch_bf16<256, 128, 4, 2, 3, 3, false>(p.mode, (unsigned)grid, k, s);
+      else launch_bf16<256, 256, 2, 4, 2, 2, false>(p.mode, (unsigned)grid, k, s);
+    }
   }
   prof_after(s);
   return hipGetLastError();

@@ -22,10 +22,11 @@ if not torch.cuda.is_available():
     ("mixtral_small", dict(T=300, d=256, d_ff=320)),
     ("decode_small", dict(T=8, d=192, E=32, d_ff=192)),
     ("deepseek_small", dict(T=200, d=192, E=64, d_ff=128, d_ff_shared=192)),
+    ("persistent", dict(T=500, d=256, E=64, k=2, d_ff=512)),   # work-queue GEMM
 ])
 def test_forward_replays_match_eager(name, kw):
     base = {"mixtral_small": "mixtral_bf16", "decode_small": "gptoss_decode_bf16",
-            "deepseek_small": "deepseek_v3_bf16"}[name]
+            "deepseek_small": "deepseek_v3_bf16", "persistent": "mixtral_bf16"}[name]
     w = WORKLOADS[base].scaled(**kw)
     print(f"[graph] {name}", flush=True)
     inp = make_inputs(w, "cuda")

@@ -91,6 +91,12 @@ EDGES = {
     "decode_threshold_out": small(T=33, k=2),     # 66 rows: prefill path
     "max_E_k": small(E=256, k=16, T=300, d=64, d_ff=64),
     "ragged_many_tiles": small(T=1111, d=320, d_ff=704, E=5, k=3),
+    # enough tiles for the persistent prefill GEMMs (256 x 256 tiles in the
+    # first GEMM, then the second; 256 x 128 tiles), with segments ending
+    # part-way into a row tile
+    "persistent_256x256_first_gemm": small(T=1024, d=192, E=8, k=2, d_ff=16384),
+    "persistent_256x256_second_gemm": small(T=4096, d=8192, E=8, k=2, d_ff=192),
+    "persistent_256x128": small(T=500, d=256, E=64, k=2, d_ff=512),
 }
 
 
