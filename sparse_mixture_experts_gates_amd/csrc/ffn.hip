@@ -550,20 +550,24 @@ struct Shape {
 constexpr int kCUs = 256;
 
 // Tile shape of one pass.  Prefill passes use 256 x 256 tiles unless that
-// leaves fewer than four rounds of tiles over the CUs (e.g. the second expert
-// GEMM with a short N), where 256 x 128 tiles trim the last, partial round.
+// leaves fewer than two rounds of tiles over the CUs (a short pass), where
+// 256 x 128 tiles trim the last, partial round.
 Shape pick_shape(int dtype, bool small, int mode, int64_t max_rows, int N) {
   if (dtype == MOE_F32) return {64, 64, 0};
   const bool glu = mode == MODE_SWIGLU;
   if (small) return {32, glu ? 64 : 128, 1};
   const int64_t big_tiles = ((max_rows + 255) / 256) * ((N + (glu ? 127 : 255)) / (glu ? 128 : 256));
-  if (big_tiles < 4 * kCUs) return {256, glu ? 64 : 128, 3};
+  if (big_tiles < 2 * kCUs) return {256, glu ? 64 : 128, 3};
   return {256, glu ? 128 : 256, 2};
 }
 
+// Upper bound of the plan entries: a row tile holds at least one row, and
+// each segment adds at most one partial tile.
 int64_t max_entries(int64_t max_rows, int G, int N, Shape sh) {
   const int64_t nt = (N + sh.BNOUT - 1) / sh.BNOUT;
-  return ((max_rows + sh.BM - 1) / sh.BM + G) * nt;
+  int64_t mt = (max_rows + sh.BM - 1) / sh.BM + G;
+  if (mt > max_rows) mt = max_rows;
+  return mt * nt;
 }
 
 template <int BM, int BN, int WM, int WN, int NS, int NSB, bool PERSIST>

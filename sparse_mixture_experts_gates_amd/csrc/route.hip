@@ -381,35 +381,36 @@ __global__ __launch_bounds__(256) void route_partial_kernel(RouteArgs a, int nsp
   out[tl * EP + et * 16 + ei] = red[tl * 17 + ei];
 }
 
+// One workgroup per token: a single CU keeps only so many misses in flight,
+// so the parts (written by other XCDs, hence read from beyond L2) are spread
+// over T workgroups.  Block b adds the parts of token b in order and runs
+// the top-k for it alone (the other rows of the score tile are masked by
+// passing T = b + 1).
 template <int EP>
-__global__ __launch_bounds__(1024) void route_reduce_topk_kernel(RouteArgs a, int nsplit) {
-  constexpr int LD = EP + 4;
-  __shared__ float lg[16 * LD];
+__global__ __launch_bounds__(256) void route_reduce_topk_kernel(RouteArgs a, int nsplit) {
+  constexpr int TPW = EP <= 16 ? 4 : (EP <= 32 ? 2 : 1);   // as in topk_from_lds
+  constexpr int BT = 4 * TPW, LD = EP + 4;
+  __shared__ float lg[BT * LD];
   const int tid = threadIdx.x, E = a.E;
-  for (int idx = tid; idx < 16 * EP; idx += 1024) {
-    const int tl = idx / EP, e = idx - tl * EP;
-    // parts added in order; eight loads in flight at a time
+  const int b = blockIdx.x;
+  for (int e = tid; e < EP; e += 256) {
+    float p[16];
     float v = 0.f;
-    int ks = 0;
-    for (; ks + 8 <= nsplit; ks += 8) {
-      float p[8];
+    for (int ks0 = 0; ks0 < nsplit; ks0 += 16) {
 #pragma unroll
-      for (int q = 0; q < 8; ++q) p[q] = a.partial[(int64_t)(ks + q) * 16 * EP + idx];
+      for (int u = 0; u < 16; ++u)
+        p[u] = ks0 + u < nsplit ? a.partial[((int64_t)(ks0 + u) * 16 + b) * EP + e] : 0.f;
 #pragma unroll
-      for (int q = 0; q < 8; ++q) v += p[q];
+      for (int u = 0; u < 16; ++u) v += p[u];
     }
-    for (; ks < nsplit; ++ks) v += a.partial[(int64_t)ks * 16 * EP + idx];
-    if (a.offset && e < E) v += a.offset[e];
-    lg[tl * LD + e] = v;
+    lg[e] = v + ((a.offset && e < E) ? a.offset[e] : 0.f);
   }
   __syncthreads();
-  if (a.logits) {
-    for (int idx = tid; idx < (int)a.T * E; idx += 1024) {
-      const int tl = idx / E, e = idx - tl * E;
-      a.logits[tl * E + e] = lg[tl * LD + e];
-    }
-  }
-  if (tid < 256) topk_from_lds<EP, 16>(lg, LD, a, 0);
+  if (a.logits)
+    for (int e = tid; e < E; e += 256) a.logits[(int64_t)b * E + e] = lg[e];
+  RouteArgs one = a;
+  one.T = b + 1;
+  topk_from_lds<EP, BT>(lg, LD, one, b);
 }
 
 int route_split(int d, int E) {
@@ -493,7 +494,7 @@ hipError_t launch_ep(const RouteArgs& a, hipStream_t s) {
   if (a.dtype == MOE_BF16 && a.T <= 16 && a.partial) {
     const int sp = route_split(a.d, a.E);
     route_partial_kernel<EP><<<dim3(EP / 16, sp), 256, 0, s>>>(a, sp);
-    route_reduce_topk_kernel<EP><<<1, 1024, 0, s>>>(a, sp);
+    route_reduce_topk_kernel<EP><<<(unsigned)a.T, 256, 0, s>>>(a, sp);
   } else if (a.dtype == MOE_BF16 && a.T <= 16)
     route_small_kernel<EP><<<1, RS_THREADS, 0, s>>>(a);
   else if (a.dtype == MOE_BF16)
