@@ -21,7 +21,9 @@ Modules:
 
 * ``moe_oracle`` -- numpy float64 definition of the forward pass, step by step
   (router scores, ordered top-k, gates, capacity, permutation, experts,
-  gate-weighted sum, shared experts).
+  gate-weighted sum, shared experts), and of the routing statistics a batch
+  yields (load fractions, mean router probabilities, balance loss, drop rate,
+  loss-free bias update).
 * ``brute``      -- pure-Python loops over tiny inputs: a second, independent
   spelling of the same definition that also counts multiplies.
 * ``accounting`` -- parameter and multiply counts the pages print.

@@ -130,3 +130,37 @@ def forward(x, w_r, w1, w2, w3=None, *, k, act, gating="softmax_topk",
                     out[i] += o[i]
         y.append(out)
     return y, idx_all, g_all, kept
+
+
+def routing_stats(logits, counts, k, num_dropped, alpha, bias, gamma):
+    """Balance signals with explicit loops [ITM-14 §Auxiliary loss;
+    ITM-14 §Auxiliary-loss-free balancing; LLM-T11 Exercise 4]: f_i = count_i
+    / T, P_i = average over tokens of exp(s_ti) / sum_j exp(s_tj), loss =
+    alpha * E * sum f_i P_i, drop rate = dropped / (T k), and the bias moved
+    by gamma against the load's side of the mean T k / E."""
+    T = len(logits)
+    E = len(logits[0])
+    f = [counts[i] / T for i in range(E)]
+    P = [0.0] * E
+    for t in range(T):
+        m = max(logits[t])
+        den = 0.0
+        for j in range(E):
+            den += math.exp(logits[t][j] - m)
+        for i in range(E):
+            P[i] += math.exp(logits[t][i] - m) / den / T
+    loss = 0.0
+    for i in range(E):
+        loss += f[i] * P[i]
+    loss *= alpha * E
+    new_bias = None
+    if bias is not None:
+        new_bias = []
+        for i in range(E):
+            if counts[i] * E > T * k:
+                new_bias.append(bias[i] - gamma)
+            elif counts[i] * E < T * k:
+                new_bias.append(bias[i] + gamma)
+            else:
+                new_bias.append(bias[i])
+    return f, P, loss, num_dropped / (T * k), new_bias

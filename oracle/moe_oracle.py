@@ -38,6 +38,11 @@ Steps (sources in the package docstring):
       renormalised, so a fully dropped token gets y = 0 (its residual carries
       it)  [ITM-14 §The computation; LLM-T11 §Expert capacity and dropped
       tokens; ITM-14 §Fine-grained and shared experts]
+ O9 ``routing_stats``   balance signals of a batch: load fractions f, mean
+      router probabilities P, the balance loss alpha N sum f P, the drop rate,
+      and the loss-free bias update  [ITM-14 §Auxiliary loss;
+      LLM-T11 §The auxiliary loss; LLM-T11 Exercise 4;
+      ITM-14 §Auxiliary-loss-free balancing]
 
 Readings of points the pages leave open are listed in the repository's design
 notes; each is restated at the function that takes it.
@@ -369,3 +374,50 @@ def route_from_logits(logits_f32, *, k, gating, capacity_factor=0.0,
     perm = permute(idx, E, C)
     return dict(keys=q, topk_idx=idx, gates=g, capacity=C, perm=perm,
                 near_tie=near_tie_tokens(q, k))
+
+
+# ----------------------------------------------------------------------------
+# O9  routing statistics and balance signals
+
+
+def softmax_probs(s):
+    """Router probabilities: the softmax over all E scores of each token
+    (max subtracted first) [LLM-T11 §The routing decision]."""
+    s = np.asarray(s, dtype=np.float64)
+    z = np.exp(s - s.max(axis=-1, keepdims=True))
+    return z / z.sum(axis=-1, keepdims=True)
+
+
+def routing_stats(logits, counts, *, k, num_dropped=0, alpha=0.01,
+                  select_bias=None, gamma=0.0):
+    """O9 from the scores s [T, E] (with any logit offset, as O1 returns them)
+    and the per-expert assignment counts before capacity (O6 ``counts``):
+
+      f_i  = count_i / T       fraction of the batch's tokens sent to expert i
+      P_i  = mean_t softmax(s_t)_i   average router probability of expert i
+      loss = alpha * E * sum_i f_i P_i          [ITM-14 §Auxiliary loss]
+      drop_rate = num_dropped / (T k)           [LLM-T11 Exercise 4]
+      bias_i' = bias_i - gamma if count_i > T k / E (overloaded),
+                bias_i + gamma if count_i < T k / E (underloaded),
+                bias_i          otherwise   [ITM-14 §Auxiliary-loss-free
+                balancing]
+
+    Readings: with k > 1 a token counts once for each expert it is sent to,
+    so sum f = k and N sum f P is k (not 1) under uniform routing; P is the
+    full-softmax probability for every gating; the load that decides the
+    bias update is the count before capacity, compared exactly (count_i * E
+    against T * k).  Returns a dict."""
+    s = np.asarray(logits, dtype=np.float64)
+    counts = np.asarray(counts, dtype=np.int64)
+    T, E = s.shape
+    f = counts.astype(np.float64) / T
+    P = softmax_probs(s).mean(axis=0)
+    loss = alpha * E * float(np.sum(f * P))
+    drop_rate = float(num_dropped) / (T * k)
+    bias_new = None
+    if select_bias is not None:
+        b = np.asarray(select_bias, dtype=np.float64)
+        load = counts * E          # compared with T * k: both exact integers
+        step = np.where(load > T * k, -gamma, np.where(load < T * k, gamma, 0.0))
+        bias_new = b + step
+    return dict(f=f, P=P, loss=loss, drop_rate=drop_rate, bias=bias_new)

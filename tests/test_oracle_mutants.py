@@ -29,11 +29,17 @@ def _battery():
     P.test_drop_count_closed_form_and_monotone()
     P.test_permutation_is_stable_bijection()
     P.test_partial_drop_not_renormalised()
+    P.test_balance_loss_is_alpha_at_uniform_routing()
+    P.test_balance_loss_is_alpha_n_at_collapse()
+    P.test_balance_loss_lower_for_balanced_than_collapsed_routing()
+    P.test_routing_stats_invariants_and_brute_force()
+    P.test_bias_update_hand_worked()
 
 
 _orig = {n: getattr(O, n) for n in (
     "sigmoid", "ordered_topk", "gate_values", "capacity", "permute",
-    "expert_ffn", "combine", "router_logits", "selection_keys", "gelu")}
+    "expert_ffn", "combine", "router_logits", "selection_keys", "gelu",
+    "routing_stats", "softmax_probs")}
 
 
 def m_sigmoid_sign(z):
@@ -109,7 +115,60 @@ def m_gelu_tanh(z):
     return 0.5 * z * (1 + np.tanh(math.sqrt(2 / math.pi) * (z + 0.044715 * z ** 3)))
 
 
+def m_stats_no_n(logits, counts, **kw):
+    r = _orig["routing_stats"](logits, counts, **kw)
+    r["loss"] /= np.asarray(logits).shape[1]
+    return r
+
+
+def m_stats_bias_sign(logits, counts, **kw):
+    kw = dict(kw)
+    kw["gamma"] = -kw.get("gamma", 0.0)
+    return _orig["routing_stats"](logits, counts, **kw)
+
+
+def m_stats_bias_ge(logits, counts, **kw):
+    # "at or above the mean" counted as overloaded
+    r = _orig["routing_stats"](logits, counts, **kw)
+    if r["bias"] is not None:
+        T, E = np.asarray(logits).shape
+        at = np.asarray(counts) * E == T * kw.get("k", 1)
+        r["bias"] = np.where(at, r["bias"] - kw.get("gamma", 0.0), r["bias"])
+    return r
+
+
+def m_stats_f_over_assignments(logits, counts, **kw):
+    r = _orig["routing_stats"](logits, counts, **kw)
+    k = kw.get("k", 1)
+    r["f"] = r["f"] / k
+    r["loss"] = r["loss"] / k
+    return r
+
+
+def m_stats_drop_rate_over_tokens(logits, counts, **kw):
+    r = _orig["routing_stats"](logits, counts, **kw)
+    r["drop_rate"] = r["drop_rate"] * kw.get("k", 1)
+    return r
+
+
+def m_probs_kept_only(s):
+    # probabilities of the top-2 experts only, renormalised (the gates, not
+    # the router's full distribution)
+    s = np.asarray(s, dtype=np.float64)
+    keep = np.zeros_like(s, dtype=bool)
+    top = np.argsort(-s, axis=-1, kind="stable")[:, :2]
+    np.put_along_axis(keep, top, True, axis=-1)
+    z = np.where(keep, np.exp(s - s.max(axis=-1, keepdims=True)), 0.0)
+    return z / z.sum(axis=-1, keepdims=True)
+
+
 MUTANTS = {
+    "balance_loss_without_n": ("routing_stats", m_stats_no_n),
+    "bias_update_sign_flipped": ("routing_stats", m_stats_bias_sign),
+    "bias_moves_at_mean_load": ("routing_stats", m_stats_bias_ge),
+    "load_fraction_over_assignments": ("routing_stats", m_stats_f_over_assignments),
+    "drop_rate_over_tokens": ("routing_stats", m_stats_drop_rate_over_tokens),
+    "router_probs_from_kept_experts": ("softmax_probs", m_probs_kept_only),
     "sigmoid_sign": ("sigmoid", m_sigmoid_sign),
     "topk_ties_to_high_index": ("ordered_topk", m_topk_high_index),
     "topk_smallest": ("ordered_topk", m_topk_ascending),

@@ -410,3 +410,91 @@ def test_parameter_accounting_matches_the_pages():
     # layer-level accounting: total vs active for the toy
     t, a = accounting.moe_layer_params(8, 2, 64, 256, "relu", router=False)
     assert (t, a) == (GOLD["toy_multiplies_all_fire"]["value"], GOLD["toy_multiplies_top2"]["value"])
+
+
+# ------------------------------------------------------------------ O9 stats
+# Balance signals [ITM-14 §Auxiliary loss; LLM-T11 §The auxiliary loss;
+# ITM-14 §Auxiliary-loss-free balancing; LLM-T11 Exercise 4].
+
+def test_balance_loss_is_alpha_at_uniform_routing():
+    # equal scores and equal loads: f = P = 1/N, so alpha N sum f P = alpha
+    # (the factor N makes the minimum 1 whatever N is [ITM-14 §Check yourself])
+    for E in (2, 4, 8, 64):
+        T = 3 * E
+        s = np.full((T, E), 0.25)
+        counts = np.full(E, T // E)
+        r = O.routing_stats(s, counts, k=1, alpha=0.01)
+        assert np.allclose(r["f"], 1.0 / E, rtol=0, atol=1e-15)
+        assert np.allclose(r["P"], 1.0 / E, rtol=0, atol=1e-15)
+        assert abs(r["loss"] - 0.01) < 1e-15
+
+
+def test_balance_loss_is_alpha_n_at_collapse():
+    # every token to expert 0 with probability 1: f = P = e_0, loss = alpha N
+    for E in (2, 8, 128):
+        T = 10
+        s = np.full((T, E), -60.0)
+        s[:, 0] = 60.0
+        counts = np.zeros(E, dtype=np.int64)
+        counts[0] = T
+        r = O.routing_stats(s, counts, k=1, alpha=0.01)
+        assert r["P"][0] == 1.0
+        assert abs(r["loss"] - 0.01 * E) < 1e-12
+
+
+def test_balance_loss_lower_for_balanced_than_collapsed_routing():
+    # the comparison the pages make [LLM-T11 §The auxiliary loss; LLM-T11
+    # Exercise 3]: probabilities drawn from a flat and from a peaked
+    # Dirichlet, each token sent to its most probable expert; log-probabilities
+    # are scores whose softmax is exactly those probabilities
+    rng = np.random.default_rng(0)
+    E, T = 4, 100
+    out = []
+    for conc in ([5.0] * E, [10.0, 0.1, 0.1, 0.1]):
+        p = rng.dirichlet(conc, size=T)
+        s = np.log(np.maximum(p, 1e-300))
+        assign = np.argmax(p, axis=-1)
+        counts = np.bincount(assign, minlength=E)
+        r = O.routing_stats(s, counts, k=1, alpha=0.01)
+        assert np.allclose(r["P"], p.mean(axis=0), rtol=1e-12, atol=1e-15)
+        out.append(r["loss"])
+    assert out[0] < out[1]
+
+
+def test_routing_stats_invariants_and_brute_force():
+    rng = np.random.default_rng(5)
+    for T, E, k in ((1, 3, 1), (5, 4, 2), (9, 6, 3), (12, 5, 5), (7, 8, 2)):
+        s = rng.normal(0.0, 2.0, size=(T, E))
+        idx = O.ordered_topk(s, k)
+        counts = np.bincount(idx.ravel(), minlength=E)
+        bias = rng.normal(0.0, 0.1, size=E)
+        dropped = int(rng.integers(0, T * k + 1))
+        r = O.routing_stats(s, counts, k=k, num_dropped=dropped, alpha=0.02,
+                            select_bias=bias, gamma=1e-3)
+        assert abs(r["f"].sum() - k) < 1e-12          # each token counted k times
+        assert abs(r["P"].sum() - 1.0) < 1e-12        # probabilities
+        assert 0.0 <= r["loss"] <= 0.02 * E * k + 1e-12
+        f, P, loss, rate, nb = brute.routing_stats(s.tolist(), counts.tolist(), k, dropped,
+                                                   0.02, bias.tolist(), 1e-3)
+        assert np.allclose(r["f"], f, rtol=0, atol=1e-15)
+        assert np.allclose(r["P"], P, rtol=1e-12, atol=1e-15)
+        assert abs(r["loss"] - loss) <= 1e-12 * max(1.0, loss)
+        assert r["drop_rate"] == rate
+        assert np.array_equal(r["bias"], np.array(nb))
+        # relabelling the experts permutes f and P and keeps the loss
+        perm = rng.permutation(E)
+        r2 = O.routing_stats(s[:, perm], counts[perm], k=k, alpha=0.02)
+        assert np.allclose(r2["P"], r["P"][perm], rtol=1e-12, atol=1e-15)
+        assert abs(r2["loss"] - r["loss"]) <= 1e-12 * max(1.0, r["loss"])
+
+
+def test_bias_update_hand_worked():
+    # T = 6 tokens, k = 2, E = 4: mean load T k / E = 3 assignments per expert;
+    # overloaded experts move down by gamma, underloaded up, the one at the
+    # mean stays [ITM-14 §Auxiliary-loss-free balancing]
+    s = np.zeros((6, 4))
+    r = O.routing_stats(s, np.array([5, 3, 1, 3]), k=2, select_bias=np.array([0.5, 0.0, -0.25, 1.0]),
+                        gamma=0.125)
+    assert r["bias"].tolist() == [0.375, 0.0, -0.125, 1.0]
+    # drop rate: 3 of the 12 assignments dropped [LLM-T11 Exercise 4]
+    assert O.routing_stats(s, np.array([5, 3, 1, 3]), k=2, num_dropped=3)["drop_rate"] == 0.25
