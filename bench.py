@@ -173,9 +173,9 @@ def main():
     B.forward(cfg, inp["x"], inp["w_router"], inp["w1"], inp["w2"], inp["w3"],
               logit_offset=inp["logit_offset"], select_bias=inp["select_bias"],
               ws1=inp["ws1"], ws3=inp["ws3"], ws2=inp["ws2"], ws=ws, y=y)
-    _, _, _, cnt, drp = B.forward_inputs(cfg, inp, ws=ws)
+    _, _, _, cnt_dev, drp_dev = B.forward_inputs(cfg, inp, ws=ws)
     torch.cuda.synchronize()
-    cnt = cnt.cpu().tolist()
+    cnt, drp = cnt_dev.cpu().tolist(), drp_dev
     if w.capacity_factor > 0:
         C = B.capacity(cfg, w.T)
         kept_counts = [min(c, C) for c in cnt]
@@ -221,17 +221,43 @@ def main():
     torch.cuda.synchronize()
     ms = t0.elapsed_time(t1) / args.steps
 
+    # routing statistics of the batch (balance signals; not part of the
+    # forward step): they read the scores, which the forward keeps internal
+    _, _, logits = B.route(cfg, inp["x"], inp["w_router"], inp["logit_offset"],
+                           inp["select_bias"], want_logits=True, ws=ws)
+    bias_in = (inp["select_bias"] if inp["select_bias"] is not None
+               else torch.zeros(w.E, dtype=torch.float32, device=dev))
+    stats_out = torch.empty(w.E, dtype=torch.float32, device=dev)
+
+    st_res = B.routing_stats(cfg, logits, cnt_dev, drp_dev, bias_in, gamma=1e-3, alpha=0.01,
+                             bias_out=stats_out, ws=ws)
+
+    def stats():
+        B.routing_stats(cfg, logits, cnt_dev, drp_dev, bias_in, gamma=1e-3, alpha=0.01,
+                        bias_out=stats_out, ws=ws, out=st_res)
+
+    torch.cuda.synchronize()
+
     # timed region 2: the same steps with the library's per-launch HIP events
     # (on the stream each kernel is launched on) for the per-kernel times
     B.profile_enable(True)
     torch.cuda.synchronize()
     for _ in range(args.steps):
         step()
+    for _ in range(args.steps):
+        stats()
     torch.cuda.synchronize()
     prof = B.profile_read()
     B.profile_enable(False)
 
     kern = {k: v[0] / max(v[1], 1) for k, v in prof.items()}
+    st_ms = kern.pop("routing_stats", float("nan"))
+    # bytes: the scores once, counts, bias in and out, f, P
+    st_bytes = w.T * w.E * 4 + 5 * w.E * 4
+    next_rows = {"routing_stats": {
+        "ms": st_ms, "bound": "hbm", "algorithmic_bytes": st_bytes,
+        "achieved_gbs": st_bytes / (st_ms * 1e-3) / 1e9,
+        "frac": st_bytes / (st_ms * 1e-3) / 1e9 / PEAK_HBM_GBS}}
     dom = "ffn1"
     dom_ms = kern.get(dom, float("nan"))
     peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
@@ -275,6 +301,7 @@ def main():
                     "dropped": int(drp.item())},
         "kernels_ms": {k: round(v, 5) for k, v in sorted(kern.items())},
         "roofline": roof,
+        "next_rows": next_rows,
     }
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, inp)

@@ -230,6 +230,44 @@ moe_status_t moe_forward(const moe_config_t* cfg, int64_t T, const void* x,
                          int32_t* expert_counts, int32_t* num_dropped,
                          void* workspace, size_t ws_bytes, void* stream);
 
+/* Routing statistics of one batch: the balance signals a routing pass yields
+ * (sources: "Mixture of experts", Inside the Model guide ch. 14, sections
+ * "Auxiliary loss" (balance-loss equation) and "Auxiliary-loss-free
+ * balancing"; "Mixture of Experts", LLM tutorial ch. 11, "The auxiliary loss"
+ * and Exercise 4):
+ *     f_i       = count_i / T                 fraction of tokens sent to i
+ *     P_i       = (1/T) sum_t softmax(s_t)_i  mean router probability of i
+ *                 (softmax over all E scores, for every gating)
+ *     loss      = alpha * E * sum_i f_i P_i   Switch balance loss
+ *     drop_rate = num_dropped / (T k)
+ *     bias_i'   = bias_i - gamma  if count_i * E > T k  (overloaded)
+ *                 bias_i + gamma  if count_i * E < T k  (underloaded)
+ *                 bias_i          otherwise
+ * With k > 1 a token counts once per expert it is sent to (sum f = k).
+ *   logits         [T, E] fp32 in: the scores s (+ offset), as moe_route
+ *                  writes them
+ *   expert_counts  [E] int32 in: assignments per expert before capacity, as
+ *                  moe_permute / moe_forward write them
+ *   num_dropped    [1] int32 in; needed only for drop_rate
+ *   select_bias    [E] fp32 in; needed only for bias_out
+ *   gamma, alpha   host scalars >= 0 (bias step, loss weight)
+ *   f, P           [E] fp32 out
+ *   loss           [1] fp32 out
+ *   drop_rate      [1] fp32 out, or NULL
+ *   bias_out       [E] fp32 out, or NULL; may be select_bias itself
+ *                  (in-place update)
+ *   workspace      device scratch of ws_bytes >= moe_workspace_size()
+ * fp32 throughout; sums run in a fixed order.  T = 0 enqueues nothing (the
+ * statistics of an empty batch are undefined).  Errors: MOE_ERR_INVALID_ARG
+ * for a missing required pointer, drop_rate without num_dropped, bias_out
+ * without select_bias, or negative / NaN gamma or alpha; MOE_ERR_WORKSPACE. */
+moe_status_t moe_routing_stats(const moe_config_t* cfg, int64_t T,
+                               const float* logits, const int32_t* expert_counts,
+                               const int32_t* num_dropped, const float* select_bias,
+                               float gamma, float alpha, float* f, float* P,
+                               float* loss, float* drop_rate, float* bias_out,
+                               void* workspace, size_t ws_bytes, void* stream);
+
 /* Per-kernel timing with HIP events, for measurement tools.
  * moe_profile_enable(1) clears the record and brackets every later launch by
  * this library with a pair of events on the launch's stream;

@@ -27,7 +27,7 @@ STATUS = {0: "MOE_OK", 1: "MOE_ERR_INVALID_ARG", 2: "MOE_ERR_UNSUPPORTED",
 
 EXPORTS = ("moe_status_str", "moe_check_config", "moe_workspace_size", "moe_capacity",
            "moe_route", "moe_permute", "moe_expert_ffn", "moe_combine", "moe_forward",
-           "moe_profile_enable", "moe_profile_read")
+           "moe_routing_stats", "moe_profile_enable", "moe_profile_read")
 
 
 class MoeError(RuntimeError):
@@ -68,6 +68,8 @@ def lib():
         L.moe_expert_ffn.argtypes = [_cfgp, _i64] + [_vp] * 12 + [_sz, _vp]
         L.moe_combine.argtypes = [_cfgp, _i64] + [_vp] * 5 + [_vp]
         L.moe_forward.argtypes = [_cfgp, _i64] + [_vp] * 16 + [_sz, _vp]
+        L.moe_routing_stats.argtypes = ([_cfgp, _i64] + [_vp] * 4 + [ctypes.c_float] * 2
+                                        + [_vp] * 6 + [_sz, _vp])
         L.moe_profile_enable.argtypes = [ctypes.c_int32]
         L.moe_profile_read.restype = ctypes.c_int32
         L.moe_profile_read.argtypes = [ctypes.POINTER(ctypes.c_char_p),
@@ -75,7 +77,7 @@ def lib():
                                        ctypes.POINTER(ctypes.c_int32), ctypes.c_int32]
         for fn in ("moe_check_config", "moe_workspace_size", "moe_capacity", "moe_route",
                    "moe_permute", "moe_expert_ffn", "moe_combine", "moe_forward",
-                   "moe_profile_enable"):
+                   "moe_routing_stats", "moe_profile_enable"):
             getattr(L, fn).restype = ctypes.c_int
         _lib_handle = L
     return _lib_handle
@@ -221,6 +223,34 @@ def forward_inputs(cfg, inp, **kw):
     return forward(cfg, inp["x"], inp["w_router"], inp["w1"], inp["w2"], inp.get("w3"),
                    logit_offset=inp.get("logit_offset"), select_bias=inp.get("select_bias"),
                    ws1=inp.get("ws1"), ws3=inp.get("ws3"), ws2=inp.get("ws2"), **kw)
+
+
+def routing_stats(cfg, logits, expert_counts, num_dropped=None, select_bias=None, gamma=0.0,
+                  alpha=0.01, bias_out=None, ws=None, out=None):
+    """Balance signals of one batch.  Returns dict(f, P, loss, drop_rate,
+    bias); drop_rate needs num_dropped, bias needs select_bias (bias_out may
+    be select_bias itself for an in-place update).  ``out`` may be an earlier
+    result dict whose tensors are then reused."""
+    T = logits.shape[0]
+    dev = logits.device
+    E = cfg.num_experts
+    if out is not None:
+        f, P, loss, rate = out["f"], out["P"], out["loss"], out["drop_rate"]
+    else:
+        f = torch.empty(E, dtype=torch.float32, device=dev)
+        P = torch.empty(E, dtype=torch.float32, device=dev)
+        loss = torch.empty(1, dtype=torch.float32, device=dev)
+        rate = torch.empty(1, dtype=torch.float32, device=dev) if num_dropped is not None else None
+    if select_bias is not None and bias_out is None:
+        bias_out = torch.empty(E, dtype=torch.float32, device=dev)
+    if ws is None:
+        ws = workspace(cfg, T, dev)
+    _check(lib().moe_routing_stats(ctypes.byref(cfg), T, _ptr(logits), _ptr(expert_counts),
+                                   _ptr(num_dropped), _ptr(select_bias), float(gamma),
+                                   float(alpha), _ptr(f), _ptr(P), _ptr(loss), _ptr(rate),
+                                   _ptr(bias_out), _ptr(ws), ws.numel(), _stream()),
+           "moe_routing_stats")
+    return dict(f=f, P=P, loss=loss, drop_rate=rate, bias=bias_out)
 
 
 def profile_enable(on=True):

@@ -72,6 +72,26 @@ size_t ffn_plan_bytes(int64_t max_rows, int G, int N, bool small, int dtype);
 hipError_t launch_ffn_plans(const FfnPassArgs& p1, const FfnPassArgs& p2, hipStream_t s);
 hipError_t launch_ffn_pass(const FfnPassArgs& a, hipStream_t s);
 
+// Routing statistics (balance signals) of one batch.
+struct StatsArgs {
+  const float* logits;      // [T, E] router scores
+  const int32_t* counts;    // [E] assignments per expert before capacity
+  const int32_t* dropped;   // [1] (read only when drop_rate is set)
+  const float* bias;        // [E] (read only when bias_out is set)
+  float gamma, alpha;
+  float* f;                 // [E]
+  float* P;                 // [E]
+  float* loss;              // [1]
+  float* drop_rate;         // [1] or null
+  float* bias_out;          // [E] or null (may alias bias)
+  float* partial;           // workspace, stats_ws_bytes()
+  int64_t T;
+  int E, k;
+};
+int stats_nblocks(int64_t T);
+size_t stats_ws_bytes(int64_t T, int E);
+hipError_t launch_stats(const StatsArgs& a, hipStream_t s);
+
 struct CombineArgs {
   const void* expert_out;   // [T*k, d]
   const int32_t* slot_pos;  // [T*k]

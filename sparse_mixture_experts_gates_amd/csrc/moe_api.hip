@@ -136,7 +136,7 @@ FfnWs ffn_ws(const moe_config_t* c, int64_t T) {
 
 struct FwdWs {
   size_t idx, gate, counts, dropped, offsets, perm_src, slot_pos, eout, sout, route, perm, ffn,
-      total;
+      stats, total;
 };
 FwdWs fwd_ws(const moe_config_t* c, int64_t T) {
   FwdWs w;
@@ -154,6 +154,7 @@ FwdWs fwd_ws(const moe_config_t* c, int64_t T) {
   w.route = o; o += up(route_ws_bytes(T, c->num_experts, c->dtype));
   w.perm = o; o += perm_ws(c, T).total;
   w.ffn = o; o += ffn_ws(c, T).total;
+  w.stats = o; o += up(stats_ws_bytes(T, c->num_experts));
   w.total = o;
   return w;
 }
@@ -476,6 +477,44 @@ int32_t moe_profile_read(const char** names, double* total_ms, int32_t* launches
     if (launches) launches[n] = cnt[i];
   }
   return n;
+}
+
+moe_status_t moe_routing_stats(const moe_config_t* cfg, int64_t T, const float* logits,
+                               const int32_t* expert_counts, const int32_t* num_dropped,
+                               const float* select_bias, float gamma, float alpha, float* f,
+                               float* P, float* loss, float* drop_rate, float* bias_out,
+                               void* workspace, size_t ws_bytes, void* stream) {
+  moe_status_t st = check_cfg(cfg, T);
+  if (st != MOE_OK) return st;
+  if (T == 0) return MOE_OK;
+  if (!logits || !expert_counts || !f || !P || !loss) return MOE_ERR_INVALID_ARG;
+  if (drop_rate && !num_dropped) return MOE_ERR_INVALID_ARG;
+  if (bias_out && !select_bias) return MOE_ERR_INVALID_ARG;
+  if (!(gamma >= 0.f) || !(alpha >= 0.f)) return MOE_ERR_INVALID_ARG;   // also rejects NaN
+  if (!al(logits, 4) || !al(expert_counts, 4) || !al(f, 4) || !al(P, 4) || !al(loss, 4) ||
+      (num_dropped && !al(num_dropped, 4)) || (select_bias && !al(select_bias, 4)) ||
+      (drop_rate && !al(drop_rate, 4)) || (bias_out && !al(bias_out, 4)))
+    return MOE_ERR_INVALID_ARG;
+  if (workspace && !al(workspace, ALIGN)) return MOE_ERR_INVALID_ARG;
+  const FwdWs w = fwd_ws(cfg, T);
+  if (!workspace || ws_bytes < w.total) return MOE_ERR_WORKSPACE;
+  StatsArgs a;
+  a.logits = logits;
+  a.counts = expert_counts;
+  a.dropped = num_dropped;
+  a.bias = select_bias;
+  a.gamma = gamma;
+  a.alpha = alpha;
+  a.f = f;
+  a.P = P;
+  a.loss = loss;
+  a.drop_rate = drop_rate;
+  a.bias_out = bias_out;
+  a.partial = reinterpret_cast<float*>(at(workspace, w.stats));
+  a.T = T;
+  a.E = cfg->num_experts;
+  a.k = cfg->top_k;
+  return hip_status(launch_stats(a, static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

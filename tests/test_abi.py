@@ -26,7 +26,7 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("moe_route", "moe_permute", "moe_expert_ffn", "moe_combine", "moe_forward",
-              "moe_workspace_size", "moe_capacity", "moe_status_str"):
+              "moe_routing_stats", "moe_workspace_size", "moe_capacity", "moe_status_str"):
         assert n in names
 
 
@@ -111,6 +111,17 @@ def test_entry_points_reject_bad_arguments_before_any_gpu_work():
     assert L.moe_forward(ctypes.byref(c), 10, p, p, n, n, p, n, p, n, n, n, p, n, n, n, n, p, 1 << 40, n) == 1
     sh = cfg(num_shared=1, d_ff_shared=128)
     assert L.moe_forward(ctypes.byref(sh), 10, p, p, n, n, p, p, p, n, n, n, p, n, n, n, n, p, 1 << 40, n) == 1
+    # routing statistics: required pointers, optional pairs, scalars, workspace
+    f32 = ctypes.c_float
+    st = L.moe_routing_stats
+    assert st(ctypes.byref(c), 10, n, p, n, n, f32(0), f32(0.01), p, p, p, n, n, p, 1 << 30, n) == 1
+    assert st(ctypes.byref(c), 10, p, p, n, n, f32(0), f32(0.01), p, p, p, p, n, p, 1 << 30, n) == 1  # rate needs dropped
+    assert st(ctypes.byref(c), 10, p, p, p, n, f32(0), f32(0.01), p, p, p, p, p, p, 1 << 30, n) == 1  # bias needs bias in
+    assert st(ctypes.byref(c), 10, p, p, n, p, f32(-1), f32(0.01), p, p, p, n, p, p, 1 << 30, n) == 1
+    assert st(ctypes.byref(c), 10, p, p, n, n, f32(0), f32(float("nan")), p, p, p, n, n, p, 1 << 30, n) == 1
+    assert st(ctypes.byref(c), 10, mis, p, n, n, f32(0), f32(0.01), p, p, p, n, n, p, 1 << 30, n) == 1
+    assert st(ctypes.byref(c), 10, p, p, n, n, f32(0), f32(0.01), p, p, p, n, n, p, 16, n) == 3
+    assert st(ctypes.byref(c), 0, n, n, n, n, f32(0), f32(0.01), n, n, n, n, n, n, 0, n) == 0
     # T = 0 is a valid no-op for every entry point
     assert L.moe_route(ctypes.byref(c), 0, p, p, n, n, n, p, p, n, 0, n) == 0
     assert L.moe_permute(ctypes.byref(c), 0, p, n, n, p, p, p, n, n, n, 0, n) == 0
