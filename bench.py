@@ -6,13 +6,16 @@ row gather, the two grouped expert GEMMs (and shared expert), and the
 gate-weighted combine.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                    [--no-cpu-baseline] [--copy-calib MiB]
+                    [--no-cpu-baseline] [--graph] [--cold-runs N] [--copy-calib MiB]
 
-Prints one JSON line.  `value` is tokens/s of the whole layer; `roofline`
-reports the dominant kernel (the first grouped GEMM) against the bf16 MFMA
-peak, timed with HIP events recorded by the library around each of its
-launches inside the timed region; `cpu_baseline` times the CPU oracle on a
-bounded token sample of the same workload.
+Prints one JSON line.  `value` is tokens/s of the whole layer over K
+back-to-back steps; `roofline` reports the dominant kernel (the first grouped
+GEMM) against the bf16 MFMA peak (HBM peak for a decode batch), timed with HIP
+events recorded by the library around each of its launches inside a second
+timed region; `cold` times N single steps each after a 1 GiB write that
+evicts L2 and the Infinity Cache; `next_rows` times the routing statistics
+call; `cpu_baseline` times the CPU oracle on a bounded token sample of the
+same workload.
 """
 
 from __future__ import annotations
@@ -83,13 +86,17 @@ def measured_traffic(kernel, workload):
     return d["traffic_bytes"]
 
 
-def cpu_baseline(w, inp, budget_s=15.0):
+def cpu_baseline(w, inp, flops_per_token, budget_s=15.0):
     """Time the CPU oracle (as it stands) on a bounded sample of tokens."""
     import numpy as np
     from oracle import moe_oracle as O
+    blas = "unknown"
     try:
         from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        info = threadpool_info()
+        threads = max([i.get("num_threads", 1) for i in info] or [1])
+        blas = ", ".join(sorted({f"{i.get('internal_api')} {i.get('version')}" for i in info
+                                 if i.get("user_api") == "blas"})) or blas
     except Exception:  # pragma: no cover
         threads = len(os.sched_getaffinity(0))
 
@@ -123,6 +130,7 @@ def cpu_baseline(w, inp, budget_s=15.0):
         reps += 1
     what = f"first {n} of the {w.T} tokens" if n < w.T else f"all {w.T} tokens"
     return {"value": reps * n / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "blas": blas, "gflops": reps * n * flops_per_token / dt / 1e9,
             "sample": f"{what} of {w.name}, {reps} pass(es) of the numpy float64 oracle "
                       f"forward (all routed experts touched by them), {dt:.1f} s"}
 
@@ -136,6 +144,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--graph", action="store_true",
                     help="capture one step in a HIP graph (torch.cuda.CUDAGraph) and time replays")
+    ap.add_argument("--cold-runs", type=int, default=20,
+                    help="extra single-step runs, each after writing 1 GiB to flush L2 and "
+                         "the Infinity Cache (median / min / p90 reported; 0 = skip)")
     ap.add_argument("--copy-calib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -221,6 +232,27 @@ def main():
     torch.cuda.synchronize()
     ms = t0.elapsed_time(t1) / args.steps
 
+    # cold runs: each step after a 1 GiB write that evicts L2 and the 256 MB
+    # Infinity Cache (the flush is not timed)
+    cold = None
+    if args.cold_runs > 0:
+        flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+        c0 = torch.cuda.Event(enable_timing=True)
+        c1 = torch.cuda.Event(enable_timing=True)
+        times = []
+        for i in range(args.cold_runs):
+            flush.fill_(float(i))
+            c0.record()
+            run()
+            c1.record()
+            torch.cuda.synchronize()
+            times.append(c0.elapsed_time(c1))
+        del flush
+        times.sort()
+        cold = {"runs": len(times), "median_ms": times[len(times) // 2], "min_ms": times[0],
+                "p90_ms": times[min(len(times) - 1, int(0.9 * len(times)))],
+                "tokens_per_s_median": w.T / (times[len(times) // 2] * 1e-3)}
+
     # routing statistics of the batch (balance signals; not part of the
     # forward step): they read the scores, which the forward keeps internal
     _, _, logits = B.route(cfg, inp["x"], inp["w_router"], inp["logit_offset"],
@@ -302,9 +334,10 @@ def main():
         "kernels_ms": {k: round(v, 5) for k, v in sorted(kern.items())},
         "roofline": roof,
         "next_rows": next_rows,
+        "cold": cold,
     }
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(w, inp)
+        res["cpu_baseline"] = cpu_baseline(w, inp, work["flops"] / w.T)
     print(json.dumps(res), flush=True)
 
 
