@@ -32,6 +32,7 @@
 
 #include "common.h"
 #include "launch.h"
+#include "plan.h"
 
 namespace moe {
 
@@ -39,14 +40,6 @@ namespace {
 
 constexpr int MODE_PLAIN = 0, MODE_RELU = 1, MODE_GELU = 2, MODE_SWIGLU = 3;
 constexpr int BK = 64;
-
-struct PlanEntry {
-  int32_t g, m0, m1, nt;
-};
-
-// Plan buffer: a 128-byte header (int32 entry count, then at int32 index
-// kPlanHeads the 8 per-XCD queue words, 64-bit each), then the entries.
-constexpr int kPlanHeader = 128, kPlanHeads = 4;
 
 struct KArgs {
   const uint16_t* A;   // or float*
@@ -62,58 +55,22 @@ struct KArgs {
   int64_t a_seg_rows, c_seg_rows;  // extra row offset per segment (shared experts)
 };
 
-// Plan: one workgroup; G <= 1024 segments.  Writes the entries of one pass
-// (NT column tiles) and, when NT2 > 0, of a second pass over the same row
-// tiles with NT2 column tiles (the two expert GEMMs share their row tiling).
-__global__ __launch_bounds__(1024) void ffn_plan_kernel(
-    const int32_t* __restrict__ seg, int G, int64_t dense_rows, int BM, int NT,
-    PlanEntry* __restrict__ plan, int32_t* __restrict__ count, int NT2,
-    PlanEntry* __restrict__ plan2, int32_t* __restrict__ count2) {
+// Plan: one workgroup; G <= 1024 segments (offsets seg[G+1], or G dense
+// segments of dense_rows rows).
+__global__ __launch_bounds__(1024) void ffn_plan_kernel(const int32_t* __restrict__ seg, int G,
+                                                        int64_t dense_rows, PlanSpec ps) {
   __shared__ int mt[1024];
   __shared__ int start[1024];
   __shared__ int rows_s[1024];
   __shared__ int base[1025];
-  const int tid = threadIdx.x;
-  for (int g = tid; g < G; g += 1024) {
+  for (int g = threadIdx.x; g < G; g += 1024) {
     const int r0 = seg ? seg[g] : 0;
     const int r1 = seg ? seg[g + 1] : (int)dense_rows;
     start[g] = r0;
     rows_s[g] = r1 - r0;
-    mt[g] = (r1 - r0 + BM - 1) / BM;
   }
   __syncthreads();
-  if (tid == 0) {
-    int acc = 0;
-    for (int g = 0; g < G; ++g) {
-      base[g] = acc;
-      acc += mt[g];
-    }
-    base[G] = acc;
-  }
-  __syncthreads();
-  const int MT = base[G];   // row tiles over all segments
-  for (int pass = 0; pass < 2; ++pass) {
-    const int nt_all = pass == 0 ? NT : NT2;
-    PlanEntry* out = pass == 0 ? plan : plan2;
-    if (nt_all <= 0) break;
-    const int V = MT * nt_all;
-    for (int L = tid; L < V; L += 1024) {
-      // entry L: segment-major, then column tile, then row tile
-      int lo = 0, hi = G - 1;  // last g with base[g] * nt_all <= L
-      while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (base[mid] * nt_all <= L) lo = mid; else hi = mid - 1;
-      }
-      const int g = lo, rem = L - base[g] * nt_all, m = mt[g];
-      const int nt = rem / m, mi = rem - nt * m;
-      const int m0 = start[g] + mi * BM;
-      int m1 = m0 + BM;
-      if (m1 > start[g] + rows_s[g]) m1 = start[g] + rows_s[g];
-      out[L] = PlanEntry{g, m0, m1, nt};
-    }
-    if (tid == 0) (pass == 0 ? count : count2)[0] = V;
-    if (tid < 16) (pass == 0 ? count : count2)[kPlanHeads + tid] = 0;   // queue words
-  }
+  build_tile_plans(start, rows_s, G, ps, mt, base);
 }
 
 // XCD-aware order: physical block P runs on XCD P % 8; give each XCD a
@@ -544,7 +501,8 @@ __global__ __launch_bounds__(256) void ffn_f32_kernel(KArgs a) {
 }
 
 struct Shape {
-  int BM, BNOUT, id;   // id: 0 fp32, 1 small batch, 2 big 256x256, 3 256x128
+  int BM, BNOUT, id;   // id: 0 fp32, 1 small batch SwiGLU 32x128, 2 256x256, 3 256x128,
+                       //     4 small batch plain 32x64
 };
 
 constexpr int kCUs = 256;
@@ -555,7 +513,9 @@ constexpr int kCUs = 256;
 Shape pick_shape(int dtype, bool small, int mode, int64_t max_rows, int N) {
   if (dtype == MOE_F32) return {64, 64, 0};
   const bool glu = mode == MODE_SWIGLU;
-  if (small) return {32, glu ? 64 : 128, 1};
+  // small batches stream each active expert's weights once; narrower
+  // 64-row weight tiles (3 blocks per CU) shorten the last round
+  if (small) return glu ? Shape{32, 64, 1} : Shape{32, 64, 4};
   const int64_t big_tiles = ((max_rows + 255) / 256) * ((N + (glu ? 127 : 255)) / (glu ? 128 : 256));
   if (big_tiles < 2 * kCUs) return {256, glu ? 64 : 128, 3};
   return {256, glu ? 128 : 256, 2};
@@ -613,18 +573,27 @@ int pass_nt(const FfnPassArgs& p) {
 }
 }  // namespace
 
-hipError_t launch_ffn_plans(const FfnPassArgs& p1, const FfnPassArgs& p2, hipStream_t s) {
+bool ffn_plan_spec(const FfnPassArgs& p1, const FfnPassArgs& p2, PlanSpec* ps) {
   const Shape sh1 = pick_shape(p1.dtype, p1.small, p1.mode, p1.max_rows, p1.N);
   const Shape sh2 = pick_shape(p2.dtype, p2.small, p2.mode, p2.max_rows, p2.N);
-  if (sh1.BM != sh2.BM || p1.seg_offsets != p2.seg_offsets) return hipErrorInvalidValue;
-  if (max_entries(p1.max_rows, p1.G, p1.N, sh1) == 0) return hipSuccess;
-  int32_t* c1 = static_cast<int32_t*>(p1.plan);
-  int32_t* c2 = static_cast<int32_t*>(p2.plan);
-  PlanEntry* e1 = reinterpret_cast<PlanEntry*>(static_cast<char*>(p1.plan) + kPlanHeader);
-  PlanEntry* e2 = reinterpret_cast<PlanEntry*>(static_cast<char*>(p2.plan) + kPlanHeader);
+  if (sh1.BM != sh2.BM || p1.seg_offsets != p2.seg_offsets) return false;
+  if (max_entries(p1.max_rows, p1.G, p1.N, sh1) == 0) return false;
+  ps->BM = sh1.BM;
+  ps->NT = pass_nt(p1);
+  ps->NT2 = pass_nt(p2);
+  ps->plan = static_cast<int32_t*>(p1.plan);
+  ps->plan2 = static_cast<int32_t*>(p2.plan);
+  return true;
+}
+
+hipError_t launch_ffn_plans(const FfnPassArgs& p1, const FfnPassArgs& p2, hipStream_t s) {
+  PlanSpec ps;
+  if (!ffn_plan_spec(p1, p2, &ps)) {
+    const Shape sh1 = pick_shape(p1.dtype, p1.small, p1.mode, p1.max_rows, p1.N);
+    return max_entries(p1.max_rows, p1.G, p1.N, sh1) == 0 ? hipSuccess : hipErrorInvalidValue;
+  }
   prof_before(p1.seg_offsets ? "ffn_plan" : "ffn_plan_shared", s);
-  ffn_plan_kernel<<<1, 1024, 0, s>>>(p1.seg_offsets, p1.G, p1.dense_rows, sh1.BM, pass_nt(p1), e1, c1,
-                                     pass_nt(p2), e2, c2);
+  ffn_plan_kernel<<<1, 1024, 0, s>>>(p1.seg_offsets, p1.G, p1.dense_rows, ps);
   prof_after(s);
   return hipGetLastError();
 }
@@ -661,6 +630,15 @@ hipError_t launch_ffn_pass(const FfnPassArgs& p, hipStream_t s) {
     }
   } else if (sh.id == 1) {
     launch_bf16<32, 128, 1, 4, 4, 4, false>(p.mode, (unsigned)grid, k, s);
+  } else if (sh.id == 4) {
+    // plain / ReLU / GeLU only (a SwiGLU wave needs a pair of column tiles)
+    constexpr int T4 = 64 * 4;
+    switch (p.mode) {
+      case MODE_PLAIN: ffn_bf16_kernel<32, 64, 1, 4, 4, 4, MODE_PLAIN, false><<<(unsigned)grid, T4, 0, s>>>(k); break;
+      case MODE_RELU: ffn_bf16_kernel<32, 64, 1, 4, 4, 4, MODE_RELU, false><<<(unsigned)grid, T4, 0, s>>>(k); break;
+      case MODE_GELU: ffn_bf16_kernel<32, 64, 1, 4, 4, 4, MODE_GELU, false><<<(unsigned)grid, T4, 0, s>>>(k); break;
+      default: return hipErrorInvalidValue;
+    }
   } else {
     // With at least two rounds of tiles: one persistent block per CU (the
     // LDS ring fills a CU).  Fewer, short tiles do not repay the queue.

@@ -27,6 +27,15 @@ struct RouteArgs {
 size_t route_ws_bytes(int64_t T, int E, int dtype);
 hipError_t launch_route(const RouteArgs& a, hipStream_t s);
 
+// Where and how the tile plans of an expert FFN's two GEMM passes go (same
+// row tiling): row tile height, column tiles per pass, and the two plan
+// buffers (header + entries).
+struct PlanSpec {
+  int BM, NT, NT2;
+  int32_t* plan;
+  int32_t* plan2;
+};
+
 struct PermuteArgs {
   const int32_t* topk_idx;  // [T*k]
   const void* x;            // [T, d] (may be null when x_perm is null)
@@ -41,9 +50,12 @@ struct PermuteArgs {
   int64_t T;
   int k, E, d, dtype;
   int64_t capacity;         // < 0: unlimited
+  const PlanSpec* plans;    // optional: the routed experts' GEMM plans, built
+                            // here when the one-workgroup path runs
 };
 int permute_nblocks(int64_t rows);
-hipError_t launch_permute(const PermuteArgs& a, hipStream_t s);
+// *plans_built (if given) tells whether a.plans were written.
+hipError_t launch_permute(const PermuteArgs& a, hipStream_t s, bool* plans_built = nullptr);
 
 // One grouped GEMM pass over ragged row segments:
 //   C[r, n] = epilogue( sum_k A[r, k] * W_seg[n, k] )  for r in the segment.
@@ -67,6 +79,9 @@ struct FfnPassArgs {
   bool small;             // small-batch (decode) tile shape
 };
 size_t ffn_plan_bytes(int64_t max_rows, int G, int N, bool small, int dtype);
+// The plan layout of the two passes of one expert FFN; false if there is
+// nothing to plan (no rows).
+bool ffn_plan_spec(const FfnPassArgs& p1, const FfnPassArgs& p2, PlanSpec* ps);
 // One plan kernel for the two passes of an expert FFN (same row tiles; the
 // entries go to p1.plan and p2.plan), then one GEMM launch per pass.
 hipError_t launch_ffn_plans(const FfnPassArgs& p1, const FfnPassArgs& p2, hipStream_t s);

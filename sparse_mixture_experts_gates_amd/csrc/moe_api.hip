@@ -174,7 +174,8 @@ moe_status_t do_route(const moe_config_t* c, int64_t T, const void* x, const voi
 moe_status_t do_permute(const moe_config_t* c, int64_t T, const int32_t* idx, const void* x,
                         int32_t* counts, int32_t* offsets, int32_t* perm_src,
                         int32_t* slot_pos, int32_t* dropped, void* x_perm, void* ws,
-                        hipStream_t s) {
+                        hipStream_t s, const PlanSpec* plans = nullptr,
+                        bool* plans_built = nullptr) {
   const PermWs w = perm_ws(c, T);
   PermuteArgs a;
   a.topk_idx = idx;
@@ -193,20 +194,28 @@ moe_status_t do_permute(const moe_config_t* c, int64_t T, const int32_t* idx, co
   a.d = c->d;
   a.dtype = c->dtype;
   a.capacity = capacity_of(c, T);
-  return hip_status(launch_permute(a, s));
+  a.plans = plans;
+  return hip_status(launch_permute(a, s, plans_built));
 }
 
-// x_perm may be null when perm_src is given: the first GEMM then reads the
-// rows of x through perm_src (row gather folded into its operand loads).
-moe_status_t do_ffn(const moe_config_t* c, int64_t T, const void* x, const void* x_perm,
-                    const int32_t* perm_src, const int32_t* offsets, const void* w1,
-                    const void* w3, const void* w2, const void* ws1, const void* ws3,
-                    const void* ws2, void* eout, void* sout, void* ws, hipStream_t s) {
+// The GEMM passes of the routed experts (p, p2) and of the shared experts
+// (q, q2).  x_perm may be null when perm_src is given: the first GEMM then
+// reads the rows of x through perm_src (row gather folded into its loads).
+struct FfnPasses {
+  FfnPassArgs p, p2, q, q2;
+  bool shared;
+};
+
+FfnPasses ffn_passes(const moe_config_t* c, int64_t T, const void* x, const void* x_perm,
+                     const int32_t* perm_src, const int32_t* offsets, const void* w1,
+                     const void* w3, const void* w2, const void* ws1, const void* ws3,
+                     const void* ws2, void* eout, void* sout, void* ws) {
   const FfnWs w = ffn_ws(c, T);
   const int64_t R = T * c->top_k;
   const int mode1 = c->act == MOE_ACT_SWIGLU ? 3 : (c->act == MOE_ACT_GELU ? 2 : 1);
-  FfnPassArgs p;
-  memset(&p, 0, sizeof(p));
+  FfnPasses f;
+  memset(&f, 0, sizeof(f));
+  FfnPassArgs& p = f.p;
   p.A = x_perm ? x_perm : x;
   p.a_rows = x_perm ? nullptr : perm_src;
   p.a_div = c->top_k;
@@ -222,7 +231,8 @@ moe_status_t do_ffn(const moe_config_t* c, int64_t T, const void* x, const void*
   p.plan = at(ws, w.plan1);
   p.max_rows = R;
   p.small = small_batch(R);
-  FfnPassArgs p2 = p;
+  FfnPassArgs& p2 = f.p2;
+  p2 = p;
   p2.A = at(ws, w.H);
   p2.a_rows = nullptr;
   p2.w = w2;
@@ -232,13 +242,10 @@ moe_status_t do_ffn(const moe_config_t* c, int64_t T, const void* x, const void*
   p2.N = c->d;
   p2.mode = 0;
   p2.plan = at(ws, w.plan2);
-  if (launch_ffn_plans(p, p2, s) != hipSuccess) return MOE_ERR_HIP;
-  if (launch_ffn_pass(p, s) != hipSuccess) return MOE_ERR_HIP;
-  if (launch_ffn_pass(p2, s) != hipSuccess) return MOE_ERR_HIP;
-  if (c->num_shared > 0) {
+  f.shared = c->num_shared > 0;
+  if (f.shared) {
     const int S = c->num_shared;
-    FfnPassArgs q;
-    memset(&q, 0, sizeof(q));
+    FfnPassArgs& q = f.q;
     q.A = x;
     q.w = ws1;
     q.w_up = ws3;
@@ -255,7 +262,8 @@ moe_status_t do_ffn(const moe_config_t* c, int64_t T, const void* x, const void*
     q.plan = at(ws, w.plan3);
     q.max_rows = (int64_t)S * T;
     q.small = small_batch(T);
-    FfnPassArgs q2 = q;
+    FfnPassArgs& q2 = f.q2;
+    q2 = q;
     q2.A = at(ws, w.Hs);
     q2.w = ws2;
     q2.w_up = nullptr;
@@ -265,11 +273,30 @@ moe_status_t do_ffn(const moe_config_t* c, int64_t T, const void* x, const void*
     q2.mode = 0;
     q2.a_seg_rows = T;
     q2.plan = at(ws, w.plan4);
-    if (launch_ffn_plans(q, q2, s) != hipSuccess) return MOE_ERR_HIP;
-    if (launch_ffn_pass(q, s) != hipSuccess) return MOE_ERR_HIP;
-    if (launch_ffn_pass(q2, s) != hipSuccess) return MOE_ERR_HIP;
+  }
+  return f;
+}
+
+// routed_plans_built: the permutation already wrote the routed experts' plans
+moe_status_t run_ffn(const FfnPasses& f, bool routed_plans_built, hipStream_t s) {
+  if (!routed_plans_built && launch_ffn_plans(f.p, f.p2, s) != hipSuccess) return MOE_ERR_HIP;
+  if (launch_ffn_pass(f.p, s) != hipSuccess) return MOE_ERR_HIP;
+  if (launch_ffn_pass(f.p2, s) != hipSuccess) return MOE_ERR_HIP;
+  if (f.shared) {
+    if (launch_ffn_plans(f.q, f.q2, s) != hipSuccess) return MOE_ERR_HIP;
+    if (launch_ffn_pass(f.q, s) != hipSuccess) return MOE_ERR_HIP;
+    if (launch_ffn_pass(f.q2, s) != hipSuccess) return MOE_ERR_HIP;
   }
   return MOE_OK;
+}
+
+moe_status_t do_ffn(const moe_config_t* c, int64_t T, const void* x, const void* x_perm,
+                    const int32_t* perm_src, const int32_t* offsets, const void* w1,
+                    const void* w3, const void* w2, const void* ws1, const void* ws3,
+                    const void* ws2, void* eout, void* sout, void* ws, hipStream_t s) {
+  return run_ffn(ffn_passes(c, T, x, x_perm, perm_src, offsets, w1, w3, w2, ws1, ws3, ws2, eout,
+                            sout, ws),
+                 false, s);
 }
 
 moe_status_t do_combine(const moe_config_t* c, int64_t T, const void* eout,
@@ -420,11 +447,17 @@ moe_status_t moe_forward(const moe_config_t* cfg, int64_t T, const void* x, cons
   st = do_route(cfg, T, x, w_router, logit_offset, select_bias, nullptr, idx, gate,
                 route_ws_bytes(T, cfg->num_experts, cfg->dtype) ? at(workspace, w.route) : nullptr, s);
   if (st != MOE_OK) return st;
+  // the permutation also writes the GEMM tile plans when it runs as one
+  // workgroup (small batches), which saves the plan kernel's launch
+  const FfnPasses passes = ffn_passes(cfg, T, x, nullptr, perm_src, offsets, w1, w3, w2, ws1,
+                                      ws3, ws2, eout, sout, at(workspace, w.ffn));
+  PlanSpec spec;
+  const bool have_spec = ffn_plan_spec(passes.p, passes.p2, &spec);
+  bool built = false;
   st = do_permute(cfg, T, idx, x, counts, offsets, perm_src, slot_pos, dropped, nullptr,
-                  at(workspace, w.perm), s);
+                  at(workspace, w.perm), s, have_spec ? &spec : nullptr, &built);
   if (st != MOE_OK) return st;
-  st = do_ffn(cfg, T, x, nullptr, perm_src, offsets, w1, w3, w2, ws1, ws3, ws2, eout, sout,
-              at(workspace, w.ffn), s);
+  st = run_ffn(passes, built, s);
   if (st != MOE_OK) return st;
   return do_combine(cfg, T, eout, slot_pos, gate, sout, y, s);
 }

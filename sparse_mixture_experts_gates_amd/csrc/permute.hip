@@ -17,6 +17,7 @@
 // in token order.  gather: one wave per kept row copies x[t] to x_perm[p].
 #include "common.h"
 #include "launch.h"
+#include "plan.h"
 
 namespace moe {
 
@@ -163,11 +164,14 @@ __global__ __launch_bounds__(1024) void permute_fused_kernel(
     const int32_t* __restrict__ idx, int n, int E, int64_t cap, int32_t* __restrict__ counts,
     int32_t* __restrict__ offsets, int32_t* __restrict__ perm_src,
     int32_t* __restrict__ slot_pos, int32_t* __restrict__ num_dropped,
-    int32_t* __restrict__ kept_total) {
+    int32_t* __restrict__ kept_total, PlanSpec ps, int want_plans) {
   __shared__ int run[FUSED_WAVES][256];
   __shared__ int sk[256];
   __shared__ int sdrop[256];
   __shared__ int soff[256];
+  __shared__ int prows[256];
+  __shared__ int pmt[256];
+  __shared__ int pbase[257];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int per = ((n + FUSED_WAVES * 64 - 1) / (FUSED_WAVES * 64)) * 64;  // slots per wave
   const int lo = w * per;
@@ -223,6 +227,12 @@ __global__ __launch_bounds__(1024) void permute_fused_kernel(
     kept_total[0] = sk[255];
   }
   __syncthreads();
+  if (want_plans) {
+    // the expert FFN's tile plans from the kept counts just formed
+    if (tid < E) prows[tid] = sk[tid] - soff[tid];
+    __syncthreads();
+    build_tile_plans(soff, prows, E, ps, pmt, pbase);
+  }
   const int total = sk[255];
   // pass 2: place every slot of this wave's run
   for (int st = 0; st < per; st += 64) {
@@ -268,14 +278,18 @@ __global__ __launch_bounds__(256) void gather_rows_kernel(
 
 int permute_nblocks(int64_t rows) { return (int)((rows + CH - 1) / CH); }
 
-hipError_t launch_permute(const PermuteArgs& a, hipStream_t s) {
+hipError_t launch_permute(const PermuteArgs& a, hipStream_t s, bool* plans_built) {
+  if (plans_built) *plans_built = false;
   const int64_t n = a.T * a.k;
   if (n == 0) return hipSuccess;
   if (n <= FUSED_MAX) {
     prof_before("permute", s);
+    const PlanSpec none{0, 0, 0, nullptr, nullptr};
     permute_fused_kernel<<<1, 1024, 0, s>>>(a.topk_idx, (int)n, a.E, a.capacity, a.counts,
                                             a.offsets, a.perm_src, a.slot_pos, a.num_dropped,
-                                            a.kept_total);
+                                            a.kept_total, a.plans ? *a.plans : none,
+                                            a.plans ? 1 : 0);
+    if (plans_built && a.plans) *plans_built = true;
     prof_after(s);
   } else {
   const int nb = permute_nblocks(n);
