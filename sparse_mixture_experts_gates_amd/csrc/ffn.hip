@@ -53,7 +53,14 @@ struct KArgs {
   int a_div;
   int K, N;
   int64_t a_seg_rows, c_seg_rows;  // extra row offset per segment (shared experts)
+  int split;                       // K halves (plan entries carry the half)
+  float* part;                     // split: fp32 partials [split][rows, N]
+  int64_t part_stride;             // rows * N
 };
+
+// A plan entry's column field: the column tile in the low 24 bits, the K
+// part of a split pass above them.
+constexpr int kNtBits = 24;
 
 // Plan: one workgroup; G <= 1024 segments (offsets seg[G+1], or G dense
 // segments of dense_rows rows).
@@ -130,9 +137,11 @@ __device__ __forceinline__ float act1(float v) {
 // so it fetches logical chunk (l%8) ^ (l/8) of its row -- full 128-byte lines
 // per 8 lanes.  Slab kt+NSTAGE-1 is requested while slab kt is multiplied;
 // one barrier per slab.
-template <int BM, int BN, int WM, int WN, int NSTAGE, int NSB, int MODE, bool PERSIST>
+template <int BM, int BN, int WM, int WN, int NSTAGE, int NSB, int MODE, bool PERSIST,
+          bool SPLIT = false>
 __global__ __launch_bounds__(64 * WM * WN)
 void ffn_bf16_kernel(KArgs a) {
+  static_assert(!SPLIT || (MODE == MODE_PLAIN && NSTAGE == 2), "split: plain-mode 256 x 256 only");
   constexpr int NW = WM * WN;
   constexpr int BMW = BM / WM, BNW = BN / WN;   // wave tile (tokens, weight rows)
   constexpr int TM = BMW / 16, TN = BNW / 16;
@@ -159,12 +168,23 @@ void ffn_bf16_kernel(KArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
   const int wm = wave / WN, wn = wave % WN;
   const int K = a.K, N = a.N;
+  // persistent: lane 0 claims the next entry of its own queue just before
+  // each epilogue, so the atomic's round trip hides behind the stores (a
+  // claim made earlier would hold an entry that an idle block could take)
+  const int xq = P & 7;
+  const int own0 = xcd_start(xq, V), own_len = xcd_start(xq + 1, V) - own0;
+  unsigned long long claimed = ~0ull;
   for (int it = 0;; ++it) {
   int e;
   if constexpr (PERSIST) {
-    // claimed when needed, not ahead: a claim held through a whole tile
-    // would keep that entry from an idle block at the end of the pass
-    if (tid == 0) tile_slot[it & 1] = next_tile(a.queues, V, P & 7);
+    if (tid == 0) {
+      int nxt = -1;
+      if (claimed != ~0ull) {
+        const unsigned f = (unsigned)claimed, b = (unsigned)(claimed >> 32);
+        if (f + b < (unsigned)own_len) nxt = own0 + (int)f;
+      }
+      tile_slot[it & 1] = nxt >= 0 ? nxt : next_tile(a.queues, V, xq);
+    }
     // also: every wave is done with the previous tile's LDS
     wait_vm_lgkm0<0>();
     ring_barrier();
@@ -179,7 +199,8 @@ void ffn_bf16_kernel(KArgs a) {
   int lane = tid & 63;
   asm volatile("" : "+v"(lane));
   const PlanEntry pe = a.plan[e];
-  const int n0 = pe.nt * BNOUT;
+  const int ks = SPLIT ? pe.nt >> kNtBits : 0;
+  const int n0 = (pe.nt & ((1 << kNtBits) - 1)) * BNOUT;
   const int64_t arow0 = (int64_t)pe.g * a.a_seg_rows;
   const int64_t wbase = (int64_t)pe.g * N * K;
 
@@ -205,10 +226,14 @@ void ffn_bf16_kernel(KArgs a) {
     return Wm + wbase + (int64_t)n * K;
   };
   // this lane's source (row, logical chunk) for each 8-row group the wave loads
+  // K slabs of this entry: all of them, or part ks of a split pass
+  const int nk_all = K / BK;
+  const int kb0 = SPLIT ? (int)((int64_t)nk_all * ks / a.split) : 0;
+  const int nk = SPLIT ? (int)((int64_t)nk_all * (ks + 1) / a.split) - kb0 : nk_all;
   const uint16_t* src[DPW];
 #pragma unroll
   for (int i = 0; i < DPW; ++i)
-    src[i] = row_ptr((wave + i * NW) * 8 + dma_row(lane)) + dma_chunk(lane) * 8;
+    src[i] = row_ptr((wave + i * NW) * 8 + dma_row(lane)) + dma_chunk(lane) * 8 + kb0 * BK;
 
   f32x4_t acc[TM][TN];
 #pragma unroll
@@ -216,7 +241,6 @@ void ffn_bf16_kernel(KArgs a) {
 #pragma unroll
     for (int j = 0; j < TN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  const int nk = K / BK;
   if constexpr (NSTAGE == 2) {
     // Software pipeline across slabs: the token slabs sit in a 2-stage ring,
     // the weight slabs in an NSB-stage ring (weights mostly come from HBM,
@@ -384,6 +408,7 @@ void ffn_bf16_kernel(KArgs a) {
   }
   }
   wait_vm_lgkm0<0>();   // the trailing reloads must land before the LDS is released
+  if (PERSIST && tid == 0) claimed = atomicAdd(a.queues + xq, 1ull);
 
   // epilogue: lane holds columns 4*(lane/16)+q of tile j, row lane%16 of
   // tile i.  N is a multiple of 64, so a 4-column group is either wholly in
@@ -407,6 +432,13 @@ void ffn_bf16_kernel(KArgs a) {
         col = n0 + wn * BNW + j * 16 + 4 * (lane >> 4);
 #pragma unroll
         for (int q = 0; q < 4; ++q) v[q] = act1<MODE>(acc[i][j][q]);
+      }
+      if constexpr (SPLIT) {
+        // split pass: the fp32 partial of part ks (added, then rounded, by
+        // whoever consumes the pass's output)
+        float* prow = a.part + ks * a.part_stride + (crow0 + r) * (int64_t)N;
+        if (row_ok && col < N) *reinterpret_cast<f32x4_t*>(prow + col) = f32x4_t{v[0], v[1], v[2], v[3]};
+        continue;
       }
       uint2 pk;
       pk.x = pack_bf16x2(v[0], v[1]);
@@ -434,7 +466,7 @@ __global__ __launch_bounds__(256) void ffn_f32_kernel(KArgs a) {
   const float* Wu = reinterpret_cast<const float*>(a.Wu);
   float* C = reinterpret_cast<float*>(a.C);
   const int K = a.K, N = a.N;
-  const int n0 = pe.nt * TB;
+  const int n0 = (pe.nt & ((1 << kNtBits) - 1)) * TB;
   const int64_t arow0 = (int64_t)pe.g * a.a_seg_rows;
   const int64_t wbase = (int64_t)pe.g * N * K;
   const int tid = threadIdx.x, tr = tid >> 4, tc = tid & 15;
@@ -557,13 +589,25 @@ int device_cus() {
 
 }  // namespace
 
-size_t ffn_plan_bytes(int64_t max_rows, int G, int N, bool small, int dtype) {
+size_t ffn_plan_bytes(int64_t max_rows, int G, int N, bool small, int dtype, int split) {
   size_t best = 0;
   for (int mode = 0; mode < 4; ++mode) {
-    const size_t b = kPlanHeader + 16 * (size_t)max_entries(max_rows, G, N, pick_shape(dtype, small, mode, max_rows, N));
+    const size_t b = kPlanHeader + 16 * (size_t)split *
+                     (size_t)max_entries(max_rows, G, N, pick_shape(dtype, small, mode, max_rows, N));
     if (b > best) best = b;
   }
   return (best + 255) / 256 * 256;
+}
+
+// Two K parts for a second expert GEMM (plain mode) that has fewer than
+// three rounds of 256 x 256 tiles and a long K: its few, long tiles would
+// otherwise leave most CUs idle in the last round.  The parts are added by
+// the consumer of the pass's output in a fixed order.
+int ffn_split(int64_t max_rows, int G, int N, int K, bool small, int dtype) {
+  if (dtype != MOE_BF16 || small) return 1;
+  const Shape sh = pick_shape(dtype, false, MODE_PLAIN, max_rows, N);
+  if (sh.id != 2 || K / BK < 64) return 1;
+  return max_entries(max_rows, G, N, sh) < 3 * kCUs ? 2 : 1;
 }
 
 namespace {
@@ -581,6 +625,7 @@ bool ffn_plan_spec(const FfnPassArgs& p1, const FfnPassArgs& p2, PlanSpec* ps) {
   ps->BM = sh1.BM;
   ps->NT = pass_nt(p1);
   ps->NT2 = pass_nt(p2);
+  ps->S2 = p2.split > 1 ? p2.split : 1;
   ps->plan = static_cast<int32_t*>(p1.plan);
   ps->plan2 = static_cast<int32_t*>(p2.plan);
   return true;
@@ -600,7 +645,9 @@ hipError_t launch_ffn_plans(const FfnPassArgs& p1, const FfnPassArgs& p2, hipStr
 
 hipError_t launch_ffn_pass(const FfnPassArgs& p, hipStream_t s) {
   const Shape sh = pick_shape(p.dtype, p.small, p.mode, p.max_rows, p.N);
-  const int64_t grid = max_entries(p.max_rows, p.G, p.N, sh);
+  const int split = p.split > 1 ? p.split : 1;
+  if (split > 1 && (sh.id != 2 || p.mode != MODE_PLAIN || !p.part)) return hipErrorInvalidValue;
+  const int64_t grid = max_entries(p.max_rows, p.G, p.N, sh) * split;
   if (grid == 0) return hipSuccess;
   int32_t* count = static_cast<int32_t*>(p.plan);
   PlanEntry* plan = reinterpret_cast<PlanEntry*>(static_cast<char*>(p.plan) + kPlanHeader);
@@ -618,6 +665,9 @@ hipError_t launch_ffn_pass(const FfnPassArgs& p, hipStream_t s) {
   k.N = p.N;
   k.a_seg_rows = p.a_seg_rows;
   k.c_seg_rows = p.c_seg_rows;
+  k.split = split;
+  k.part = p.part;
+  k.part_stride = p.max_rows * (int64_t)p.N;
   const char* nm = p.seg_offsets ? (p.mode == MODE_PLAIN ? "ffn2" : "ffn1")
                                  : (p.mode == MODE_PLAIN ? "ffn2_shared" : "ffn1_shared");
   prof_before(nm, s);
@@ -645,12 +695,47 @@ hipError_t launch_ffn_pass(const FfnPassArgs& p, hipStream_t s) {
     const int cus = device_cus();
     if (grid >= 2 * (int64_t)cus) {
       if (sh.id == 3) launch_bf16<256, 128, 4, 2, 3, 3, true>(p.mode, (unsigned)cus, k, s);
+      else if (split > 1)
+        ffn_bf16_kernel<256, 256, 2, 4, 2, 2, MODE_PLAIN, true, true><<<(unsigned)cus, 512, 0, s>>>(k);
       else launch_bf16<256, 256, 2, 4, 2, 2, true>(p.mode, (unsigned)cus, k, s);
     } else {
       if (sh.id == 3) launch_bf16<256, 128, 4, 2, 3, 3, false>(p.mode, (unsigned)grid, k, s);
+      else if (split > 1)
+        ffn_bf16_kernel<256, 256, 2, 4, 2, 2, MODE_PLAIN, false, true><<<(unsigned)grid, 512, 0, s>>>(k);
       else launch_bf16<256, 256, 2, 4, 2, 2, false>(p.mode, (unsigned)grid, k, s);
     }
   }
+  prof_after(s);
+  return hipGetLastError();
+}
+
+namespace {
+// C = bf16(part 0 + part 1), eight columns per thread.
+__global__ __launch_bounds__(256) void split_reduce_kernel(const float* __restrict__ part,
+                                                           int64_t stride, uint16_t* __restrict__ C,
+                                                           int64_t n8) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n8) return;
+  const f32x4_t* p0 = reinterpret_cast<const f32x4_t*>(part) + 2 * i;
+  const f32x4_t* p1 = reinterpret_cast<const f32x4_t*>(part + stride) + 2 * i;
+  const f32x4_t a0 = p0[0], a1 = p0[1], b0 = p1[0], b1 = p1[1];
+  u32x4_t o;
+  o[0] = pack_bf16x2(a0[0] + b0[0], a0[1] + b0[1]);
+  o[1] = pack_bf16x2(a0[2] + b0[2], a0[3] + b0[3]);
+  o[2] = pack_bf16x2(a1[0] + b1[0], a1[1] + b1[1]);
+  o[3] = pack_bf16x2(a1[2] + b1[2], a1[3] + b1[3]);
+  reinterpret_cast<u32x4_t*>(C)[i] = o;
+}
+}  // namespace
+
+hipError_t launch_ffn_split_reduce(const FfnPassArgs& p, hipStream_t s) {
+  if (p.split <= 1) return hipSuccess;
+  if (p.split != 2) return hipErrorInvalidValue;
+  const int64_t n8 = p.max_rows * (int64_t)p.N / 8;
+  if (n8 == 0) return hipSuccess;
+  prof_before("ffn2_split_reduce", s);
+  split_reduce_kernel<<<(unsigned)((n8 + 255) / 256), 256, 0, s>>>(
+      p.part, p.max_rows * (int64_t)p.N, static_cast<uint16_t*>(p.C), n8);
   prof_after(s);
   return hipGetLastError();
 }

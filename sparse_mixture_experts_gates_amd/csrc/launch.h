@@ -32,6 +32,7 @@ hipError_t launch_route(const RouteArgs& a, hipStream_t s);
 // buffers (header + entries).
 struct PlanSpec {
   int BM, NT, NT2;
+  int S2;                   // K parts of the second pass (1 = not split)
   int32_t* plan;
   int32_t* plan2;
 };
@@ -77,8 +78,14 @@ struct FfnPassArgs {
   void* plan;             // workspace for the tile plan
   int64_t max_rows;       // upper bound of rows over all segments (host)
   bool small;             // small-batch (decode) tile shape
+  int split;              // K parts (second GEMM only; 1 = none)
+  float* part;            // split: fp32 partials [split][max_rows, N]
 };
-size_t ffn_plan_bytes(int64_t max_rows, int G, int N, bool small, int dtype);
+size_t ffn_plan_bytes(int64_t max_rows, int G, int N, bool small, int dtype, int split = 1);
+// K parts (1 or 2) of a routed second GEMM pass of this shape.
+int ffn_split(int64_t max_rows, int G, int N, int K, bool small, int dtype);
+// For a split pass: C = bf16(sum of the fp32 parts) for all max_rows rows.
+hipError_t launch_ffn_split_reduce(const FfnPassArgs& p, hipStream_t s);
 // The plan layout of the two passes of one expert FFN; false if there is
 // nothing to plan (no rows).
 bool ffn_plan_spec(const FfnPassArgs& p1, const FfnPassArgs& p2, PlanSpec* ps);
@@ -115,6 +122,10 @@ struct CombineArgs {
   void* y;                  // [T, d]
   int64_t T;
   int k, d, S, dtype;
+  // bf16 only: the expert outputs as two fp32 K parts of a split GEMM
+  // ([2][T*k, d], stride part_stride); expert_out is then unused
+  const float* part;
+  int64_t part_stride;
 };
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
 

@@ -109,7 +109,8 @@ PermWs perm_ws(const moe_config_t* c, int64_t T) {
 }
 
 struct FfnWs {
-  size_t H, Hs, plan1, plan2, plan3, plan4, total;
+  size_t H, Hs, plan1, plan2, plan3, plan4, part, total;
+  int split;   // K parts of the routed second GEMM
 };
 FfnWs ffn_ws(const moe_config_t* c, int64_t T) {
   FfnWs w;
@@ -120,10 +121,13 @@ FfnWs ffn_ws(const moe_config_t* c, int64_t T) {
   o += up((size_t)R * c->d_ff * esize(c));
   w.Hs = o;
   o += up((size_t)S * T * (S ? c->d_ff_shared : 0) * esize(c));
+  w.split = ffn_split(R, c->num_experts, c->d, c->d_ff, small_batch(R), c->dtype);
   w.plan1 = o;
   o += ffn_plan_bytes(R, c->num_experts, c->d_ff, small_batch(R), c->dtype);
   w.plan2 = o;
-  o += ffn_plan_bytes(R, c->num_experts, c->d, small_batch(R), c->dtype);
+  o += ffn_plan_bytes(R, c->num_experts, c->d, small_batch(R), c->dtype, w.split);
+  w.part = o;
+  if (w.split > 1) o += up((size_t)w.split * R * c->d * 4);
   w.plan3 = w.plan4 = o;
   if (S) {
     o += ffn_plan_bytes((int64_t)S * T, S, c->d_ff_shared, small_batch(T), c->dtype);
@@ -242,6 +246,8 @@ FfnPasses ffn_passes(const moe_config_t* c, int64_t T, const void* x, const void
   p2.N = c->d;
   p2.mode = 0;
   p2.plan = at(ws, w.plan2);
+  p2.split = w.split;
+  p2.part = w.split > 1 ? reinterpret_cast<float*>(at(ws, w.part)) : nullptr;
   f.shared = c->num_shared > 0;
   if (f.shared) {
     const int S = c->num_shared;
@@ -273,6 +279,8 @@ FfnPasses ffn_passes(const moe_config_t* c, int64_t T, const void* x, const void
     q2.mode = 0;
     q2.a_seg_rows = T;
     q2.plan = at(ws, w.plan4);
+    q2.split = 1;
+    q2.part = nullptr;
   }
   return f;
 }
@@ -290,20 +298,24 @@ moe_status_t run_ffn(const FfnPasses& f, bool routed_plans_built, hipStream_t s)
   return MOE_OK;
 }
 
+// The stepwise entry point: expert_out in bf16 (a split second GEMM's parts
+// are added and rounded here; moe_forward lets the combine do it).
 moe_status_t do_ffn(const moe_config_t* c, int64_t T, const void* x, const void* x_perm,
                     const int32_t* perm_src, const int32_t* offsets, const void* w1,
                     const void* w3, const void* w2, const void* ws1, const void* ws3,
                     const void* ws2, void* eout, void* sout, void* ws, hipStream_t s) {
-  return run_ffn(ffn_passes(c, T, x, x_perm, perm_src, offsets, w1, w3, w2, ws1, ws3, ws2, eout,
-                            sout, ws),
-                 false, s);
+  const FfnPasses f =
+      ffn_passes(c, T, x, x_perm, perm_src, offsets, w1, w3, w2, ws1, ws3, ws2, eout, sout, ws);
+  const moe_status_t st = run_ffn(f, false, s);
+  if (st != MOE_OK) return st;
+  return hip_status(launch_ffn_split_reduce(f.p2, s));
 }
 
 moe_status_t do_combine(const moe_config_t* c, int64_t T, const void* eout,
                         const int32_t* slot_pos, const float* gate, const void* sout, void* y,
-                        hipStream_t s) {
+                        hipStream_t s, const float* part = nullptr, int64_t part_stride = 0) {
   CombineArgs a{eout, slot_pos, gate, sout, y, T, c->top_k, c->d,
-                sout ? c->num_shared : 0, c->dtype};
+                sout ? c->num_shared : 0, c->dtype, part, part_stride};
   return hip_status(launch_combine(a, s));
 }
 
@@ -459,6 +471,9 @@ moe_status_t moe_forward(const moe_config_t* cfg, int64_t T, const void* x, cons
   if (st != MOE_OK) return st;
   st = run_ffn(passes, built, s);
   if (st != MOE_OK) return st;
+  if (passes.p2.split > 1)   // the combine adds the second GEMM's K parts
+    return do_combine(cfg, T, eout, slot_pos, gate, sout, y, s, passes.p2.part,
+                      passes.p2.max_rows * (int64_t)passes.p2.N);
   return do_combine(cfg, T, eout, slot_pos, gate, sout, y, s);
 }
 

@@ -284,7 +284,7 @@ hipError_t launch_permute(const PermuteArgs& a, hipStream_t s, bool* plans_built
   if (n == 0) return hipSuccess;
   if (n <= FUSED_MAX) {
     prof_before("permute", s);
-    const PlanSpec none{0, 0, 0, nullptr, nullptr};
+    const PlanSpec none{0, 0, 0, 1, nullptr, nullptr};
     permute_fused_kernel<<<1, 1024, 0, s>>>(a.topk_idx, (int)n, a.E, a.capacity, a.counts,
                                             a.offsets, a.perm_src, a.slot_pos, a.num_dropped,
                                             a.kept_total, a.plans ? *a.plans : none,

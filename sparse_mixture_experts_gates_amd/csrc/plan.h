@@ -41,7 +41,10 @@ __device__ inline void build_tile_plans(const int* start, const int* rows, int G
   __syncthreads();
   const int MT = base[G];   // row tiles over all segments
   for (int pass = 0; pass < 2; ++pass) {
-    const int nt_all = pass == 0 ? ps.NT : ps.NT2;
+    // a split pass (K in S parts) lists every row tile once per part:
+    // segment, column tile, part, row tile
+    const int S = pass == 0 ? 1 : (ps.S2 > 1 ? ps.S2 : 1);
+    const int nt_all = (pass == 0 ? ps.NT : ps.NT2) * S;
     int32_t* count = pass == 0 ? ps.plan : ps.plan2;
     if (nt_all <= 0) break;
     PlanEntry* out = reinterpret_cast<PlanEntry*>(reinterpret_cast<char*>(count) + kPlanHeader);
@@ -53,11 +56,12 @@ __device__ inline void build_tile_plans(const int* start, const int* rows, int G
         if (base[mid] * nt_all <= L) lo = mid; else hi = mid - 1;
       }
       const int g = lo, rem = L - base[g] * nt_all, m = mt[g];
-      const int nt = rem / m, mi = rem - nt * m;
+      const int c = rem / m, mi = rem - c * m;
+      const int nt = c / S, part = c - nt * S;
       const int m0 = start[g] + mi * BM;
       int m1 = m0 + BM;
       if (m1 > start[g] + rows[g]) m1 = start[g] + rows[g];
-      out[L] = PlanEntry{g, m0, m1, nt};
+      out[L] = PlanEntry{g, m0, m1, nt | (part << 24)};
     }
     if (tid == 0) count[0] = V;
     if (tid < 16) count[kPlanHeads + tid] = 0;   // queue words

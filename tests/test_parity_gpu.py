@@ -100,6 +100,23 @@ EDGES = {
 }
 
 
+# Larger shapes checked on a seeded token sample: a second GEMM with fewer
+# than three rounds of 256 x 256 tiles and K = 4096 runs split over K, its
+# parts added by the combine (moe_forward) or by a reduce (moe_expert_ffn).
+SAMPLED_EDGES = {
+    "split_k_second_gemm": small(T=4096, d=4096, E=8, k=2, d_ff=4096),
+}
+
+
+@pytest.mark.parametrize("name", list(SAMPLED_EDGES))
+def test_sampled_edge_case(name):
+    w = SAMPLED_EDGES[name]
+    say(f"[edge-sampled] {name}")
+    rep = MC.check_layer(w, seed_tokens=(11, 64))
+    say(f"[edge-sampled] {name} ok {json.dumps(rep)}")
+    torch.cuda.empty_cache()
+
+
 @pytest.mark.parametrize("name", list(EDGES))
 def test_edge_case(name):
     w = EDGES[name]
