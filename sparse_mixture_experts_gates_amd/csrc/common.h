@@ -72,6 +72,11 @@ __device__ __forceinline__ void wait_vm_lgkm0() {
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | ((N >> 4) << 14));
 }
 
+// s_waitcnt lgkmcnt(0) only (vmcnt 63 = no wait on vector memory).
+__device__ __forceinline__ void wait_lgkm0() {
+  __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (3 << 14));
+}
+
 // One direct-to-LDS load of 8 whole slab rows (1 KB): lane l writes LDS bytes
 // 16*l (row l/8, stored chunk l%8), so it must fetch logical chunk
 // (l%8) ^ (l/8) of its row; 8 lanes cover one full 128-byte line.

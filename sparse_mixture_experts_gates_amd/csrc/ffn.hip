@@ -185,8 +185,10 @@ void ffn_bf16_kernel(KArgs a) {
       }
       tile_slot[it & 1] = nxt >= 0 ? nxt : next_tile(a.queues, V, xq);
     }
-    // also: every wave is done with the previous tile's LDS
-    wait_vm_lgkm0<0>();
+    // also: every wave is done with the previous tile's LDS (its loads have
+    // landed before the epilogue; its stores need not wait: outstanding
+    // stores only make the next prologue's vmcnt wait longer)
+    wait_lgkm0();
     ring_barrier();
     e = __builtin_amdgcn_readfirstlane(tile_slot[it & 1]);
     if (e < 0) break;
@@ -204,15 +206,41 @@ void ffn_bf16_kernel(KArgs a) {
   const int64_t arow0 = (int64_t)pe.g * a.a_seg_rows;
   const int64_t wbase = (int64_t)pe.g * N * K;
 
-  // slab row `row` (tokens first, then weight rows) -> its global row start
-  auto row_ptr = [&](int row) -> const uint16_t* {
-    if (row < BM) {
-      int r = pe.m0 + row;
-      if (r > pe.m1 - 1) r = pe.m1 - 1;
-      const int64_t sr = a.a_rows ? (int64_t)(a.a_rows[r] / a.a_div) : arow0 + r;
-      return a.A + sr * K;
+  // K slabs of this entry: all of them, or part ks of a split pass
+  const int nk_all = K / BK;
+  const int kb0 = SPLIT ? (int)((int64_t)nk_all * ks / a.split) : 0;
+  const int nk = SPLIT ? (int)((int64_t)nk_all * (ks + 1) / a.split) - kb0 : nk_all;
+  // this lane's source (row, logical chunk) for each 8-row group the wave
+  // loads: token groups first (rows past the segment end clamped to its last
+  // row), then weight groups
+  constexpr int DPA0 = BM / 8 / NW;
+  static_assert((BM / 8) % NW == 0, "token load groups must divide over the waves");
+  const uint16_t* src[DPW];
+  {
+    int rr[DPA0];
+#pragma unroll
+    for (int i = 0; i < DPA0; ++i) {
+      const int r = pe.m0 + (wave + i * NW) * 8 + dma_row(lane);
+      rr[i] = r > pe.m1 - 1 ? pe.m1 - 1 : r;
     }
-    const int rho = row - BM;
+    int64_t sr[DPA0];
+    if (a.a_rows) {
+      // gathered rows: every index load in flight before the first use
+      int v[DPA0];
+#pragma unroll
+      for (int i = 0; i < DPA0; ++i) v[i] = a.a_rows[rr[i]];
+#pragma unroll
+      for (int i = 0; i < DPA0; ++i) sr[i] = v[i] / a.a_div;
+    } else {
+#pragma unroll
+      for (int i = 0; i < DPA0; ++i) sr[i] = arow0 + rr[i];
+    }
+#pragma unroll
+    for (int i = 0; i < DPA0; ++i) src[i] = a.A + sr[i] * K + dma_chunk(lane) * 8 + kb0 * BK;
+  }
+#pragma unroll
+  for (int i = DPA0; i < DPW; ++i) {
+    const int rho = (wave + i * NW) * 8 + dma_row(lane) - BM;
     int n;
     const uint16_t* Wm = a.W;
     if (MODE == MODE_SWIGLU) {
@@ -223,17 +251,8 @@ void ffn_bf16_kernel(KArgs a) {
       n = n0 + rho;
     }
     if (n > N - 1) n = N - 1;
-    return Wm + wbase + (int64_t)n * K;
-  };
-  // this lane's source (row, logical chunk) for each 8-row group the wave loads
-  // K slabs of this entry: all of them, or part ks of a split pass
-  const int nk_all = K / BK;
-  const int kb0 = SPLIT ? (int)((int64_t)nk_all * ks / a.split) : 0;
-  const int nk = SPLIT ? (int)((int64_t)nk_all * (ks + 1) / a.split) - kb0 : nk_all;
-  const uint16_t* src[DPW];
-#pragma unroll
-  for (int i = 0; i < DPW; ++i)
-    src[i] = row_ptr((wave + i * NW) * 8 + dma_row(lane)) + dma_chunk(lane) * 8 + kb0 * BK;
+    src[i] = Wm + wbase + (int64_t)n * K + dma_chunk(lane) * 8 + kb0 * BK;
+  }
 
   f32x4_t acc[TM][TN];
 #pragma unroll
