@@ -72,7 +72,7 @@ def topk_by_selection(q, k):
 
 
 def forward(x, w_r, w1, w2, w3=None, *, k, act, gating="softmax_topk",
-            capacity_factor=0.0, logit_offset=None, select_bias=None,
+            capacity_factor=0.0, capacity_priority="token", logit_offset=None, select_bias=None,
             shared=None, counter=None):
     """Returns (y, topk_idx, gates, kept) as nested Python lists."""
     T, E = len(x), len(w_r)
@@ -98,19 +98,22 @@ def forward(x, w_r, w1, w2, w3=None, *, k, act, gating="softmax_topk",
             g = [math.exp(s[e] - m) / z for e in sel]
         idx_all.append(sel)
         g_all.append(g)
-    # capacity: first C tokens (in token order) per expert are kept
+    # capacity: the first C slots per expert are kept, visiting the slots
+    # token by token, or (slot-major priority) every token's first choice,
+    # then every token's second choice, ...
     cap = None
     if capacity_factor > 0.0:
         cap = math.floor(capacity_factor * k * T / E)
     seen = [0] * E
-    kept = []
-    for t in range(T):
-        row = []
-        for j in range(k):
-            e = idx_all[t][j]
-            row.append(cap is None or seen[e] < cap)
-            seen[e] += 1
-        kept.append(row)
+    kept = [[False] * k for _ in range(T)]
+    if capacity_priority == "slot":
+        visits = [(t, j) for j in range(k) for t in range(T)]
+    else:
+        visits = [(t, j) for t in range(T) for j in range(k)]
+    for t, j in visits:
+        e = idx_all[t][j]
+        kept[t][j] = cap is None or seen[e] < cap
+        seen[e] += 1
     d = len(x[0])
     y = []
     for t in range(T):

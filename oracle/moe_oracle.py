@@ -28,7 +28,8 @@ Steps (sources in the package docstring):
       [LLM-T11 §Expert capacity and dropped tokens; LLM-T11 Exercise 4;
        ITM-14 §Auxiliary loss]
  O6 ``permute``         per-expert counts, kept = min(count, C), stable order
-      (expert ascending, token ascending), drop mask, drop count
+      (expert ascending, then token ascending -- or, with slot-major
+      priority, slot then token), drop mask, drop count
       [LLM-T11 Exercise 4; LM-33 §Simple MoE Layer Implementation]
  O7 ``expert_ffn``      ReLU / GeLU(erf) MLP or SwiGLU gated MLP, no biases
       [LLM-T11 §The mathematics; LLM-T11 §Modern MoE variants (SwiGLU
@@ -186,21 +187,35 @@ class Permutation:
     num_dropped: int
 
 
-def permute(topk_idx, E, C):
+PRIORITIES = ("token", "slot")
+
+
+def priority_order(T, k, priority="token"):
+    """The order in which slots claim expert capacity: token-major (every slot
+    of token 0, then of token 1, ...) or slot-major (every token's first
+    choice, then every token's second choice, ...; GShard-style priority, a
+    NEXT routing variant), as flat slot indices t*k + j."""
+    if priority == "slot":
+        return [t * k + j for j in range(k) for t in range(T)]
+    return list(range(T * k))
+
+
+def permute(topk_idx, E, C, priority="token"):
     """Group kept slots by expert.
 
-    Rows of expert e are its kept slots in ascending token order, and experts
-    follow in ascending order.  A slot is kept iff fewer than C earlier tokens
-    were already sent to the same expert (reading: "the excess is dropped"
-    [LLM-T11 §Expert capacity and dropped tokens] keeps the first C in token
-    order).  num_dropped = sum_e max(0, count_e - C) [LLM-T11 Exercise 4].
+    A slot is kept iff fewer than C slots that come before it in the priority
+    order were already sent to the same expert (reading: "the excess is
+    dropped" [LLM-T11 §Expert capacity and dropped tokens] keeps the first C;
+    the default order is ascending token).  Rows of expert e are its kept
+    slots in that same order, and experts follow in ascending order.
+    num_dropped = sum_e max(0, count_e - C) [LLM-T11 Exercise 4].
     """
     topk_idx = np.asarray(topk_idx)
     T, k = topk_idx.shape
     flat = topk_idx.reshape(-1)
     counts = np.zeros(E, dtype=np.int64)
     rank = np.zeros(T * k, dtype=np.int64)
-    for a in range(T * k):                 # ascending token, then slot
+    for a in priority_order(T, k, priority):
         e = int(flat[a])
         rank[a] = counts[e]
         counts[e] += 1
@@ -313,7 +328,7 @@ class Result:
 
 def forward(x, w_router, w1, w2, w3=None, *, k, act, gating="softmax_topk",
             capacity_factor=0.0, logit_offset=None, select_bias=None,
-            shared=None):
+            shared=None, capacity_priority="token"):
     """The forward pass O1..O8 over all T tokens, float64 throughout."""
     x = np.asarray(x, dtype=np.float64)
     T = x.shape[0]
@@ -323,7 +338,7 @@ def forward(x, w_router, w1, w2, w3=None, *, k, act, gating="softmax_topk",
     idx = ordered_topk(q, k)
     g = gate_values(s, idx, gating)
     C = capacity(capacity_factor, k, T, E)
-    perm = permute(idx, E, C)
+    perm = permute(idx, E, C, capacity_priority)
     kept = (perm.slot_pos >= 0).reshape(T, k)
     y = combine(x, idx, g, kept, w1, w2, w3, act, shared)
     return Result(s, q, idx, g, C, perm, y)
@@ -362,7 +377,7 @@ def near_tie_tokens(keys, k, eps=NEAR_TIE_EPS):
 
 
 def route_from_logits(logits_f32, *, k, gating, capacity_factor=0.0,
-                      select_bias=None):
+                      select_bias=None, capacity_priority="token"):
     """O2..O6 starting from given float32 scores: keys in float32, top-k,
     float64 gates, capacity and permutation.  Returns a dict."""
     s32 = np.asarray(logits_f32, dtype=np.float32)
@@ -371,7 +386,7 @@ def route_from_logits(logits_f32, *, k, gating, capacity_factor=0.0,
     idx = ordered_topk(q, k)
     g = gate_values(s32.astype(np.float64), idx, gating)
     C = capacity(capacity_factor, k, T, E)
-    perm = permute(idx, E, C)
+    perm = permute(idx, E, C, capacity_priority)
     return dict(keys=q, topk_idx=idx, gates=g, capacity=C, perm=perm,
                 near_tie=near_tie_tokens(q, k))
 

@@ -34,12 +34,15 @@ def _battery():
     P.test_balance_loss_lower_for_balanced_than_collapsed_routing()
     P.test_routing_stats_invariants_and_brute_force()
     P.test_bias_update_hand_worked()
+    P.test_slot_priority_matches_brute_force()
+    P.test_slot_priority_hand_worked()
+    P.test_slot_priority_invariants()
 
 
 _orig = {n: getattr(O, n) for n in (
     "sigmoid", "ordered_topk", "gate_values", "capacity", "permute",
     "expert_ffn", "combine", "router_logits", "selection_keys", "gelu",
-    "routing_stats", "softmax_probs")}
+    "routing_stats", "softmax_probs", "priority_order")}
 
 
 def m_sigmoid_sign(z):
@@ -162,7 +165,19 @@ def m_probs_kept_only(s):
     return z / z.sum(axis=-1, keepdims=True)
 
 
+def m_priority_ignored(T, k, priority="token"):
+    return _orig["priority_order"](T, k, "token")
+
+
+def m_priority_slot_tokens_reversed(T, k, priority="token"):
+    if priority == "slot":
+        return [t * k + j for j in range(k) for t in reversed(range(T))]
+    return _orig["priority_order"](T, k, priority)
+
+
 MUTANTS = {
+    "slot_priority_ignored": ("priority_order", m_priority_ignored),
+    "slot_priority_tokens_reversed": ("priority_order", m_priority_slot_tokens_reversed),
     "balance_loss_without_n": ("routing_stats", m_stats_no_n),
     "bias_update_sign_flipped": ("routing_stats", m_stats_bias_sign),
     "bias_moves_at_mean_load": ("routing_stats", m_stats_bias_ge),

@@ -498,3 +498,57 @@ def test_bias_update_hand_worked():
     assert r["bias"].tolist() == [0.375, 0.0, -0.125, 1.0]
     # drop rate: 3 of the 12 assignments dropped [LLM-T11 Exercise 4]
     assert O.routing_stats(s, np.array([5, 3, 1, 3]), k=2, num_dropped=3)["drop_rate"] == 0.25
+
+
+# ------------------------------------------------ slot-major capacity priority
+# A NEXT routing variant: every token's first choice claims capacity before
+# any second choice (GShard-style priority).  The pages name capacity and
+# drops [LLM-T11 §Expert capacity and dropped tokens] but not this order.
+
+def test_slot_priority_matches_brute_force():
+    rng = np.random.default_rng(77)
+    T, d, E, d_ff = 10, 6, 4, 5
+    for k in (2, 3):
+        for rho in (0.5, 0.8, 1.0):
+            x, wr, w1, w2, w3, sh = rand_layer(rng, T, d, E, d_ff, "relu", shared=0)
+            ref = O.forward(x, wr, w1, w2, w3, k=k, act="relu", capacity_factor=rho,
+                            capacity_priority="slot")
+            y, idx, g, kept = brute.forward(tolist(x), tolist(wr), tolist(w1), tolist(w2),
+                                            None, k=k, act="relu", capacity_factor=rho,
+                                            capacity_priority="slot")
+            assert ((ref.perm.slot_pos.reshape(T, k) >= 0) == np.array(kept)).all()
+            np.testing.assert_allclose(ref.y, np.array(y), rtol=0, atol=1e-12)
+
+
+def test_slot_priority_hand_worked():
+    # E = 2, C = 2; token 0 prefers expert 1, tokens 1 and 2 prefer expert 0.
+    # Token order keeps (t0: both, t1: both) and drops all of token 2;
+    # slot-major keeps every first choice and drops the second choices of
+    # tokens 0 and 2.
+    idx = np.array([[1, 0], [0, 1], [0, 1]])
+    tok = O.permute(idx, 2, 2, "token")
+    slot = O.permute(idx, 2, 2, "slot")
+    assert (tok.slot_pos.reshape(3, 2) >= 0).tolist() == [[True, True], [True, True], [False, False]]
+    assert (slot.slot_pos.reshape(3, 2) >= 0).tolist() == [[True, False], [True, True], [True, False]]
+    # same counts and drops, rows of each expert in priority order
+    assert tok.counts.tolist() == slot.counts.tolist() == [3, 3]
+    assert tok.num_dropped == slot.num_dropped == 2
+    assert slot.perm_src.tolist()[:4] == [2, 4, 0, 3]    # e0: t1.j0, t2.j0; e1: t0.j0, t1.j1
+
+
+def test_slot_priority_invariants():
+    rng = np.random.default_rng(3)
+    for _ in range(30):
+        T, E = int(rng.integers(1, 40)), int(rng.integers(2, 9))
+        k = int(rng.integers(1, E + 1))
+        idx = O.ordered_topk(rng.normal(size=(T, E)), k)
+        C = int(rng.integers(0, T + 1))
+        tok, slot = O.permute(idx, E, C, "token"), O.permute(idx, E, C, "slot")
+        # kept per expert is min(count, C) either way
+        assert (tok.offsets == slot.offsets).all() and tok.num_dropped == slot.num_dropped
+        if k == 1:   # one slot per token: the two orders coincide
+            assert (tok.slot_pos == slot.slot_pos).all() and (tok.perm_src == slot.perm_src).all()
+        # an expert with at most C first choices keeps all of them
+        first = np.bincount(idx[:, 0], minlength=E)
+        ok = first[idx[:, 0]] <= C
+        assert (slot.slot_pos.reshape(T, k)[ok, 0] >= 0).all()
