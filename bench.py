@@ -116,7 +116,7 @@ def cpu_baseline(w, inp, flops_per_token, budget_s=15.0):
         t0 = time.perf_counter()
         O.forward(x[:n], wr, w1, w2, w3, k=w.k, act=w.act, gating=w.gating,
                   capacity_factor=float(np.float32(w.capacity_factor)), logit_offset=off,
-                  select_bias=bias, shared=sh)
+                  select_bias=bias, shared=sh, capacity_priority=w.capacity_priority)
         return time.perf_counter() - t0
 
     n = min(w.T, 64)

@@ -77,6 +77,19 @@ extern "C" {
 #define MOE_GATE_SIGMOID_TOPK 1
 #define MOE_GATE_SOFTMAX_FULL 2
 
+/* which slots claim expert capacity first (cfg->capacity_priority)
+ *  TOKEN : ascending token, a token's slots in choice order -- the first C
+ *          assignments of each expert are kept ("Mixture of Experts", LLM
+ *          tutorial ch. 11, "Expert capacity and dropped tokens": the excess
+ *          is dropped).
+ *  SLOT  : every token's first choice (ascending token), then every token's
+ *          second choice, ...: a token loses its first choice only if C
+ *          other first choices precede it (GShard-style priority).
+ * Each expert's rows in expert_offsets / perm_src follow the same order.
+ * Without a capacity limit nothing is dropped and only the row order differs. */
+#define MOE_PRIORITY_TOKEN 0
+#define MOE_PRIORITY_SLOT  1
+
 typedef enum {
   MOE_OK = 0,
   MOE_ERR_INVALID_ARG = 1,  /* null required pointer, misaligned pointer,
@@ -94,7 +107,7 @@ typedef enum {
  * num_shared > 0) positive multiples of 64 for bf16, of 4 for fp32;
  * num_shared in [0, 8], shared experts are SwiGLU and need dtype bf16 or fp32
  * like the rest.  Enum fields are int32 so the struct has one layout in every
- * language (40 bytes, no padding). */
+ * language (44 bytes, no padding). */
 typedef struct moe_config {
   int32_t d;                /* model width                                  */
   int32_t num_experts;      /* E, routed experts                            */
@@ -106,6 +119,7 @@ typedef struct moe_config {
   float   capacity_factor;  /* rho; <= 0 means no capacity limit            */
   int32_t num_shared;       /* always-on shared SwiGLU experts (0 = none)   */
   int32_t d_ff_shared;      /* their hidden width                           */
+  int32_t capacity_priority;  /* MOE_PRIORITY_*                             */
 } moe_config_t;
 
 /* Human-readable name of a status code (static storage; never NULL). */

@@ -21,6 +21,7 @@ LIB_PATH = os.environ.get("MOE_MI355X_LIB") or os.path.join(_HERE, "libmoe_mi355
 MOE_F32, MOE_BF16 = 0, 1
 ACTS = {"relu": 0, "gelu": 1, "swiglu": 2}
 GATINGS = {"softmax_topk": 0, "sigmoid_topk": 1, "softmax_full": 2}
+PRIORITIES = {"token": 0, "slot": 1}
 DECODE_MAX_ROWS = 64
 STATUS = {0: "MOE_OK", 1: "MOE_ERR_INVALID_ARG", 2: "MOE_ERR_UNSUPPORTED",
           3: "MOE_ERR_WORKSPACE", 4: "MOE_ERR_HIP"}
@@ -41,7 +42,8 @@ class MoeConfig(ctypes.Structure):
                 ("top_k", ctypes.c_int32), ("d_ff", ctypes.c_int32),
                 ("act", ctypes.c_int32), ("gating", ctypes.c_int32),
                 ("dtype", ctypes.c_int32), ("capacity_factor", ctypes.c_float),
-                ("num_shared", ctypes.c_int32), ("d_ff_shared", ctypes.c_int32)]
+                ("num_shared", ctypes.c_int32), ("d_ff_shared", ctypes.c_int32),
+                ("capacity_priority", ctypes.c_int32)]
 
 
 _lib_handle = None
@@ -84,16 +86,17 @@ def lib():
 
 
 def config(d, num_experts, top_k, d_ff, act="swiglu", gating="softmax_topk",
-           dtype="bf16", capacity_factor=0.0, num_shared=0, d_ff_shared=0):
+           dtype="bf16", capacity_factor=0.0, num_shared=0, d_ff_shared=0,
+           capacity_priority="token"):
     return MoeConfig(d, num_experts, top_k, d_ff, ACTS[act], GATINGS[gating],
                      MOE_BF16 if dtype == "bf16" else MOE_F32, float(capacity_factor),
-                     num_shared, d_ff_shared)
+                     num_shared, d_ff_shared, PRIORITIES[capacity_priority])
 
 
 def config_for(w, T=None):
     """MoeConfig of a workloads.Workload."""
     return config(w.d, w.E, w.k, w.d_ff, w.act, w.gating, w.dtype, w.capacity_factor,
-                  w.num_shared, w.d_ff_shared)
+                  w.num_shared, w.d_ff_shared, w.capacity_priority)
 
 
 def _check(st, where):

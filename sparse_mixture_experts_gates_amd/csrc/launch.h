@@ -51,6 +51,7 @@ struct PermuteArgs {
   int64_t T;
   int k, E, d, dtype;
   int64_t capacity;         // < 0: unlimited
+  int slot_major;           // capacity and row order by slot, then token
   const PlanSpec* plans;    // optional: the routed experts' GEMM plans, built
                             // here when the one-workgroup path runs
 };

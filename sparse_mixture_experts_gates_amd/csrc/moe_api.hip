@@ -76,6 +76,8 @@ moe_status_t check_cfg(const moe_config_t* c, int64_t T) {
     return MOE_ERR_INVALID_ARG;
   if (c->dtype != MOE_F32 && c->dtype != MOE_BF16) return MOE_ERR_INVALID_ARG;
   if (isnan(c->capacity_factor)) return MOE_ERR_INVALID_ARG;
+  if (c->capacity_priority != MOE_PRIORITY_TOKEN && c->capacity_priority != MOE_PRIORITY_SLOT)
+    return MOE_ERR_INVALID_ARG;
   if (c->num_shared > 0 && c->d_ff_shared <= 0) return MOE_ERR_INVALID_ARG;
   if (c->num_experts > 256 || c->top_k > 16 || c->num_shared > 8) return MOE_ERR_UNSUPPORTED;
   const int q = c->dtype == MOE_BF16 ? 64 : 4;
@@ -198,6 +200,7 @@ moe_status_t do_permute(const moe_config_t* c, int64_t T, const int32_t* idx, co
   a.d = c->d;
   a.dtype = c->dtype;
   a.capacity = capacity_of(c, T);
+  a.slot_major = c->capacity_priority == MOE_PRIORITY_SLOT ? 1 : 0;
   a.plans = plans;
   return hip_status(launch_permute(a, s, plans_built));
 }

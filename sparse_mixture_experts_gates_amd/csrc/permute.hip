@@ -25,8 +25,18 @@ namespace {
 
 constexpr int CH = 1024;  // slots per chunk
 
+// Slots are visited in priority order: the L-th visited slot is slot L
+// (token-major: every slot of token 0, then of token 1, ...), or with
+// slot-major priority (tslot = T) token L % T's choice L / T, so every
+// token's first choice comes before any second choice.  Ranks, capacity and
+// the row order inside each expert follow this order.
+__device__ __forceinline__ int slot_of(int L, int tslot, int k) {
+  return tslot ? (L % tslot) * k + L / tslot : L;
+}
+
 __global__ __launch_bounds__(256) void permute_count_kernel(
-    const int32_t* __restrict__ idx, int64_t n, int E, int32_t* __restrict__ bc) {
+    const int32_t* __restrict__ idx, int64_t n, int E, int32_t* __restrict__ bc, int tslot,
+    int k) {
   __shared__ int hist[256];
   for (int e = threadIdx.x; e < E; e += 256) hist[e] = 0;
   __syncthreads();
@@ -34,7 +44,7 @@ __global__ __launch_bounds__(256) void permute_count_kernel(
   for (int i = threadIdx.x; i < CH; i += 256) {
     const int64_t a = base + i;
     if (a < n) {
-      const int e = idx[a];
+      const int e = idx[slot_of((int)a, tslot, k)];
       if (e >= 0 && e < E) atomicAdd(&hist[e], 1);
     }
   }
@@ -96,7 +106,7 @@ __global__ __launch_bounds__(64) void permute_scatter_kernel(
     const int32_t* __restrict__ idx, int64_t n, int E, int64_t cap,
     const int32_t* __restrict__ bc, const int32_t* __restrict__ offsets,
     const int32_t* __restrict__ kept_total, int32_t* __restrict__ perm_src,
-    int32_t* __restrict__ slot_pos) {
+    int32_t* __restrict__ slot_pos, int tslot, int k) {
   __shared__ int run[256];
   __shared__ int off_s[256];
   const int lane = threadIdx.x;
@@ -110,10 +120,11 @@ __global__ __launch_bounds__(64) void permute_scatter_kernel(
   const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   for (int st = 0; st < CH / 64; ++st) {
     const int64_t a = base + st * 64 + lane;
+    const int sa = a < n ? slot_of((int)a, tslot, k) : 0;   // physical slot
     int e = -1;
     bool valid = a < n;
     if (valid) {
-      e = idx[a];
+      e = idx[sa];
       valid = (e >= 0 && e < E);
     }
     uint64_t peers = __ballot(valid);
@@ -131,12 +142,12 @@ __global__ __launch_bounds__(64) void permute_scatter_kernel(
     if (a < n) {
       if (valid && (cap < 0 || r < cap)) {
         const int p = off_s[e] + r;
-        slot_pos[a] = p;
-        perm_src[p] = (int32_t)a;
+        slot_pos[sa] = p;
+        perm_src[p] = sa;
       } else {
-        slot_pos[a] = -1;
+        slot_pos[sa] = -1;
       }
-      if (a >= total) perm_src[a] = -1;
+      if (a >= total) perm_src[a] = -1;   // rows past the kept ones
     }
   }
 }
@@ -164,7 +175,7 @@ __global__ __launch_bounds__(1024) void permute_fused_kernel(
     const int32_t* __restrict__ idx, int n, int E, int64_t cap, int32_t* __restrict__ counts,
     int32_t* __restrict__ offsets, int32_t* __restrict__ perm_src,
     int32_t* __restrict__ slot_pos, int32_t* __restrict__ num_dropped,
-    int32_t* __restrict__ kept_total, PlanSpec ps, int want_plans) {
+    int32_t* __restrict__ kept_total, PlanSpec ps, int want_plans, int tslot, int k) {
   __shared__ int run[FUSED_WAVES][256];
   __shared__ int sk[256];
   __shared__ int sdrop[256];
@@ -184,7 +195,7 @@ __global__ __launch_bounds__(1024) void permute_fused_kernel(
     int e = -1;
     bool valid = a < n;
     if (valid) {
-      e = idx[a];
+      e = idx[slot_of(a, tslot, k)];
       valid = e >= 0 && e < E;
     }
     const uint64_t peers = expert_peers(e, valid);
@@ -237,10 +248,11 @@ __global__ __launch_bounds__(1024) void permute_fused_kernel(
   // pass 2: place every slot of this wave's run
   for (int st = 0; st < per; st += 64) {
     const int a = lo + st + lane;
+    const int sa = a < n ? slot_of(a, tslot, k) : 0;   // physical slot
     int e = -1;
     bool valid = a < n;
     if (valid) {
-      e = idx[a];
+      e = idx[sa];
       valid = e >= 0 && e < E;
     }
     const uint64_t peers = expert_peers(e, valid);
@@ -251,12 +263,12 @@ __global__ __launch_bounds__(1024) void permute_fused_kernel(
     if (a < n) {
       if (valid && (cap < 0 || r < cap)) {
         const int p = soff[e] + r;
-        slot_pos[a] = p;
-        perm_src[p] = a;
+        slot_pos[sa] = p;
+        perm_src[p] = sa;
       } else {
-        slot_pos[a] = -1;
+        slot_pos[sa] = -1;
       }
-      if (a >= total) perm_src[a] = -1;
+      if (a >= total) perm_src[a] = -1;   // rows past the kept ones
     }
   }
 }
@@ -281,6 +293,7 @@ int permute_nblocks(int64_t rows) { return (int)((rows + CH - 1) / CH); }
 hipError_t launch_permute(const PermuteArgs& a, hipStream_t s, bool* plans_built) {
   if (plans_built) *plans_built = false;
   const int64_t n = a.T * a.k;
+  const int tslot = a.slot_major && a.k > 1 ? (int)a.T : 0;
   if (n == 0) return hipSuccess;
   if (n <= FUSED_MAX) {
     prof_before("permute", s);
@@ -288,13 +301,13 @@ hipError_t launch_permute(const PermuteArgs& a, hipStream_t s, bool* plans_built
     permute_fused_kernel<<<1, 1024, 0, s>>>(a.topk_idx, (int)n, a.E, a.capacity, a.counts,
                                             a.offsets, a.perm_src, a.slot_pos, a.num_dropped,
                                             a.kept_total, a.plans ? *a.plans : none,
-                                            a.plans ? 1 : 0);
+                                            a.plans ? 1 : 0, tslot, a.k);
     if (plans_built && a.plans) *plans_built = true;
     prof_after(s);
   } else {
   const int nb = permute_nblocks(n);
   prof_before("permute_count", s);
-  permute_count_kernel<<<nb, 256, 0, s>>>(a.topk_idx, n, a.E, a.block_counts);
+  permute_count_kernel<<<nb, 256, 0, s>>>(a.topk_idx, n, a.E, a.block_counts, tslot, a.k);
   prof_after(s);
   prof_before("permute_scan", s);
   permute_scan_kernel<<<1, 256, 0, s>>>(a.block_counts, nb, a.E, a.capacity, a.counts,
@@ -302,7 +315,8 @@ hipError_t launch_permute(const PermuteArgs& a, hipStream_t s, bool* plans_built
   prof_after(s);
   prof_before("permute_scatter", s);
   permute_scatter_kernel<<<nb, 64, 0, s>>>(a.topk_idx, n, a.E, a.capacity, a.block_counts,
-                                           a.offsets, a.kept_total, a.perm_src, a.slot_pos);
+                                           a.offsets, a.kept_total, a.perm_src, a.slot_pos,
+                                           tslot, a.k);
   prof_after(s);
   }
   if (a.x_perm) {

@@ -53,6 +53,7 @@ class Workload:
     bias: Optional[Tuple[str, float]] = None     # ("normal", var)
     num_shared: int = 0
     d_ff_shared: int = 0
+    capacity_priority: str = "token"   # "token" or "slot": which slots claim capacity first
     x_tag: int = TAG_X
     seed: int = 0
 

@@ -82,7 +82,7 @@ def check_routing(w, inp, g, report):
     assert (err <= 1e-4 + 1e-5 * np.abs(s_ref)).all(), f"router scores off by {err.max():.3e}"
     r = O.route_from_logits(g["logits"], k=w.k, gating=w.gating,
                             capacity_factor=float(np.float32(w.capacity_factor)),
-                            select_bias=bias)
+                            select_bias=bias, capacity_priority=w.capacity_priority)
     near = r["near_tie"]
     mism = (r["topk_idx"] != g["idx"]).any(axis=1)
     bad = mism & ~near
@@ -102,7 +102,7 @@ def check_routing(w, inp, g, report):
     assert np.abs(g["gate"] - g_ref).max() <= 1e-6
     # permutation from the GPU's selection: bit-exact
     C = O.capacity(float(np.float32(w.capacity_factor)), w.k, w.T, w.E)
-    pr = O.permute(g["idx"], w.E, C)
+    pr = O.permute(g["idx"], w.E, C, w.capacity_priority)
     assert (pr.counts == g["expert_counts"]).all()
     assert (pr.offsets == g["expert_offsets"]).all()
     assert (pr.perm_src == g["perm_src"]).all()

@@ -38,7 +38,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_config_struct_layout():
-    assert ctypes.sizeof(B.MoeConfig) == 40
+    assert ctypes.sizeof(B.MoeConfig) == 44
 
 
 def test_status_strings():
@@ -69,6 +69,9 @@ def test_config_validation():
     assert B.check_config(c, 10) == 1
     c = cfg(); c.capacity_factor = float("nan")
     assert B.check_config(c, 10) == 1
+    c = cfg(); c.capacity_priority = 2
+    assert B.check_config(c, 10) == 1
+    assert B.check_config(cfg(capacity_priority="slot"), 10) == 0
     assert B.check_config(cfg(d=100), 10) == 2              # bf16 needs multiples of 64
     assert B.check_config(cfg(d=102, dtype="f32"), 10) == 2
     assert B.check_config(cfg(d=100, dtype="f32"), 10) == 0

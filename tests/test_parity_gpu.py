@@ -97,6 +97,13 @@ EDGES = {
     "persistent_256x256_first_gemm": small(T=1024, d=192, E=8, k=2, d_ff=16384),
     "persistent_256x256_second_gemm": small(T=4096, d=8192, E=8, k=2, d_ff=192),
     "persistent_256x128": small(T=500, d=256, E=64, k=2, d_ff=512),
+    # slot-major capacity priority: one-workgroup and chunked permutations,
+    # with drops and without a limit (row order only)
+    "slot_priority_capacity": small(T=400, k=2, capacity_factor=1.0, offset=("normal", 0.5),
+                                    capacity_priority="slot"),
+    "slot_priority_chunked": small(T=3000, k=3, capacity_factor=0.9, offset=("normal", 0.5),
+                                   capacity_priority="slot"),
+    "slot_priority_no_limit": small(T=300, k=3, capacity_priority="slot"),
 }
 
 
