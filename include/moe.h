@@ -1,6 +1,7 @@
 /*
- * moe.h -- C ABI of libmoe_mi355x.so: the forward pass of a sparse
- * mixture-of-experts feed-forward layer on AMD Instinct MI355X (gfx950).
+ * moe.h -- C ABI of libmoe_mi355x.so: the forward pass (and its backward
+ * pass, for training) of a sparse mixture-of-experts feed-forward layer on
+ * AMD Instinct MI355X (gfx950).
  *
  * The layer (sources: "Mixture of experts", Inside the Model guide ch. 14,
  * section "The computation", equation block; "Mixture of Experts", LLM
@@ -281,6 +282,88 @@ moe_status_t moe_routing_stats(const moe_config_t* cfg, int64_t T,
                                float gamma, float alpha, float* f, float* P,
                                float* loss, float* drop_rate, float* bias_out,
                                void* workspace, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------ training ---
+ * The backward pass of the same layer (sources: "Mixture of Experts", LLM
+ * tutorial ch. 11, "The routing decision", last paragraph, and "Training
+ * instability"; "Mixture of experts", Inside the Model ch. 14, "Auxiliary
+ * loss" and "Check yourself").  Given dy = dLoss/dy it returns the gradients
+ * of <dy, y> (+ the balance loss alpha E sum_i f_i P_i when aux_alpha > 0)
+ * with respect to x, w_router and every expert weight.  The routing is held
+ * fixed: top-k selection and the capacity cut are discrete and pass no
+ * gradient; the router learns through the gate values (all three gatings)
+ * and, with the balance loss, through P (f is a count and carries none).
+ * select_bias and logit_offset receive no gradient.  bf16 only
+ * (MOE_ERR_UNSUPPORTED otherwise).
+ *
+ * Two calls: moe_forward_train() is moe_forward() that keeps what the
+ * backward needs (routing, router scores, gathered rows, expert
+ * pre-activations, hidden activations, expert outputs) in a caller-owned
+ * `saved` buffer; moe_backward() reads it.  The saved buffer must not be
+ * written between the two calls; it may be reused for the next step. */
+
+/* Bytes of the saved buffer of moe_forward_train() for T tokens.  Host only. */
+moe_status_t moe_train_workspace_size(const moe_config_t* cfg, int64_t T,
+                                      size_t* bytes);
+
+/* The forward pass of moe_forward() (same arguments and the same y bits),
+ * keeping in `saved` (saved_bytes >= moe_train_workspace_size(), 256-byte
+ * aligned) the routing, the router scores, the permuted input rows and, per
+ * kept row, the first GEMM's pre-activations (W1 x, and W3 x for SwiGLU,
+ * rounded to bf16), the hidden activations and the expert outputs; the
+ * shared experts' likewise. */
+moe_status_t moe_forward_train(const moe_config_t* cfg, int64_t T,
+                               const void* x, const void* w_router,
+                               const float* logit_offset,
+                               const float* select_bias, const void* w1,
+                               const void* w3, const void* w2, const void* ws1,
+                               const void* ws3, const void* ws2, void* y,
+                               void* saved, size_t saved_bytes, void* stream);
+
+/* Device pointers into a saved buffer (host arithmetic only, nothing is
+ * enqueued): the router scores [T, E] fp32, topk_idx [T, k], topk_gate [T, k],
+ * expert_counts [E], num_dropped [1], expert_offsets [E+1], slot_pos [T*k], as
+ * moe_forward_train() wrote them.  Any output pointer may be NULL. */
+moe_status_t moe_saved_routing(const moe_config_t* cfg, int64_t T, void* saved,
+                               float** logits, int32_t** topk_idx,
+                               float** topk_gate, int32_t** expert_counts,
+                               int32_t** num_dropped, int32_t** expert_offsets,
+                               int32_t** slot_pos);
+
+/* Bytes of the workspace moe_backward() needs for T tokens.  Host only. */
+moe_status_t moe_backward_workspace_size(const moe_config_t* cfg, int64_t T,
+                                         size_t* bytes);
+
+/* Gradients of one layer.
+ *   x, w_router, w1, w3, w2, ws1, ws3, ws2   as given to moe_forward_train()
+ *   saved      the buffer moe_forward_train() filled (saved_bytes as there)
+ *   dy         [T, d] bf16: gradient of the loss with respect to y
+ *   aux_alpha  host scalar >= 0: weight of the balance loss (0 = none)
+ *   dx         [T, d] bf16 out
+ *   dw_router  [E, d] fp32 out (router math in FP32)
+ *   dw1, dw3   [E, d_ff, d] bf16 out (dw3 only for SwiGLU, else NULL)
+ *   dw2        [E, d, d_ff] bf16 out
+ *   dws1, dws3 [S, d_ff_shared, d], dws2 [S, d, d_ff_shared] bf16 out (NULL
+ *              when num_shared == 0)
+ *   d_gate     [T, k] fp32 out or NULL: dLoss/dg (0 on dropped slots)
+ *   d_logits   [T, E] fp32 out or NULL: dLoss/ds, the router score gradient
+ *   workspace  device scratch, ws_bytes >= moe_backward_workspace_size()
+ * Every output is overwritten (an expert with no kept row gets zero weight
+ * gradients).  Per kept slot: dg = <dy, Expert(x)>, the expert's output
+ * gradient g dy (rounded to bf16); then dH = (g dy) W2, the activation's
+ * derivative from the saved pre-activations, dX, dW1, dW2, dW3 on bf16 MFMA
+ * with fp32 accumulation over the expert's rows, each rounded once to bf16;
+ * dx sums the kept slots' dX, the shared experts' dX and ds . w_router in
+ * fp32 and rounds once.  Deterministic (no atomics). */
+moe_status_t moe_backward(const moe_config_t* cfg, int64_t T, const void* x,
+                          const void* w_router, const void* w1, const void* w3,
+                          const void* w2, const void* ws1, const void* ws3,
+                          const void* ws2, const void* saved,
+                          size_t saved_bytes, const void* dy, float aux_alpha,
+                          void* dx, float* dw_router, void* dw1, void* dw3,
+                          void* dw2, void* dws1, void* dws3, void* dws2,
+                          float* d_gate, float* d_logits, void* workspace,
+                          size_t ws_bytes, void* stream);
 
 /* Per-kernel timing with HIP events, for measurement tools.
  * moe_profile_enable(1) clears the record and brackets every later launch by

@@ -28,7 +28,9 @@ STATUS = {0: "MOE_OK", 1: "MOE_ERR_INVALID_ARG", 2: "MOE_ERR_UNSUPPORTED",
 
 EXPORTS = ("moe_status_str", "moe_check_config", "moe_workspace_size", "moe_capacity",
            "moe_route", "moe_permute", "moe_expert_ffn", "moe_combine", "moe_forward",
-           "moe_routing_stats", "moe_profile_enable", "moe_profile_read")
+           "moe_routing_stats", "moe_profile_enable", "moe_profile_read",
+           "moe_train_workspace_size", "moe_forward_train", "moe_saved_routing",
+           "moe_backward_workspace_size", "moe_backward")
 
 
 class MoeError(RuntimeError):
@@ -72,6 +74,12 @@ def lib():
         L.moe_forward.argtypes = [_cfgp, _i64] + [_vp] * 16 + [_sz, _vp]
         L.moe_routing_stats.argtypes = ([_cfgp, _i64] + [_vp] * 4 + [ctypes.c_float] * 2
                                         + [_vp] * 6 + [_sz, _vp])
+        L.moe_train_workspace_size.argtypes = [_cfgp, _i64, ctypes.POINTER(_sz)]
+        L.moe_forward_train.argtypes = [_cfgp, _i64] + [_vp] * 12 + [_sz, _vp]
+        L.moe_saved_routing.argtypes = [_cfgp, _i64, _vp] + [ctypes.POINTER(_vp)] * 7
+        L.moe_backward_workspace_size.argtypes = [_cfgp, _i64, ctypes.POINTER(_sz)]
+        L.moe_backward.argtypes = ([_cfgp, _i64] + [_vp] * 9 + [_sz, _vp, ctypes.c_float]
+                                   + [_vp] * 11 + [_sz, _vp])
         L.moe_profile_enable.argtypes = [ctypes.c_int32]
         L.moe_profile_read.restype = ctypes.c_int32
         L.moe_profile_read.argtypes = [ctypes.POINTER(ctypes.c_char_p),
@@ -79,7 +87,9 @@ def lib():
                                        ctypes.POINTER(ctypes.c_int32), ctypes.c_int32]
         for fn in ("moe_check_config", "moe_workspace_size", "moe_capacity", "moe_route",
                    "moe_permute", "moe_expert_ffn", "moe_combine", "moe_forward",
-                   "moe_routing_stats", "moe_profile_enable"):
+                   "moe_routing_stats", "moe_profile_enable", "moe_train_workspace_size",
+                   "moe_forward_train", "moe_saved_routing", "moe_backward_workspace_size",
+                   "moe_backward"):
             getattr(L, fn).restype = ctypes.c_int
         _lib_handle = L
     return _lib_handle
@@ -254,6 +264,105 @@ def routing_stats(cfg, logits, expert_counts, num_dropped=None, select_bias=None
                                    _ptr(bias_out), _ptr(ws), ws.numel(), _stream()),
            "moe_routing_stats")
     return dict(f=f, P=P, loss=loss, drop_rate=rate, bias=bias_out)
+
+
+# ------------------------------------------------------------------ training
+def train_workspace_size(cfg, T):
+    n = _sz(0)
+    _check(lib().moe_train_workspace_size(ctypes.byref(cfg), T, ctypes.byref(n)),
+           "moe_train_workspace_size")
+    return n.value
+
+
+def backward_workspace_size(cfg, T):
+    n = _sz(0)
+    _check(lib().moe_backward_workspace_size(ctypes.byref(cfg), T, ctypes.byref(n)),
+           "moe_backward_workspace_size")
+    return n.value
+
+
+def forward_train(cfg, x, w_router, w1, w2, w3=None, *, logit_offset=None, select_bias=None,
+                  ws1=None, ws3=None, ws2=None, saved=None, y=None):
+    """Training forward.  Returns (y, saved): ``saved`` is the uint8 buffer
+    that moe_backward reads (keep it unchanged until then)."""
+    T = x.shape[0]
+    dev = x.device
+    if y is None:
+        y = torch.empty((T, cfg.d), dtype=_dt(cfg), device=dev)
+    if saved is None:
+        saved = torch.empty(max(train_workspace_size(cfg, T), 1), dtype=torch.uint8, device=dev)
+    _check(lib().moe_forward_train(ctypes.byref(cfg), T, _ptr(x), _ptr(w_router),
+                                   _ptr(logit_offset), _ptr(select_bias), _ptr(w1), _ptr(w3),
+                                   _ptr(w2), _ptr(ws1), _ptr(ws3), _ptr(ws2), _ptr(y),
+                                   _ptr(saved), saved.numel(), _stream()),
+           "moe_forward_train")
+    return y, saved
+
+
+def forward_train_inputs(cfg, inp, **kw):
+    """forward_train() on a dict from workloads.make_inputs."""
+    return forward_train(cfg, inp["x"], inp["w_router"], inp["w1"], inp["w2"], inp.get("w3"),
+                         logit_offset=inp.get("logit_offset"),
+                         select_bias=inp.get("select_bias"), ws1=inp.get("ws1"),
+                         ws3=inp.get("ws3"), ws2=inp.get("ws2"), **kw)
+
+
+def saved_routing(cfg, T, saved):
+    """Views (torch tensors) of the routing a training forward kept in saved:
+    logits, topk_idx, topk_gate, expert_counts, num_dropped, expert_offsets,
+    slot_pos."""
+    ptrs = [_vp() for _ in range(7)]
+    _check(lib().moe_saved_routing(ctypes.byref(cfg), T, _ptr(saved),
+                                   *[ctypes.byref(p) for p in ptrs]), "moe_saved_routing")
+    base = saved.data_ptr()
+    k, E = cfg.top_k, cfg.num_experts
+    spec = [("logits", (T, E), torch.float32), ("topk_idx", (T, k), torch.int32),
+            ("topk_gate", (T, k), torch.float32), ("expert_counts", (E,), torch.int32),
+            ("num_dropped", (1,), torch.int32), ("expert_offsets", (E + 1,), torch.int32),
+            ("slot_pos", (T * k,), torch.int32)]
+    out = {}
+    for p, (name, shape, dt) in zip(ptrs, spec):
+        off = p.value - base
+        n = 1
+        for v in shape:
+            n *= v
+        out[name] = saved[off:off + n * 4].view(dt).view(shape)
+    return out
+
+
+def backward(cfg, x, w_router, w1, w2, w3, saved, dy, *, ws1=None, ws3=None, ws2=None,
+             aux_alpha=0.0, ws=None, grads=None, want_gate_grads=False):
+    """Gradients of one layer from a training forward's ``saved`` buffer.
+    Returns dict(dx, dw_router, dw1, dw3, dw2, dws1, dws3, dws2, d_gate,
+    d_logits); ``grads`` may be an earlier result dict whose tensors are
+    reused."""
+    T = x.shape[0]
+    dev = x.device
+    glu = cfg.act == ACTS["swiglu"]
+    S = cfg.num_shared
+    if grads is None:
+        grads = dict(
+            dx=torch.empty_like(x), dw_router=torch.empty(w_router.shape, dtype=torch.float32,
+                                                          device=dev),
+            dw1=torch.empty_like(w1), dw3=torch.empty_like(w3) if glu else None,
+            dw2=torch.empty_like(w2),
+            dws1=torch.empty_like(ws1) if S else None, dws3=torch.empty_like(ws3) if S else None,
+            dws2=torch.empty_like(ws2) if S else None,
+            d_gate=torch.empty((T, cfg.top_k), dtype=torch.float32, device=dev)
+            if want_gate_grads else None,
+            d_logits=torch.empty((T, cfg.num_experts), dtype=torch.float32, device=dev)
+            if want_gate_grads else None)
+    if ws is None:
+        ws = torch.empty(max(backward_workspace_size(cfg, T), 1), dtype=torch.uint8, device=dev)
+    g = grads
+    _check(lib().moe_backward(ctypes.byref(cfg), T, _ptr(x), _ptr(w_router), _ptr(w1), _ptr(w3),
+                              _ptr(w2), _ptr(ws1), _ptr(ws3), _ptr(ws2), _ptr(saved),
+                              saved.numel(), _ptr(dy), float(aux_alpha), _ptr(g["dx"]),
+                              _ptr(g["dw_router"]), _ptr(g["dw1"]), _ptr(g["dw3"]),
+                              _ptr(g["dw2"]), _ptr(g["dws1"]), _ptr(g["dws3"]), _ptr(g["dws2"]),
+                              _ptr(g["d_gate"]), _ptr(g["d_logits"]), _ptr(ws), ws.numel(),
+                              _stream()), "moe_backward")
+    return g
 
 
 def profile_enable(on=True):

@@ -1,0 +1,697 @@
+// Backward pass of the sparse MoE layer, bf16 operands, fp32 accumulation.
+//
+// The routing is held fixed: the gradient reaches the router only through the
+// soft gate values and, with the balance loss, through the mean router
+// probabilities ("Mixture of Experts", LLM tutorial ch. 11, "The routing
+// decision" and "Training instability"; "Mixture of experts", Inside the
+// Model ch. 14, "Auxiliary loss" and "Check yourself").  Steps:
+//
+//   gate kernel   per token: dg_j = <dy, O_j> for each kept slot, the expert
+//                 output gradient dO_j = g_j dy (bf16, on the permuted row),
+//                 and the score gradient ds = J^T dg (+ balance loss), fp32
+//   dH GEMM       dH = dO . W2_e over each expert's rows; the epilogue applies
+//                 the activation's derivative with the saved pre-activations
+//                 (SwiGLU: dG = dH u silu'(g), dU = dH silu(g))
+//   dX GEMM       dX = dG . W1_e (+ dU . W3_e) over each expert's rows
+//   dW GEMMs      dW2_e = dO_e^T H_e, dW1_e = dG_e^T X_e, dW3_e = dU_e^T X_e:
+//                 the contraction runs over the expert's rows (ragged K)
+//   dx kernel     dx_t = sum over kept slots of dX rows + shared experts'
+//                 dX + ds_t . W_r, one rounding
+//   router        dW_r = ds^T x, fp32, fixed-order partial sums
+//
+// GEMM layout.  Every backward GEMM has its output's contiguous dimension on
+// the MFMA row side (P) and its other dimension on the column side (Q), as
+// the forward does.  P is always stored with that output dimension
+// contiguous (W2_e rows for dH, W1_e / W3_e rows for dX, H or x rows for the
+// weight gradients), so its K index is strided: P tiles are staged in LDS as
+// k-rows of 64-element lines and read with ds_read_b64_tr_b16, which hands
+// each lane 4 consecutive k of one column (two reads make one 8-k MFMA
+// operand).  Q is K-contiguous (activation rows) for dH / dX, read like the
+// forward's operands, and k-strided for the weight gradients (tr reads too).
+#include <string.h>
+
+#include "common.h"
+#include "launch.h"
+#include "plan.h"
+
+namespace moe {
+
+namespace {
+
+constexpr int BK = 64;
+constexpr int GB_BM = 256, GB_BN = 256;     // output tile: Q extent x P extent
+constexpr int GB_WM = 2, GB_WN = 4;         // waves along Q, along P
+constexpr int GB_NW = GB_WM * GB_WN;
+
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+
+// P-side / MN-major LDS tile: BK k-rows, each split into 64-element lines of
+// 128 bytes.  Line (k, nb) sits at index k * NL + nb; within a line, 16-byte
+// chunk c sits at chunk c ^ ((k & 3) << 1), so the four k-rows one transposed
+// read touches (same columns) land on distinct bank groups.
+template <int NL>
+__device__ __forceinline__ int mn_off(int k, int col) {   // bf16 element offset
+  const int nb = col >> 6, c = (col >> 3) & 7, h = col & 7;
+  return (k * NL + nb) * 64 + ((c ^ ((k & 3) << 1)) << 3) + h;
+}
+
+// One MFMA operand (16 columns x 32 k) from an MN-major tile: lane l covers
+// column l%16, k 8*(l/16) .. +7.  Each transposed read gathers 4 k-rows x 16
+// columns over a 16-lane group: lanes 4q..4q+3 address row q, 4 columns each.
+template <int NL>
+__device__ __forceinline__ bf16x8_t read_mn(const uint16_t* tile, int col0, int k0, int lane) {
+  const int q = (lane & 15) >> 2;
+  const int col = col0 + 4 * (lane & 3);
+  const int kr = k0 + 8 * (lane >> 4) + q;
+  auto p0 = (__attribute__((address_space(3))) i16x4_t*)MOE_LDS_PTR(tile + mn_off<NL>(kr, col));
+  auto p1 = (__attribute__((address_space(3))) i16x4_t*)MOE_LDS_PTR(tile + mn_off<NL>(kr + 4, col));
+  const i16x4_t a = __builtin_amdgcn_ds_read_tr16_b64_v4i16(p0);
+  const i16x4_t b = __builtin_amdgcn_ds_read_tr16_b64_v4i16(p1);
+  const i16x4_t v[2] = {a, b};
+  return __builtin_bit_cast(bf16x8_t, v);
+}
+
+// Direct-to-LDS load of 8 lines of an MN-major tile (1 KB): lane l fills line
+// l/8, stored chunk l%8, so it fetches logical chunk (l%8) ^ ((k & 3) << 1).
+__device__ __forceinline__ int mn_chunk(int lane, int k) { return (lane & 7) ^ ((k & 3) << 1); }
+
+struct GemmArgs {
+  int kind;                   // BG_DH, BG_DX, BG_DW
+  const uint16_t* P;          // MN-major operand (see launch.h)
+  const uint16_t* P2;
+  int64_t ldp, p_seg;         // row pitch; per-segment element offset (dH/dX weights)
+  int64_t p_row_seg;          // dW: per-segment row offset of P
+  const uint16_t* Q;
+  const uint16_t* Q2;
+  int64_t ldq;
+  int64_t q_row_seg;          // row offset of segment g in Q (dense segments)
+  uint16_t* C;
+  uint16_t* C2;
+  int64_t ldc, c_seg;         // dW: per-segment element offset of C
+  int64_t c_row_seg;          // dH/dX: row offset of segment g in C (dense segments)
+  const uint16_t* S1;         // dH: saved pre-activations (G or Z) and U
+  const uint16_t* S2;
+  const PlanEntry* plan;      // dH/dX row tiles
+  const int32_t* count;
+  const int32_t* seg;         // dW: [G+1] row offsets, or null (dense)
+  int64_t dense_rows;
+  const uint16_t* zero;       // >= 256 zero elements
+  int K, N, M;                // dH/dX: K per operand pair; N output cols; dW: M output rows
+  int nk1;                    // dX: slabs of the first operand pair
+  int G, MT, NT;              // dW tile grid
+};
+
+__device__ __forceinline__ int xcd_remap_b(int P, int V) {
+  const int x = P & 7, i = P >> 3, q = V >> 3, r = V & 7;
+  return (x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q) + i;
+}
+
+__device__ __forceinline__ float sigm(float z) { return 1.0f / (1.0f + __expf(-z)); }
+
+// d/dz of the erf GeLU: Phi(z) + z phi(z)
+__device__ __forceinline__ float gelu_grad(float z) {
+  return 0.5f * (1.0f + erff(z * 0.70710678118654752f)) +
+         z * 0.39894228040143268f * __expf(-0.5f * z * z);
+}
+
+template <int KIND, int EPI>
+__global__ __launch_bounds__(64 * GB_NW) void bwd_gemm_kernel(GemmArgs a) {
+  constexpr int BM = GB_BM, BN = GB_BN, WN = GB_WN, NW = GB_NW;
+  constexpr int BMW = BM / GB_WM, BNW = BN / WN;
+  constexpr int TM = BMW / 16, TN = BNW / 16;
+  constexpr int NLP = BN / 64, NLQ = BM / 64;
+  constexpr int SP = BK * BN, SQ = BK * BM;
+  constexpr bool QMN = KIND == BG_DW;
+  constexpr int DP = BK * NLP / 8 / NW;     // P load instructions per wave per slab
+  constexpr int DQ = (QMN ? BK * NLQ : BM) / 8 / NW;
+  static_assert(DP * NW * 8 == BK * NLP && DQ * NW * 8 == (QMN ? BK * NLQ : BM), "load split");
+  __shared__ __attribute__((aligned(1024))) uint16_t ring[2 * (SP + SQ)];
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int wm = wave / WN, wn = wave % WN;
+
+  int g, m0, m1, n0, nk;
+  int64_t prow0 = 0, qrow0 = 0, klen = 0;
+  if constexpr (KIND == BG_DW) {
+    const int V = a.G * a.MT * a.NT;
+    if ((int)blockIdx.x >= V) return;
+    const int e = xcd_remap_b(blockIdx.x, V);
+    g = e / (a.MT * a.NT);
+    const int rem = e - g * a.MT * a.NT;
+    const int nt = rem / a.MT, mt = rem - nt * a.MT;
+    m0 = mt * BM;
+    m1 = m0 + BM < a.M ? m0 + BM : a.M;
+    n0 = nt * BN;
+    const int64_t r0 = a.seg ? a.seg[g] : 0;
+    klen = a.seg ? a.seg[g + 1] - r0 : a.dense_rows;
+    prow0 = (int64_t)g * a.p_row_seg + r0;
+    qrow0 = (int64_t)g * a.q_row_seg + r0;
+    nk = (int)((klen + BK - 1) / BK);
+  } else {
+    const int V = a.count[0];
+    if ((int)blockIdx.x >= V) return;
+    const PlanEntry pe = a.plan[xcd_remap_b(blockIdx.x, V)];
+    g = pe.g;
+    m0 = pe.m0;
+    m1 = pe.m1;
+    n0 = pe.nt * BN;
+    qrow0 = (int64_t)g * a.q_row_seg;
+    nk = KIND == BG_DX && EPI == 1 ? 2 * a.nk1 : a.K / BK;
+  }
+  const int N = a.N;
+
+  // Per-lane load sources.  P: DP instructions of 8 lines; Q: DQ instructions
+  // (8 rows of 64 k, or 8 lines of an MN-major tile).
+  int p_k[DP], p_col[DP];
+#pragma unroll
+  for (int i = 0; i < DP; ++i) {
+    const int L = (wave + i * NW) * 8 + (lane >> 3);
+    p_k[i] = L / NLP;
+    int col = n0 + (L % NLP) * 64;
+    if (col > N - 64) col = N - 64;            // past the last column: any valid line
+    p_col[i] = col + mn_chunk(lane, p_k[i]) * 8;
+  }
+  int q_k[DQ], q_col[DQ];
+  int64_t q_off[DQ];   // K-major Q: element offset of this lane's row and chunk
+#pragma unroll
+  for (int i = 0; i < DQ; ++i) {
+    if constexpr (QMN) {
+      const int L = (wave + i * NW) * 8 + (lane >> 3);
+      q_k[i] = L / NLQ;
+      int col = m0 + (L % NLQ) * 64;
+      if (col > a.M - 64) col = a.M - 64;
+      q_col[i] = col + mn_chunk(lane, q_k[i]) * 8;
+      q_off[i] = 0;
+    } else {
+      int r = m0 + (wave + i * NW) * 8 + dma_row(lane);
+      if (r > m1 - 1) r = m1 - 1;
+      q_k[i] = 0;
+      q_col[i] = 0;
+      q_off[i] = (qrow0 + r) * a.ldq + dma_chunk(lane) * 8;
+    }
+  }
+  const uint16_t* const pw = a.P + (int64_t)g * a.p_seg;
+  const uint16_t* const pw2 = a.P2 ? a.P2 + (int64_t)g * a.p_seg : pw;
+
+  auto issue = [&](int kt, int stage) {
+    uint16_t* sp = ring + stage * (SP + SQ);
+    uint16_t* sq = sp + SP;
+#pragma unroll
+    for (int i = 0; i < DP; ++i) {
+      const uint16_t* src;
+      if constexpr (KIND == BG_DW) {
+        const int64_t r = (int64_t)kt * BK + p_k[i];
+        src = r < klen ? a.P + (prow0 + r) * a.ldp + p_col[i] : a.zero + 8 * (lane & 7);
+      } else if constexpr (KIND == BG_DX) {
+        const bool second = kt >= a.nk1;
+        const int kk = (second ? kt - a.nk1 : kt) * BK + p_k[i];
+        src = (second ? pw2 : pw) + (int64_t)kk * a.ldp + p_col[i];
+      } else {
+        src = pw + (int64_t)(kt * BK + p_k[i]) * a.ldp + p_col[i];
+      }
+      dma_rows(src, sp + (wave + i * NW) * 512);
+    }
+#pragma unroll
+    for (int i = 0; i < DQ; ++i) {
+      const uint16_t* src;
+      if constexpr (QMN) {
+        const int64_t r = (int64_t)kt * BK + q_k[i];
+        src = r < klen ? a.Q + (qrow0 + r) * a.ldq + q_col[i] : a.zero + 8 * (lane & 7);
+      } else if constexpr (KIND == BG_DX) {
+        const bool second = kt >= a.nk1;
+        src = (second ? a.Q2 : a.Q) + q_off[i] + (int64_t)(second ? kt - a.nk1 : kt) * BK;
+      } else {
+        src = a.Q + q_off[i] + (int64_t)kt * BK;
+      }
+      dma_rows(src, sq + (wave + i * NW) * 512);
+    }
+  };
+
+  f32x4_t acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  if (nk > 0) issue(0, 0);
+  for (int kt = 0; kt < nk; ++kt) {
+    wait_vm_lgkm0<0>();
+    ring_barrier();
+    if (kt + 1 < nk) issue(kt + 1, (kt + 1) & 1);
+    const uint16_t* sp = ring + (kt & 1) * (SP + SQ);
+    const uint16_t* sq = sp + SP;
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      bf16x8_t fp[TN], fq[TM];
+#pragma unroll
+      for (int j = 0; j < TN; ++j) fp[j] = read_mn<NLP>(sp, wn * BNW + j * 16, kk * 32, lane);
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        if constexpr (QMN) {
+          fq[i] = read_mn<NLQ>(sq, wm * BMW + i * 16, kk * 32, lane);
+        } else {
+          const int ch = kk * 4 + (lane >> 4);
+          fq[i] = *reinterpret_cast<const bf16x8_t*>(sq + swz(wm * BMW + i * 16 + (lane & 15), ch));
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fp[j], fq[i], acc[i][j], 0, 0, 0);
+    }
+  }
+  wait_vm_lgkm0<0>();
+
+  // epilogue: lane holds output columns 4*(lane/16)+q of tile j, row lane%16
+  // of tile i
+  const int64_t crow0 = KIND == BG_DW ? 0 : (int64_t)g * a.c_row_seg;
+  uint16_t* const cbase = a.C + (KIND == BG_DW ? (int64_t)g * a.c_seg : 0);
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+    const int m = m0 + wm * BMW + i * 16 + (lane & 15);
+    if (m >= m1) continue;
+    const int64_t row = (crow0 + m) * a.ldc;
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const int col = n0 + wn * BNW + j * 16 + 4 * (lane >> 4);
+      if (col >= N) continue;
+      float v[4] = {acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]};
+      if constexpr (KIND == BG_DH && EPI != 0) {
+        // activation backward with the saved pre-activations
+        const uint2 s1 = *reinterpret_cast<const uint2*>(a.S1 + row + col);
+        const uint32_t z32[4] = {s1.x & 0xffffu, s1.x >> 16, s1.y & 0xffffu, s1.y >> 16};
+        if constexpr (EPI == 3) {
+          const uint2 s2 = *reinterpret_cast<const uint2*>(a.S2 + row + col);
+          const uint32_t u32[4] = {s2.x & 0xffffu, s2.x >> 16, s2.y & 0xffffu, s2.y >> 16};
+          float dg[4], du[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const float z = bf16_to_f32(z32[q]), u = bf16_to_f32(u32[q]);
+            const float sg = sigm(z);
+            du[q] = v[q] * z * sg;
+            dg[q] = v[q] * u * sg * (1.0f + z * (1.0f - sg));
+          }
+          uint2 pg, pu;
+          pg.x = pack_bf16x2(dg[0], dg[1]);
+          pg.y = pack_bf16x2(dg[2], dg[3]);
+          pu.x = pack_bf16x2(du[0], du[1]);
+          pu.y = pack_bf16x2(du[2], du[3]);
+          *reinterpret_cast<uint2*>(cbase + row + col) = pg;
+          *reinterpret_cast<uint2*>(a.C2 + row + col) = pu;
+          continue;
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float z = bf16_to_f32(z32[q]);
+          v[q] = EPI == 1 ? (z > 0.f ? v[q] : 0.f) : v[q] * gelu_grad(z);
+        }
+      }
+      uint2 pk;
+      pk.x = pack_bf16x2(v[0], v[1]);
+      pk.y = pack_bf16x2(v[2], v[3]);
+      *reinterpret_cast<uint2*>(cbase + row + col) = pk;
+    }
+  }
+}
+
+// ---------------------------------------------------------------- gate step
+// One wave per token.  dg_j = <dy_t, O_j> over the kept slots (O in bf16, or
+// the two fp32 K parts of a split second GEMM), dO_j = bf16(g_j dy_t) on the
+// slot's permuted row, then the score gradient of the token (dense [E]).
+__global__ __launch_bounds__(256) void gate_bwd_kernel(GateBwdArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= a.T) return;
+  const int d = a.d, k = a.k, E = a.E;
+  const int nch = d >> 3;                      // 8-element chunks per row
+  const uint16_t* dyr = a.dy + t * d;
+  // slot-indexed values stay in registers: every loop over the k <= 16 slots
+  // is unrolled with a guard
+  float dgv[16], gv[16];
+  int ev[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    dgv[j] = 0.f;
+    gv[j] = 0.f;
+    ev[j] = -1;
+    if (j >= k) continue;
+    const int r = a.slot_pos[t * k + j];
+    const float g = a.gate[t * k + j];
+    ev[j] = a.topk_idx[t * k + j];
+    gv[j] = g;
+    if (r < 0) continue;                       // dropped: no output, dg = 0
+    float s = 0.f;
+    for (int c = lane; c < nch; c += 64) {
+      const u32x4_t y8 = *reinterpret_cast<const u32x4_t*>(dyr + c * 8);
+      float yf[8];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        yf[2 * q] = bf16_to_f32(y8[q] & 0xffffu);
+        yf[2 * q + 1] = bf16_to_f32(y8[q] >> 16);
+      }
+      float of[8];
+      if (a.part) {
+        const float* p0 = a.part + (int64_t)r * d + c * 8;
+        const float* p1 = p0 + a.part_stride;
+        const f32x4_t a0 = *reinterpret_cast<const f32x4_t*>(p0);
+        const f32x4_t a1 = *reinterpret_cast<const f32x4_t*>(p0 + 4);
+        const f32x4_t b0 = *reinterpret_cast<const f32x4_t*>(p1);
+        const f32x4_t b1 = *reinterpret_cast<const f32x4_t*>(p1 + 4);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          of[q] = a0[q] + b0[q];
+          of[4 + q] = a1[q] + b1[q];
+        }
+      } else {
+        const u32x4_t o8 = *reinterpret_cast<const u32x4_t*>(a.eout + (int64_t)r * d + c * 8);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          of[2 * q] = bf16_to_f32(o8[q] & 0xffffu);
+          of[2 * q + 1] = bf16_to_f32(o8[q] >> 16);
+        }
+      }
+      u32x4_t w;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) s += yf[q] * of[q];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) w[q] = pack_bf16x2(g * yf[2 * q], g * yf[2 * q + 1]);
+      *reinterpret_cast<u32x4_t*>(a.d_out + (int64_t)r * d + c * 8) = w;
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off, 64);
+    dgv[j] = s;
+  }
+  float A = 0.f;
+#pragma unroll
+  for (int j = 0; j < 16; ++j)
+    if (j < k) A += gv[j] * dgv[j];
+  if (a.d_gate && lane < k) {
+    float v = 0.f;
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+      if (j == lane) v = dgv[j];
+    a.d_gate[t * k + lane] = v;
+  }
+  const float* s_t = a.logits + t * E;
+  // full softmax p (needed by the full-softmax gates and by the balance loss)
+  const bool need_p = a.gating == MOE_GATE_SOFTMAX_FULL || a.aux_scale != 0.f;
+  float sv[4], pv[4];
+  float mx = -INFINITY;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int e = lane + 64 * u;
+    sv[u] = e < E ? s_t[e] : -INFINITY;
+    mx = fmaxf(mx, sv[u]);
+  }
+  float fp = 0.f;
+  if (need_p) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
+    float z = 0.f;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      pv[u] = lane + 64 * u < E ? __expf(sv[u] - mx) : 0.f;
+      z += pv[u];
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) z += __shfl_xor(z, off, 64);
+    const float inv = 1.0f / z;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) pv[u] *= inv;
+    if (a.aux_scale != 0.f) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int e = lane + 64 * u;
+        if (e < E) fp += pv[u] * (float)a.counts[e];
+      }
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) fp += __shfl_xor(fp, off, 64);
+    }
+  } else {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) pv[u] = 0.f;
+  }
+  // sigmoid gates: Z = sum of the selected sigmoids
+  float Zs = 0.f;
+  if (a.gating == MOE_GATE_SIGMOID_TOPK) {
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+      if (j < k) Zs += sigm(s_t[ev[j]]);
+  }
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int e = lane + 64 * u;
+    if (e >= E) continue;
+    // this expert's slot, if selected
+    int js = -1;
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+      if (j < k && ev[j] == e) js = j;
+    float dgs = 0.f, gs = 0.f;
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+      if (j == js) {
+        dgs = dgv[j];
+        gs = gv[j];
+      }
+    float ds = 0.f;
+    if (a.gating == MOE_GATE_SOFTMAX_TOPK) {
+      if (js >= 0) ds = gs * (dgs - A);
+    } else if (a.gating == MOE_GATE_SIGMOID_TOPK) {
+      if (js >= 0) {
+        const float sg = sigm(sv[u]);
+        ds = sg * (1.0f - sg) * (dgs - A) / Zs;
+      }
+    } else {
+      ds = pv[u] * ((js >= 0 ? dgs : 0.f) - A);
+    }
+    if (a.aux_scale != 0.f) ds += a.aux_scale * pv[u] * ((float)a.counts[e] - fp);
+    a.d_logits[t * E + e] = ds;
+  }
+}
+
+// ------------------------------------------------------------------ dx step
+// One wave per token, 8 columns per lane and step: the kept slots' dX rows in
+// slot order, then the shared experts', then the router term sum_e ds_e W_r[e]
+// (only the selected experts' when the score gradient is zero elsewhere).
+__global__ __launch_bounds__(256) void dx_kernel(DxArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= a.T) return;
+  const int d = a.d, k = a.k, E = a.E;
+  const float* ds = a.d_logits + t * E;
+  for (int c = lane; c < (d >> 3); c += 64) {
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < k; ++j) {
+      const int r = a.slot_pos[t * k + j];
+      if (r < 0) continue;
+      const u32x4_t v = *reinterpret_cast<const u32x4_t*>(a.dxp + (int64_t)r * d + c * 8);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        acc[2 * q] += bf16_to_f32(v[q] & 0xffffu);
+        acc[2 * q + 1] += bf16_to_f32(v[q] >> 16);
+      }
+    }
+    for (int s = 0; s < a.S; ++s) {
+      const u32x4_t v = *reinterpret_cast<const u32x4_t*>(a.dxs + ((int64_t)s * a.T + t) * d + c * 8);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        acc[2 * q] += bf16_to_f32(v[q] & 0xffffu);
+        acc[2 * q + 1] += bf16_to_f32(v[q] >> 16);
+      }
+    }
+    const int n_r = a.sparse_ds ? k : E;
+    for (int j = 0; j < n_r; ++j) {
+      const int e = a.sparse_ds ? a.topk_idx[t * k + j] : j;
+      const float w = ds[e];
+      const u32x4_t v = *reinterpret_cast<const u32x4_t*>(a.w_router + (int64_t)e * d + c * 8);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        acc[2 * q] += w * bf16_to_f32(v[q] & 0xffffu);
+        acc[2 * q + 1] += w * bf16_to_f32(v[q] >> 16);
+      }
+    }
+    u32x4_t o;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) o[q] = pack_bf16x2(acc[2 * q], acc[2 * q + 1]);
+    *reinterpret_cast<u32x4_t*>(a.dx + t * d + c * 8) = o;
+  }
+}
+
+// -------------------------------------------------------------- router dW_r
+// dW_r[e, i] = sum_t ds[t, e] x[t, i].  Workgroup (column block of 256, expert
+// block of 32, token chunk): thread i sums its column over the chunk's tokens
+// for 32 experts; the chunks are then added in order.
+constexpr int WR_EB = 32;
+__global__ __launch_bounds__(256) void wr_partial_kernel(WrArgs a) {
+  __shared__ float dsl[64][WR_EB];
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  const bool col_ok = i < a.d;
+  const int e0 = blockIdx.y * WR_EB;
+  const int64_t t0 = (int64_t)blockIdx.z * a.chunk;
+  const int64_t t1 = t0 + a.chunk < a.T ? t0 + a.chunk : a.T;
+  const int ne = a.E - e0 < WR_EB ? a.E - e0 : WR_EB;
+  float acc[WR_EB];
+#pragma unroll
+  for (int e = 0; e < WR_EB; ++e) acc[e] = 0.f;
+  for (int64_t tb = t0; tb < t1; tb += 64) {
+    __syncthreads();
+    for (int q = threadIdx.x; q < 64 * WR_EB; q += 256) {
+      const int tt = q / WR_EB, e = q % WR_EB;
+      dsl[tt][e] = (tb + tt < t1 && e < ne) ? a.d_logits[(tb + tt) * a.E + e0 + e] : 0.f;
+    }
+    __syncthreads();
+    const int nt = t1 - tb < 64 ? (int)(t1 - tb) : 64;
+    for (int tt = 0; tt < nt && col_ok; ++tt) {
+      const float xv = bf16_to_f32(a.x[(tb + tt) * a.d + i]);
+#pragma unroll
+      for (int e = 0; e < WR_EB; ++e) acc[e] += dsl[tt][e] * xv;
+    }
+  }
+  if (!col_ok) return;
+  float* out = a.partial + ((int64_t)blockIdx.z * a.E + e0) * a.d + i;
+  for (int e = 0; e < ne; ++e) out[(int64_t)e * a.d] = acc[e];
+}
+
+__global__ __launch_bounds__(256) void wr_reduce_kernel(WrArgs a, int nchunks) {
+  const int64_t n = (int64_t)a.E * a.d;
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= n) return;
+  float s = 0.f;
+  for (int c = 0; c < nchunks; ++c) s += a.partial[(int64_t)c * n + idx];
+  a.dw_router[idx] = s;
+}
+
+__global__ __launch_bounds__(256) void zero_kernel(uint32_t* p, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < n) p[i] = 0u;
+}
+
+int wr_chunk(int64_t T, int E, int d) {
+  // enough workgroups to cover the chip about four times over
+  const int64_t per = (int64_t)((d + 255) / 256) * ((E + WR_EB - 1) / WR_EB);
+  int64_t chunks = (4 * 256 + per - 1) / per;
+  if (chunks > (T + 63) / 64) chunks = (T + 63) / 64;
+  if (chunks < 1) chunks = 1;
+  int64_t c = (T + chunks - 1) / chunks;
+  c = (c + 63) / 64 * 64;
+  return (int)c;
+}
+
+}  // namespace
+
+size_t wr_ws_bytes(int64_t T, int E, int d) {
+  const int c = wr_chunk(T, E, d);
+  const int64_t nch = (T + c - 1) / c;
+  return (size_t)nch * E * d * 4;
+}
+
+int64_t bwd_dw_blocks(int G, int M, int N) {
+  return (int64_t)G * ((M + GB_BM - 1) / GB_BM) * ((N + GB_BN - 1) / GB_BN);
+}
+
+int bwd_tile_rows() { return GB_BM; }
+int bwd_tile_cols() { return GB_BN; }
+
+hipError_t launch_bwd_gemm(const BwdGemm& b, hipStream_t s) {
+  GemmArgs a;
+  memset(&a, 0, sizeof(a));
+  a.kind = b.kind;
+  a.P = static_cast<const uint16_t*>(b.P);
+  a.P2 = static_cast<const uint16_t*>(b.P2);
+  a.ldp = b.ldp;
+  a.p_seg = b.p_seg;
+  a.p_row_seg = b.p_row_seg;
+  a.Q = static_cast<const uint16_t*>(b.Q);
+  a.Q2 = static_cast<const uint16_t*>(b.Q2 ? b.Q2 : b.Q);
+  a.ldq = b.ldq;
+  a.q_row_seg = b.q_row_seg;
+  a.C = static_cast<uint16_t*>(b.C);
+  a.C2 = static_cast<uint16_t*>(b.C2);
+  a.ldc = b.ldc;
+  a.c_seg = b.c_seg;
+  a.c_row_seg = b.c_row_seg;
+  a.S1 = static_cast<const uint16_t*>(b.S1);
+  a.S2 = static_cast<const uint16_t*>(b.S2);
+  a.count = static_cast<const int32_t*>(b.plan);
+  a.plan = b.plan ? reinterpret_cast<const PlanEntry*>(static_cast<const char*>(b.plan) + kPlanHeader)
+                  : nullptr;
+  a.seg = b.seg;
+  a.dense_rows = b.dense_rows;
+  a.zero = static_cast<const uint16_t*>(b.zero);
+  a.K = b.K;
+  a.N = b.N;
+  a.M = b.M;
+  a.nk1 = b.K / BK;
+  a.G = b.G;
+  a.MT = (b.M + GB_BM - 1) / GB_BM;
+  a.NT = (b.N + GB_BN - 1) / GB_BN;
+  constexpr int TH = 64 * GB_NW;
+  unsigned grid;
+  if (b.kind == BG_DW) {
+    const int64_t V = (int64_t)a.G * a.MT * a.NT;
+    if (V == 0) return hipSuccess;
+    grid = (unsigned)V;
+    prof_before(b.name, s);
+    bwd_gemm_kernel<BG_DW, 0><<<grid, TH, 0, s>>>(a);
+  } else {
+    if (b.max_entries == 0) return hipSuccess;
+    grid = (unsigned)b.max_entries;
+    prof_before(b.name, s);
+    if (b.kind == BG_DX) {
+      if (b.epi == 1) bwd_gemm_kernel<BG_DX, 1><<<grid, TH, 0, s>>>(a);
+      else bwd_gemm_kernel<BG_DX, 0><<<grid, TH, 0, s>>>(a);
+    } else {
+      switch (b.epi) {
+        case 1: bwd_gemm_kernel<BG_DH, 1><<<grid, TH, 0, s>>>(a); break;
+        case 2: bwd_gemm_kernel<BG_DH, 2><<<grid, TH, 0, s>>>(a); break;
+        case 3: bwd_gemm_kernel<BG_DH, 3><<<grid, TH, 0, s>>>(a); break;
+        default: bwd_gemm_kernel<BG_DH, 0><<<grid, TH, 0, s>>>(a); break;
+      }
+    }
+  }
+  prof_after(s);
+  return hipGetLastError();
+}
+
+hipError_t launch_gate_bwd(const GateBwdArgs& a, hipStream_t s) {
+  if (a.T == 0) return hipSuccess;
+  prof_before("bwd_gate", s);
+  gate_bwd_kernel<<<(unsigned)((a.T + 3) / 4), 256, 0, s>>>(a);
+  prof_after(s);
+  return hipGetLastError();
+}
+
+hipError_t launch_dx(const DxArgs& a, hipStream_t s) {
+  if (a.T == 0) return hipSuccess;
+  prof_before("bwd_dx", s);
+  dx_kernel<<<(unsigned)((a.T + 3) / 4), 256, 0, s>>>(a);
+  prof_after(s);
+  return hipGetLastError();
+}
+
+hipError_t launch_router_bwd(const WrArgs& in, hipStream_t s) {
+  if (in.T == 0) return hipSuccess;
+  WrArgs a = in;
+  a.chunk = wr_chunk(a.T, a.E, a.d);
+  const int nch = (int)((a.T + a.chunk - 1) / a.chunk);
+  prof_before("bwd_router", s);
+  dim3 grid((a.d + 255) / 256, (a.E + WR_EB - 1) / WR_EB, nch);
+  wr_partial_kernel<<<grid, 256, 0, s>>>(a);
+  const int64_t n = (int64_t)a.E * a.d;
+  wr_reduce_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(a, nch);
+  prof_after(s);
+  return hipGetLastError();
+}
+
+hipError_t launch_zero(void* p, size_t bytes, hipStream_t s) {
+  const int64_t n = (int64_t)(bytes / 4);
+  if (n == 0) return hipSuccess;
+  zero_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(static_cast<uint32_t*>(p), n);
+  return hipGetLastError();
+}
+
+}  // namespace moe

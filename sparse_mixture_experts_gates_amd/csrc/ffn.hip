@@ -56,6 +56,8 @@ struct KArgs {
   int split;                       // K halves (plan entries carry the half)
   float* part;                     // split: fp32 partials [split][rows, N]
   int64_t part_stride;             // rows * N
+  uint16_t* save1;                 // SAVE: pre-activations (W1 x), laid out like C
+  uint16_t* save2;                 // SAVE, SwiGLU: W3 x
 };
 
 // A plan entry's column field: the column tile in the low 24 bits, the K
@@ -138,7 +140,7 @@ __device__ __forceinline__ float act1(float v) {
 // per 8 lanes.  Slab kt+NSTAGE-1 is requested while slab kt is multiplied;
 // one barrier per slab.
 template <int BM, int BN, int WM, int WN, int NSTAGE, int NSB, int MODE, bool PERSIST,
-          bool SPLIT = false>
+          bool SPLIT = false, bool SAVE = false>
 __global__ __launch_bounds__(64 * WM * WN)
 void ffn_bf16_kernel(KArgs a) {
   static_assert(!SPLIT || (MODE == MODE_PLAIN && NSTAGE == 2), "split: plain-mode 256 x 256 only");
@@ -443,12 +445,24 @@ void ffn_bf16_kernel(KArgs a) {
     for (int j = 0; j < JOUT; ++j) {
       float v[4];
       int col;
+      // training forward: keep the pre-activations for the backward pass
+      auto save = [&](uint16_t* dst, const f32x4_t& z) {
+        uint2 pz;
+        pz.x = pack_bf16x2(z[0], z[1]);
+        pz.y = pack_bf16x2(z[2], z[3]);
+        if (row_ok && col < N) *reinterpret_cast<uint2*>(dst + (crow0 + r) * (int64_t)N + col) = pz;
+      };
       if (MODE == MODE_SWIGLU) {
         col = n0 + wn * HALF + j * 16 + 4 * (lane >> 4);
+        if constexpr (SAVE) {
+          save(a.save1, acc[i][j]);
+          save(a.save2, acc[i][j + TN / 2]);
+        }
 #pragma unroll
         for (int q = 0; q < 4; ++q) v[q] = silu_f(acc[i][j][q]) * acc[i][j + TN / 2][q];
       } else {
         col = n0 + wn * BNW + j * 16 + 4 * (lane >> 4);
+        if constexpr (SAVE) save(a.save1, acc[i][j]);
 #pragma unroll
         for (int q = 0; q < 4; ++q) v[q] = act1<MODE>(acc[i][j][q]);
       }
@@ -584,6 +598,14 @@ int64_t max_entries(int64_t max_rows, int G, int N, Shape sh) {
 template <int BM, int BN, int WM, int WN, int NS, int NSB, bool PERSIST>
 void launch_bf16(int mode, unsigned grid, const KArgs& k, hipStream_t s) {
   constexpr int T = 64 * WM * WN;
+  if (k.save1) {   // training forward: the activation passes keep their pre-activations
+    switch (mode) {
+      case MODE_RELU: ffn_bf16_kernel<BM, BN, WM, WN, NS, NSB, MODE_RELU, PERSIST, false, true><<<grid, T, 0, s>>>(k); break;
+      case MODE_GELU: ffn_bf16_kernel<BM, BN, WM, WN, NS, NSB, MODE_GELU, PERSIST, false, true><<<grid, T, 0, s>>>(k); break;
+      default: ffn_bf16_kernel<BM, BN, WM, WN, NS, NSB, MODE_SWIGLU, PERSIST, false, true><<<grid, T, 0, s>>>(k); break;
+    }
+    return;
+  }
   switch (mode) {
     case MODE_PLAIN: ffn_bf16_kernel<BM, BN, WM, WN, NS, NSB, MODE_PLAIN, PERSIST><<<grid, T, 0, s>>>(k); break;
     case MODE_RELU: ffn_bf16_kernel<BM, BN, WM, WN, NS, NSB, MODE_RELU, PERSIST><<<grid, T, 0, s>>>(k); break;
@@ -650,6 +672,15 @@ bool ffn_plan_spec(const FfnPassArgs& p1, const FfnPassArgs& p2, PlanSpec* ps) {
   return true;
 }
 
+hipError_t launch_plan_kernel(const int32_t* seg, int G, int64_t dense_rows, const PlanSpec& ps,
+                              hipStream_t s) {
+  if (G > 1024) return hipErrorInvalidValue;
+  prof_before("plan", s);
+  ffn_plan_kernel<<<1, 1024, 0, s>>>(seg, G, dense_rows, ps);
+  prof_after(s);
+  return hipGetLastError();
+}
+
 hipError_t launch_ffn_plans(const FfnPassArgs& p1, const FfnPassArgs& p2, hipStream_t s) {
   PlanSpec ps;
   if (!ffn_plan_spec(p1, p2, &ps)) {
@@ -687,6 +718,11 @@ hipError_t launch_ffn_pass(const FfnPassArgs& p, hipStream_t s) {
   k.split = split;
   k.part = p.part;
   k.part_stride = p.max_rows * (int64_t)p.N;
+  k.save1 = static_cast<uint16_t*>(p.save1);
+  k.save2 = static_cast<uint16_t*>(p.save2);
+  if (k.save1 && (p.dtype != MOE_BF16 || p.mode == MODE_PLAIN || split > 1 ||
+                  (p.mode == MODE_SWIGLU && !k.save2)))
+    return hipErrorInvalidValue;
   const char* nm = p.seg_offsets ? (p.mode == MODE_PLAIN ? "ffn2" : "ffn1")
                                  : (p.mode == MODE_PLAIN ? "ffn2_shared" : "ffn1_shared");
   prof_before(nm, s);
@@ -702,6 +738,13 @@ hipError_t launch_ffn_pass(const FfnPassArgs& p, hipStream_t s) {
   } else if (sh.id == 4) {
     // plain / ReLU / GeLU only (a SwiGLU wave needs a pair of column tiles)
     constexpr int T4 = 64 * 4;
+    if (k.save1) {
+      if (p.mode == MODE_RELU) ffn_bf16_kernel<32, 64, 1, 4, 4, 4, MODE_RELU, false, false, true><<<(unsigned)grid, T4, 0, s>>>(k);
+      else if (p.mode == MODE_GELU) ffn_bf16_kernel<32, 64, 1, 4, 4, 4, MODE_GELU, false, false, true><<<(unsigned)grid, T4, 0, s>>>(k);
+      else return hipErrorInvalidValue;
+      prof_after(s);
+      return hipGetLastError();
+    }
     switch (p.mode) {
       case MODE_PLAIN: ffn_bf16_kernel<32, 64, 1, 4, 4, 4, MODE_PLAIN, false><<<(unsigned)grid, T4, 0, s>>>(k); break;
       case MODE_RELU: ffn_bf16_kernel<32, 64, 1, 4, 4, 4, MODE_RELU, false><<<(unsigned)grid, T4, 0, s>>>(k); break;

@@ -81,8 +81,16 @@ struct FfnPassArgs {
   bool small;             // small-batch (decode) tile shape
   int split;              // K parts (second GEMM only; 1 = none)
   float* part;            // split: fp32 partials [split][max_rows, N]
+  // first GEMM, training forward: the pre-activations in dtype, laid out like
+  // C -- SwiGLU: W1 x to save1 and W3 x to save2; ReLU / GeLU: W1 x to save1
+  void* save1;
+  void* save2;
 };
 size_t ffn_plan_bytes(int64_t max_rows, int G, int N, bool small, int dtype, int split = 1);
+// Plans of two passes with the same row tiles (ps.BM) over G segments (row
+// offsets seg[G+1], or G dense segments of dense_rows rows).
+hipError_t launch_plan_kernel(const int32_t* seg, int G, int64_t dense_rows, const PlanSpec& ps,
+                              hipStream_t s);
 // K parts (1 or 2) of a routed second GEMM pass of this shape.
 int ffn_split(int64_t max_rows, int G, int N, int K, bool small, int dtype);
 // For a split pass: C = bf16(sum of the fp32 parts) for all max_rows rows.
@@ -129,5 +137,88 @@ struct CombineArgs {
   int64_t part_stride;
 };
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
+
+// ------------------------------------------------------------ backward pass
+// Backward grouped GEMMs (bf16).  Output C[m, n] = sum_k P(n, k) Q(m, k):
+//  BG_DH  rows m of each expert's segment (plan), P = weights W2_e read as
+//         (n = d_ff column, k = d row), Q = dO rows (k contiguous); epilogue
+//         epi 0 plain, 1 ReLU', 2 GeLU', 3 SwiGLU (C = dG, C2 = dU from the
+//         saved S1 = W1 x, S2 = W3 x)
+//  BG_DX  rows m (plan), P = W1_e (+ W3_e as P2) read as (n = d column, k =
+//         d_ff row), Q = dG (+ dU as Q2); epi 1 = two operand pairs
+//  BG_DW  per segment g a full M x N output, k over the segment's rows:
+//         P(n, k) = P[(g p_row_seg + r0 + k) ldp + n], Q(m, k) likewise
+enum { BG_DH = 0, BG_DX = 1, BG_DW = 2 };
+struct BwdGemm {
+  int kind, epi;
+  const char* name;
+  const void* P;
+  const void* P2;
+  int64_t ldp, p_seg, p_row_seg;
+  const void* Q;
+  const void* Q2;
+  int64_t ldq, q_row_seg;
+  void* C;
+  void* C2;
+  int64_t ldc, c_seg, c_row_seg;
+  const void* S1;
+  const void* S2;
+  const void* plan;        // BG_DH / BG_DX: plan buffer (header + entries)
+  int64_t max_entries;     // grid of a plan-driven launch
+  const int32_t* seg;      // BG_DW: [G+1] row offsets or null (dense_rows each)
+  int64_t dense_rows;
+  const void* zero;        // BG_DW: >= 64 zero bf16 elements (16-byte aligned)
+  int K, N, M, G;
+};
+int bwd_tile_rows();
+int bwd_tile_cols();
+int64_t bwd_dw_blocks(int G, int M, int N);
+hipError_t launch_bwd_gemm(const BwdGemm& b, hipStream_t s);
+
+struct GateBwdArgs {
+  const uint16_t* dy;       // [T, d]
+  const uint16_t* eout;     // [T*k, d] expert outputs (bf16), or
+  const float* part;        // two fp32 K parts [2][T*k, d] (stride part_stride)
+  int64_t part_stride;
+  const int32_t* slot_pos;  // [T*k]
+  const int32_t* topk_idx;  // [T*k]
+  const float* gate;        // [T*k]
+  const float* logits;      // [T, E]
+  const int32_t* counts;    // [E] (balance loss)
+  float aux_scale;          // alpha E / T^2, 0 = no balance loss
+  uint16_t* d_out;          // [T*k, d] dO on the permuted rows
+  float* d_gate;            // [T, k] or null
+  float* d_logits;          // [T, E]
+  int64_t T;
+  int d, k, E, gating;
+};
+hipError_t launch_gate_bwd(const GateBwdArgs& a, hipStream_t s);
+
+struct DxArgs {
+  const uint16_t* dxp;      // [T*k, d] per permuted row
+  const uint16_t* dxs;      // [S, T, d] shared experts (S may be 0)
+  const int32_t* slot_pos;
+  const int32_t* topk_idx;
+  const float* d_logits;    // [T, E]
+  const uint16_t* w_router; // [E, d]
+  uint16_t* dx;             // [T, d]
+  int64_t T;
+  int d, k, E, S;
+  int sparse_ds;            // ds is zero outside the selected experts
+};
+hipError_t launch_dx(const DxArgs& a, hipStream_t s);
+
+struct WrArgs {
+  const float* d_logits;    // [T, E]
+  const uint16_t* x;        // [T, d]
+  float* dw_router;         // [E, d]
+  float* partial;           // workspace, wr_ws_bytes()
+  int64_t T;
+  int E, d;
+  int64_t chunk;            // set by the launcher
+};
+size_t wr_ws_bytes(int64_t T, int E, int d);
+hipError_t launch_router_bwd(const WrArgs& a, hipStream_t s);
+hipError_t launch_zero(void* p, size_t bytes, hipStream_t s);
 
 }  // namespace moe

@@ -12,6 +12,7 @@
 
 #include "common.h"
 #include "launch.h"
+#include "plan.h"
 
 namespace moe {
 
@@ -165,7 +166,75 @@ FwdWs fwd_ws(const moe_config_t* c, int64_t T) {
   return w;
 }
 
+// Training forward: the forward's workspace followed by what the backward
+// reads besides it (scores, gathered rows, pre-activations).
+struct TrainWs {
+  FwdWs fwd;
+  size_t logits, x_perm, save1, save2, ssave1, ssave2, total;
+};
+TrainWs train_ws(const moe_config_t* c, int64_t T) {
+  TrainWs w;
+  w.fwd = fwd_ws(c, T);
+  const int64_t R = T * c->top_k;
+  const int64_t ST = (int64_t)c->num_shared * T;
+  const bool glu = c->act == MOE_ACT_SWIGLU;
+  size_t o = w.fwd.total;
+  w.logits = o; o += up((size_t)T * c->num_experts * 4);
+  w.x_perm = o; o += up((size_t)R * c->d * 2);
+  w.save1 = o; o += up((size_t)R * c->d_ff * 2);
+  w.save2 = o; o += glu ? up((size_t)R * c->d_ff * 2) : 0;
+  w.ssave1 = o; o += up((size_t)ST * (ST ? c->d_ff_shared : 0) * 2);
+  w.ssave2 = o; o += up((size_t)ST * (ST ? c->d_ff_shared : 0) * 2);
+  w.total = o;
+  return w;
+}
+
+constexpr size_t kZeroBytes = 4096;
+
+int64_t bwd_entries(int64_t rows, int G, int N) {
+  const int BM = bwd_tile_rows(), BN = bwd_tile_cols();
+  int64_t mt = (rows + BM - 1) / BM + G;
+  if (mt > rows) mt = rows;
+  return mt * ((N + BN - 1) / BN);
+}
+size_t bwd_plan_bytes(int64_t rows, int G, int N) {
+  return up(kPlanHeader + 16 * (size_t)bwd_entries(rows, G, N));
+}
+
+struct BwdWs {
+  size_t zero, dO, dG, dU, dXp, dlogits, dGs, dUs, dXs, plan_h, plan_x, splan_h, splan_x, wr, total;
+};
+BwdWs bwd_ws(const moe_config_t* c, int64_t T) {
+  BwdWs w;
+  const int64_t R = T * c->top_k;
+  const int S = c->num_shared;
+  const int64_t ST = (int64_t)S * T;
+  const bool glu = c->act == MOE_ACT_SWIGLU;
+  size_t o = 0;
+  w.zero = o; o += kZeroBytes;
+  w.dO = o; o += up((size_t)R * c->d * 2);
+  w.dG = o; o += up((size_t)R * c->d_ff * 2);
+  w.dU = o; o += glu ? up((size_t)R * c->d_ff * 2) : 0;
+  w.dXp = o; o += up((size_t)R * c->d * 2);
+  w.dlogits = o; o += up((size_t)T * c->num_experts * 4);
+  w.dGs = o; o += up((size_t)ST * (S ? c->d_ff_shared : 0) * 2);
+  w.dUs = o; o += up((size_t)ST * (S ? c->d_ff_shared : 0) * 2);
+  w.dXs = o; o += up((size_t)ST * c->d * 2);
+  w.plan_h = o; o += bwd_plan_bytes(R, c->num_experts, c->d_ff);
+  w.plan_x = o; o += bwd_plan_bytes(R, c->num_experts, c->d);
+  w.splan_h = w.splan_x = o;
+  if (S) {
+    o += bwd_plan_bytes(ST, S, c->d_ff_shared);
+    w.splan_x = o;
+    o += bwd_plan_bytes(ST, S, c->d);
+  }
+  w.wr = o; o += up(wr_ws_bytes(T, c->num_experts, c->d));
+  w.total = o;
+  return w;
+}
+
 char* at(void* base, size_t off) { return static_cast<char*>(base) + off; }
+const char* at(const void* base, size_t off) { return static_cast<const char*>(base) + off; }
 
 moe_status_t hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
 
@@ -216,7 +285,8 @@ struct FfnPasses {
 FfnPasses ffn_passes(const moe_config_t* c, int64_t T, const void* x, const void* x_perm,
                      const int32_t* perm_src, const int32_t* offsets, const void* w1,
                      const void* w3, const void* w2, const void* ws1, const void* ws3,
-                     const void* ws2, void* eout, void* sout, void* ws) {
+                     const void* ws2, void* eout, void* sout, void* ws,
+                     const TrainWs* train = nullptr, void* saved = nullptr) {
   const FfnWs w = ffn_ws(c, T);
   const int64_t R = T * c->top_k;
   const int mode1 = c->act == MOE_ACT_SWIGLU ? 3 : (c->act == MOE_ACT_GELU ? 2 : 1);
@@ -238,6 +308,10 @@ FfnPasses ffn_passes(const moe_config_t* c, int64_t T, const void* x, const void
   p.plan = at(ws, w.plan1);
   p.max_rows = R;
   p.small = small_batch(R);
+  if (train) {
+    p.save1 = at(saved, train->save1);
+    p.save2 = c->act == MOE_ACT_SWIGLU ? at(saved, train->save2) : nullptr;
+  }
   FfnPassArgs& p2 = f.p2;
   p2 = p;
   p2.A = at(ws, w.H);
@@ -249,6 +323,7 @@ FfnPasses ffn_passes(const moe_config_t* c, int64_t T, const void* x, const void
   p2.N = c->d;
   p2.mode = 0;
   p2.plan = at(ws, w.plan2);
+  p2.save1 = p2.save2 = nullptr;
   p2.split = w.split;
   p2.part = w.split > 1 ? reinterpret_cast<float*>(at(ws, w.part)) : nullptr;
   f.shared = c->num_shared > 0;
@@ -271,6 +346,10 @@ FfnPasses ffn_passes(const moe_config_t* c, int64_t T, const void* x, const void
     q.plan = at(ws, w.plan3);
     q.max_rows = (int64_t)S * T;
     q.small = small_batch(T);
+    if (train) {
+      q.save1 = at(saved, train->ssave1);
+      q.save2 = at(saved, train->ssave2);
+    }
     FfnPassArgs& q2 = f.q2;
     q2 = q;
     q2.A = at(ws, w.Hs);
@@ -284,6 +363,7 @@ FfnPasses ffn_passes(const moe_config_t* c, int64_t T, const void* x, const void
     q2.plan = at(ws, w.plan4);
     q2.split = 1;
     q2.part = nullptr;
+    q2.save1 = q2.save2 = nullptr;
   }
   return f;
 }
@@ -566,6 +646,319 @@ moe_status_t moe_routing_stats(const moe_config_t* cfg, int64_t T, const float* 
   a.E = cfg->num_experts;
   a.k = cfg->top_k;
   return hip_status(launch_stats(a, static_cast<hipStream_t>(stream)));
+}
+
+
+moe_status_t moe_train_workspace_size(const moe_config_t* cfg, int64_t T, size_t* bytes) {
+  moe_status_t st = check_cfg(cfg, T);
+  if (st != MOE_OK) return st;
+  if (!bytes) return MOE_ERR_INVALID_ARG;
+  if (cfg->dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  *bytes = train_ws(cfg, T).total;
+  return MOE_OK;
+}
+
+moe_status_t moe_forward_train(const moe_config_t* cfg, int64_t T, const void* x,
+                               const void* w_router, const float* logit_offset,
+                               const float* select_bias, const void* w1, const void* w3,
+                               const void* w2, const void* ws1, const void* ws3, const void* ws2,
+                               void* y, void* saved, size_t saved_bytes, void* stream) {
+  moe_status_t st = check_cfg(cfg, T);
+  if (st != MOE_OK) return st;
+  if (cfg->dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  if (T == 0) return MOE_OK;
+  if (!x || !w_router || !w1 || !w2 || !y) return MOE_ERR_INVALID_ARG;
+  if (cfg->act == MOE_ACT_SWIGLU && !w3) return MOE_ERR_INVALID_ARG;
+  if (cfg->num_shared > 0 && (!ws1 || !ws3 || !ws2)) return MOE_ERR_INVALID_ARG;
+  const void* p16[] = {x, w_router, w1, w2, y, w3, ws1, ws3, ws2};
+  for (const void* p : p16)
+    if (p && !al(p, 16)) return MOE_ERR_INVALID_ARG;
+  if ((logit_offset && !al(logit_offset, 4)) || (select_bias && !al(select_bias, 4)))
+    return MOE_ERR_INVALID_ARG;
+  if (!saved || !al(saved, ALIGN)) return MOE_ERR_INVALID_ARG;
+  const TrainWs tw = train_ws(cfg, T);
+  if (saved_bytes < tw.total) return MOE_ERR_WORKSPACE;
+  const FwdWs& w = tw.fwd;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int32_t* idx = reinterpret_cast<int32_t*>(at(saved, w.idx));
+  float* gate = reinterpret_cast<float*>(at(saved, w.gate));
+  int32_t* counts = reinterpret_cast<int32_t*>(at(saved, w.counts));
+  int32_t* dropped = reinterpret_cast<int32_t*>(at(saved, w.dropped));
+  int32_t* offsets = reinterpret_cast<int32_t*>(at(saved, w.offsets));
+  int32_t* perm_src = reinterpret_cast<int32_t*>(at(saved, w.perm_src));
+  int32_t* slot_pos = reinterpret_cast<int32_t*>(at(saved, w.slot_pos));
+  float* logits = reinterpret_cast<float*>(at(saved, tw.logits));
+  void* x_perm = at(saved, tw.x_perm);
+  void* eout = at(saved, w.eout);
+  void* sout = cfg->num_shared > 0 ? at(saved, w.sout) : nullptr;
+  st = do_route(cfg, T, x, w_router, logit_offset, select_bias, logits, idx, gate,
+                route_ws_bytes(T, cfg->num_experts, cfg->dtype) ? at(saved, w.route) : nullptr, s);
+  if (st != MOE_OK) return st;
+  // the rows are gathered once (the weight gradients read them again)
+  const FfnPasses passes = ffn_passes(cfg, T, x, x_perm, perm_src, offsets, w1, w3, w2, ws1, ws3,
+                                      ws2, eout, sout, at(saved, w.ffn), &tw, saved);
+  PlanSpec spec;
+  const bool have_spec = ffn_plan_spec(passes.p, passes.p2, &spec);
+  bool built = false;
+  st = do_permute(cfg, T, idx, x, counts, offsets, perm_src, slot_pos, dropped, x_perm,
+                  at(saved, w.perm), s, have_spec ? &spec : nullptr, &built);
+  if (st != MOE_OK) return st;
+  st = run_ffn(passes, built, s);
+  if (st != MOE_OK) return st;
+  if (passes.p2.split > 1)
+    return do_combine(cfg, T, eout, slot_pos, gate, sout, y, s, passes.p2.part,
+                      passes.p2.max_rows * (int64_t)passes.p2.N);
+  return do_combine(cfg, T, eout, slot_pos, gate, sout, y, s);
+}
+
+moe_status_t moe_saved_routing(const moe_config_t* cfg, int64_t T, void* saved,
+                               float** logits, int32_t** topk_idx, float** topk_gate,
+                               int32_t** expert_counts, int32_t** num_dropped,
+                               int32_t** expert_offsets, int32_t** slot_pos) {
+  moe_status_t st = check_cfg(cfg, T);
+  if (st != MOE_OK) return st;
+  if (cfg->dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  if (!saved) return MOE_ERR_INVALID_ARG;
+  const TrainWs tw = train_ws(cfg, T);
+  if (logits) *logits = reinterpret_cast<float*>(at(saved, tw.logits));
+  if (topk_idx) *topk_idx = reinterpret_cast<int32_t*>(at(saved, tw.fwd.idx));
+  if (topk_gate) *topk_gate = reinterpret_cast<float*>(at(saved, tw.fwd.gate));
+  if (expert_counts) *expert_counts = reinterpret_cast<int32_t*>(at(saved, tw.fwd.counts));
+  if (num_dropped) *num_dropped = reinterpret_cast<int32_t*>(at(saved, tw.fwd.dropped));
+  if (expert_offsets) *expert_offsets = reinterpret_cast<int32_t*>(at(saved, tw.fwd.offsets));
+  if (slot_pos) *slot_pos = reinterpret_cast<int32_t*>(at(saved, tw.fwd.slot_pos));
+  return MOE_OK;
+}
+
+moe_status_t moe_backward_workspace_size(const moe_config_t* cfg, int64_t T, size_t* bytes) {
+  moe_status_t st = check_cfg(cfg, T);
+  if (st != MOE_OK) return st;
+  if (!bytes) return MOE_ERR_INVALID_ARG;
+  if (cfg->dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  *bytes = bwd_ws(cfg, T).total;
+  return MOE_OK;
+}
+
+moe_status_t moe_backward(const moe_config_t* cfg, int64_t T, const void* x, const void* w_router,
+                          const void* w1, const void* w3, const void* w2, const void* ws1,
+                          const void* ws3, const void* ws2, const void* saved, size_t saved_bytes,
+                          const void* dy, float aux_alpha, void* dx, float* dw_router, void* dw1,
+                          void* dw3, void* dw2, void* dws1, void* dws3, void* dws2,
+                          float* d_gate, float* d_logits, void* workspace, size_t ws_bytes,
+                          void* stream) {
+  moe_status_t st = check_cfg(cfg, T);
+  if (st != MOE_OK) return st;
+  if (cfg->dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  if (!(aux_alpha >= 0.f) || isinf(aux_alpha)) return MOE_ERR_INVALID_ARG;
+  if (T == 0) return MOE_OK;
+  const bool glu = cfg->act == MOE_ACT_SWIGLU;
+  const int S = cfg->num_shared;
+  if (!x || !w_router || !w1 || !w2 || !saved || !dy || !dx || !dw_router || !dw1 || !dw2)
+    return MOE_ERR_INVALID_ARG;
+  if (glu && (!w3 || !dw3)) return MOE_ERR_INVALID_ARG;
+  if (S > 0 && (!ws1 || !ws3 || !ws2 || !dws1 || !dws3 || !dws2)) return MOE_ERR_INVALID_ARG;
+  const void* p16[] = {x, w_router, w1, w2, w3, ws1, ws3, ws2, dy, dx, dw_router, dw1, dw3, dw2,
+                       dws1, dws3, dws2};
+  for (const void* p : p16)
+    if (p && !al(p, 16)) return MOE_ERR_INVALID_ARG;
+  if ((d_gate && !al(d_gate, 4)) || (d_logits && !al(d_logits, 4))) return MOE_ERR_INVALID_ARG;
+  if (!al(saved, ALIGN) || !workspace || !al(workspace, ALIGN)) return MOE_ERR_INVALID_ARG;
+  const TrainWs tw = train_ws(cfg, T);
+  const BwdWs bw = bwd_ws(cfg, T);
+  if (saved_bytes < tw.total || ws_bytes < bw.total) return MOE_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int64_t R = T * cfg->top_k;
+  const int E = cfg->num_experts, d = cfg->d, dff = cfg->d_ff, dffs = cfg->d_ff_shared;
+  const FwdWs& fw = tw.fwd;
+  const FfnWs ffw = ffn_ws(cfg, T);
+  const char* fbase = at(saved, fw.ffn);
+  const int32_t* offsets = reinterpret_cast<const int32_t*>(at(saved, fw.offsets));
+  const int32_t* slot_pos = reinterpret_cast<const int32_t*>(at(saved, fw.slot_pos));
+  const int32_t* idx = reinterpret_cast<const int32_t*>(at(saved, fw.idx));
+  float* dlog = d_logits ? d_logits : reinterpret_cast<float*>(at(workspace, bw.dlogits));
+  void* zero = at(workspace, bw.zero);
+  void* dO = at(workspace, bw.dO);
+  void* dG = at(workspace, bw.dG);
+  void* dU = glu ? at(workspace, bw.dU) : nullptr;
+  void* dXp = at(workspace, bw.dXp);
+  if (launch_zero(zero, kZeroBytes, s) != hipSuccess) return MOE_ERR_HIP;
+
+  // gates: dO, dg, ds
+  GateBwdArgs ga;
+  memset(&ga, 0, sizeof(ga));
+  ga.dy = static_cast<const uint16_t*>(dy);
+  if (ffw.split > 1) {
+    ga.part = reinterpret_cast<const float*>(fbase + ffw.part);
+    ga.part_stride = R * (int64_t)d;
+  } else {
+    ga.eout = reinterpret_cast<const uint16_t*>(at(saved, fw.eout));
+  }
+  ga.slot_pos = slot_pos;
+  ga.topk_idx = idx;
+  ga.gate = reinterpret_cast<const float*>(at(saved, fw.gate));
+  ga.logits = reinterpret_cast<const float*>(at(saved, tw.logits));
+  ga.counts = reinterpret_cast<const int32_t*>(at(saved, fw.counts));
+  ga.aux_scale = (float)((double)aux_alpha * E / ((double)T * (double)T));
+  ga.d_out = static_cast<uint16_t*>(dO);
+  ga.d_gate = d_gate;
+  ga.d_logits = dlog;
+  ga.T = T;
+  ga.d = d;
+  ga.k = cfg->top_k;
+  ga.E = E;
+  ga.gating = cfg->gating;
+  if (launch_gate_bwd(ga, s) != hipSuccess) return MOE_ERR_HIP;
+
+  const int epi = glu ? 3 : (cfg->act == MOE_ACT_GELU ? 2 : 1);
+  auto run_expert_grads = [&](bool shared) -> moe_status_t {
+    // one set of experts: routed (segments = expert rows) or shared (dense)
+    const int G = shared ? S : E;
+    const int64_t rows = shared ? (int64_t)S * T : R;
+    const int f = shared ? dffs : dff;
+    const int32_t* seg = shared ? nullptr : offsets;
+    void* plan_h = at(workspace, shared ? bw.splan_h : bw.plan_h);
+    void* plan_x = at(workspace, shared ? bw.splan_x : bw.plan_x);
+    PlanSpec ps;
+    ps.BM = bwd_tile_rows();
+    ps.NT = (f + bwd_tile_cols() - 1) / bwd_tile_cols();
+    ps.NT2 = (d + bwd_tile_cols() - 1) / bwd_tile_cols();
+    ps.S2 = 1;
+    ps.plan = static_cast<int32_t*>(plan_h);
+    ps.plan2 = static_cast<int32_t*>(plan_x);
+    if (launch_plan_kernel(seg, G, T, ps, s) != hipSuccess) return MOE_ERR_HIP;
+    const void* Gsv = shared ? at(saved, tw.ssave1) : at(saved, tw.save1);
+    const void* Usv = shared ? at(saved, tw.ssave2) : (glu ? at(saved, tw.save2) : nullptr);
+    const void* Hin = shared ? fbase + ffw.Hs : fbase + ffw.H;
+    void* gG = shared ? at(workspace, bw.dGs) : dG;
+    void* gU = shared ? at(workspace, bw.dUs) : dU;
+    void* gX = shared ? at(workspace, bw.dXs) : dXp;
+    const void* gO = shared ? dy : dO;
+    const void* Xin = shared ? x : at(saved, tw.x_perm);
+    const int e1 = shared ? 3 : epi;
+    const bool g2 = shared || glu;
+    BwdGemm b;
+    // dH = dO . W2 -> dG, dU (or dZ)
+    memset(&b, 0, sizeof(b));
+    b.kind = BG_DH;
+    b.epi = e1;
+    b.name = shared ? "bwd_dh_shared" : "bwd_dh";
+    b.P = shared ? ws2 : w2;
+    b.ldp = f;
+    b.p_seg = (int64_t)d * f;
+    b.Q = gO;
+    b.ldq = d;
+    b.q_row_seg = 0;
+    b.C = gG;
+    b.C2 = gU;
+    b.ldc = f;
+    b.c_row_seg = shared ? T : 0;
+    b.S1 = Gsv;
+    b.S2 = Usv;
+    b.plan = plan_h;
+    b.max_entries = bwd_entries(rows, G, f);
+    b.K = d;
+    b.N = f;
+    b.G = G;
+    if (launch_bwd_gemm(b, s) != hipSuccess) return MOE_ERR_HIP;
+    // dW2 = dO^T H
+    memset(&b, 0, sizeof(b));
+    b.kind = BG_DW;
+    b.name = shared ? "bwd_dw2_shared" : "bwd_dw2";
+    b.P = Hin;
+    b.ldp = f;
+    b.p_row_seg = shared ? T : 0;
+    b.Q = gO;
+    b.ldq = d;
+    b.q_row_seg = 0;
+    b.C = shared ? dws2 : dw2;
+    b.ldc = f;
+    b.c_seg = (int64_t)d * f;
+    b.seg = seg;
+    b.dense_rows = T;
+    b.zero = zero;
+    b.M = d;
+    b.N = f;
+    b.G = G;
+    if (launch_bwd_gemm(b, s) != hipSuccess) return MOE_ERR_HIP;
+    // dX = dG . W1 (+ dU . W3)
+    memset(&b, 0, sizeof(b));
+    b.kind = BG_DX;
+    b.epi = g2 ? 1 : 0;
+    b.name = shared ? "bwd_dx_shared" : "bwd_dx";
+    b.P = shared ? ws1 : w1;
+    b.P2 = g2 ? (shared ? ws3 : w3) : nullptr;
+    b.ldp = d;
+    b.p_seg = (int64_t)f * d;
+    b.Q = gG;
+    b.Q2 = g2 ? gU : nullptr;
+    b.ldq = f;
+    b.q_row_seg = shared ? T : 0;
+    b.C = gX;
+    b.ldc = d;
+    b.c_row_seg = shared ? T : 0;
+    b.plan = plan_x;
+    b.max_entries = bwd_entries(rows, G, d);
+    b.K = f;
+    b.N = d;
+    b.G = G;
+    if (launch_bwd_gemm(b, s) != hipSuccess) return MOE_ERR_HIP;
+    // dW1 = dG^T X, dW3 = dU^T X
+    for (int u = 0; u < (g2 ? 2 : 1); ++u) {
+      memset(&b, 0, sizeof(b));
+      b.kind = BG_DW;
+      b.name = shared ? (u ? "bwd_dw3_shared" : "bwd_dw1_shared") : (u ? "bwd_dw3" : "bwd_dw1");
+      b.P = Xin;
+      b.ldp = d;
+      b.p_row_seg = 0;
+      b.Q = u ? gU : gG;
+      b.ldq = f;
+      b.q_row_seg = shared ? T : 0;
+      b.C = shared ? (u ? dws3 : dws1) : (u ? dw3 : dw1);
+      b.ldc = d;
+      b.c_seg = (int64_t)f * d;
+      b.seg = seg;
+      b.dense_rows = T;
+      b.zero = zero;
+      b.M = f;
+      b.N = d;
+      b.G = G;
+      if (launch_bwd_gemm(b, s) != hipSuccess) return MOE_ERR_HIP;
+    }
+    return MOE_OK;
+  };
+  st = run_expert_grads(false);
+  if (st != MOE_OK) return st;
+  if (S > 0) {
+    st = run_expert_grads(true);
+    if (st != MOE_OK) return st;
+  }
+
+  DxArgs xa;
+  xa.dxp = static_cast<const uint16_t*>(dXp);
+  xa.dxs = S > 0 ? reinterpret_cast<const uint16_t*>(at(workspace, bw.dXs)) : nullptr;
+  xa.slot_pos = slot_pos;
+  xa.topk_idx = idx;
+  xa.d_logits = dlog;
+  xa.w_router = static_cast<const uint16_t*>(w_router);
+  xa.dx = static_cast<uint16_t*>(dx);
+  xa.T = T;
+  xa.d = d;
+  xa.k = cfg->top_k;
+  xa.E = E;
+  xa.S = S;
+  xa.sparse_ds = cfg->gating != MOE_GATE_SOFTMAX_FULL && aux_alpha == 0.f;
+  if (launch_dx(xa, s) != hipSuccess) return MOE_ERR_HIP;
+
+  WrArgs wa;
+  wa.d_logits = dlog;
+  wa.x = static_cast<const uint16_t*>(x);
+  wa.dw_router = dw_router;
+  wa.partial = reinterpret_cast<float*>(at(workspace, bw.wr));
+  wa.T = T;
+  wa.E = E;
+  wa.d = d;
+  wa.chunk = 0;
+  return hip_status(launch_router_bwd(wa, s));
 }
 
 }  // extern "C"

@@ -18,6 +18,8 @@ Recipe (one line per tensor; "N(0, v)" names the variance v):
   o_e = -s ln(e+1) (a Zipf(s) prior on the scores; the normaliser is a uniform
   shift and is left out).
 * ``bias_normal`` draws the selection-only balancing bias b ~ N(0, v).
+* backward pass: the output gradient dy [T, d] ~ N(0, 1) in the layer dtype
+  (``make_output_grad``), standing in for the gradient a loss would send back.
 
 Named workloads follow the layer shapes used for measurement: a toy fp32
 layer, a Switch-style top-1 layer with capacity, a Mixtral-shape layer, a
@@ -35,6 +37,7 @@ import torch
 
 TAG_X, TAG_WR, TAG_W1, TAG_W3, TAG_W2 = 1, 2, 3, 4, 5
 TAG_OFFSET, TAG_BIAS, TAG_WS1, TAG_WS3, TAG_WS2, TAG_X_DECODE = 6, 7, 8, 9, 10, 11
+TAG_DY = 12
 
 
 @dataclass(frozen=True)
@@ -146,3 +149,8 @@ def make_inputs(w: Workload, device="cpu", with_weights=True):
         b = _normal((w.E,), p, TAG_BIAS, w, device, torch.float32)
     inp["select_bias"] = b
     return inp
+
+
+def make_output_grad(w: Workload, device="cpu"):
+    """The output gradient dy [T, d] of workload ``w`` (N(0, 1), layer dtype)."""
+    return _normal((w.T, w.d), 1.0, TAG_DY, w, device, w.torch_dtype)

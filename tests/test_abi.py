@@ -141,3 +141,58 @@ def test_binding_refuses_host_tensors():
     with pytest.raises(ValueError):
         B.route(c, torch.zeros((4, 256), dtype=torch.bfloat16),
                 torch.zeros((8, 256), dtype=torch.bfloat16))
+
+
+def test_training_entry_points_reject_bad_arguments_before_any_gpu_work():
+    L = B.lib()
+    c = cfg()
+    by = ctypes.byref
+    p = ctypes.c_void_p(1 << 20)      # 256-byte aligned, never dereferenced
+    n = None
+    f32 = ctypes.c_float
+    big = 1 << 40
+    c32 = cfg(dtype="f32")
+    ft = L.moe_forward_train
+    assert ft(by(c32), 10, p, p, n, n, p, p, p, n, n, n, p, p, big, n) == 2   # bf16 only
+    assert ft(by(c), 10, p, p, n, n, p, n, p, n, n, n, p, p, big, n) == 1     # SwiGLU needs w3
+    assert ft(by(c), 10, p, p, n, n, p, p, p, n, n, n, p, n, big, n) == 1     # saved buffer
+    assert ft(by(c), 10, p, p, n, n, p, p, p, n, n, n, p, p, 16, n) == 3      # saved too small
+    assert ft(by(c), 0, n, n, n, n, n, n, n, n, n, n, n, n, 0, n) == 0
+
+    def bw(T=10, saved_bytes=big, aux=0.0, dw3=p, ws_bytes=big, cfg_=c):
+        # x, w_router, w1, w3, w2, ws1, ws3, ws2, saved, saved_bytes, dy, aux,
+        # dx, dw_router, dw1, dw3, dw2, dws1, dws3, dws2, d_gate, d_logits,
+        # workspace, ws_bytes, stream
+        return L.moe_backward(by(cfg_), T, p, p, p, p, p, n, n, n, p, saved_bytes, p, f32(aux),
+                              p, p, p, dw3, p, n, n, n, n, n, p, ws_bytes, n)
+    assert bw(cfg_=c32) == 2
+    assert bw(aux=-1.0) == 1
+    assert bw(aux=float("nan")) == 1
+    assert bw(aux=float("inf")) == 1
+    assert bw(dw3=None) == 1
+    assert bw(saved_bytes=16) == 3
+    assert bw(ws_bytes=16) == 3
+    assert L.moe_backward(by(c), 0, *([n] * 9), 0, n, f32(0), *([n] * 10), n, 0, n) == 0
+    sh = cfg(num_shared=1, d_ff_shared=128)
+    assert bw(cfg_=sh) == 1                     # shared experts need their weights and grads
+
+
+def test_training_sizes_and_saved_views_on_host():
+    c = cfg()
+    T = 1000
+    tr = B.train_workspace_size(c, T)
+    assert tr > B.workspace_size(c, T)
+    assert B.backward_workspace_size(c, T) > 0
+    with pytest.raises(B.MoeError):
+        B.train_workspace_size(cfg(dtype="f32"), T)
+    L = B.lib()
+    base = 1 << 30
+    ptrs = [ctypes.c_void_p() for _ in range(7)]
+    assert L.moe_saved_routing(ctypes.byref(c), T, ctypes.c_void_p(base),
+                               *[ctypes.byref(q) for q in ptrs]) == 0
+    offs = [q.value - base for q in ptrs]
+    sizes = [T * 8 * 4, T * 2 * 4, T * 2 * 4, 8 * 4, 4, 9 * 4, T * 2 * 4]
+    spans = sorted(zip(offs, sizes))
+    for (o, s_), (o2, _) in zip(spans, spans[1:]):
+        assert 0 <= o and o + s_ <= o2          # disjoint, inside the buffer
+    assert spans[-1][0] + spans[-1][1] <= tr
