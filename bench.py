@@ -7,6 +7,7 @@ gate-weighted combine.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                     [--no-cpu-baseline] [--graph] [--cold-runs N] [--copy-calib MiB]
+                    [--no-backward]
 
 Prints one JSON line.  `value` is tokens/s of the whole layer over K
 back-to-back steps; `roofline` reports the dominant kernel (the first grouped
@@ -14,8 +15,9 @@ GEMM) against the bf16 MFMA peak (HBM peak for a decode batch), timed with HIP
 events recorded by the library around each of its launches inside a second
 timed region; `cold` times N single steps each after a 1 GiB write that
 evicts L2 and the Infinity Cache; `next_rows` times the routing statistics
-call; `cpu_baseline` times the CPU oracle on a bounded token sample of the
-same workload.
+call and the training step (moe_forward_train + moe_backward, per kernel);
+`cpu_baseline` times the CPU oracle on a bounded token sample of the same
+workload.
 """
 
 from __future__ import annotations
@@ -135,6 +137,78 @@ def cpu_baseline(w, inp, flops_per_token, budget_s=15.0):
                       f"forward (all routed experts touched by them), {dt:.1f} s"}
 
 
+def backward_work(w, counts):
+    """Algorithmic FLOPs of one backward pass: per kept routed row, each
+    expert matrix is used twice more (input gradient and weight gradient),
+    2 * n_mat * 2 d d_ff; the shared experts likewise over all tokens; the
+    router 2 * 2 T d E (dW_r and its dx term).  The dominant GEMMs: dX and the
+    dW of W1 (and W3)."""
+    n_mat = 3 if w.act == "swiglu" else 2
+    kept = int(sum(counts))
+    per = 2 * w.d * w.d_ff
+    f = {"bwd_dh": kept * per, "bwd_dw2": kept * per, "bwd_dx": kept * (n_mat - 1) * per,
+         "bwd_dw1": kept * per}
+    if n_mat == 3:
+        f["bwd_dw3"] = kept * per
+    shared = w.num_shared * 2 * 3 * 2 * w.T * w.d * w.d_ff_shared
+    total = sum(f.values()) + shared + 4 * w.T * w.d * w.E
+    return total, f
+
+
+def measure_backward(B, w, inp, cfg, counts, steps, warmup):
+    """Training step of the layer: moe_forward_train, then moe_backward on a
+    seeded output gradient; both timed over `steps` back-to-back calls, then
+    per kernel with the library's HIP events."""
+    import torch
+    from sparse_mixture_experts_gates_amd.workloads import make_output_grad
+    dy = make_output_grad(w, "cuda:0")
+    y, saved = B.forward_train_inputs(cfg, inp)
+    g = B.backward(cfg, inp["x"], inp["w_router"], inp["w1"], inp["w2"], inp["w3"], saved, dy,
+                   ws1=inp["ws1"], ws3=inp["ws3"], ws2=inp["ws2"])
+    bws = torch.empty(B.backward_workspace_size(cfg, w.T), dtype=torch.uint8, device="cuda:0")
+
+    def fwd():
+        B.forward_train_inputs(cfg, inp, saved=saved, y=y)
+
+    def bwd():
+        B.backward(cfg, inp["x"], inp["w_router"], inp["w1"], inp["w2"], inp["w3"], saved, dy,
+                   ws1=inp["ws1"], ws3=inp["ws3"], ws2=inp["ws2"], ws=bws, grads=g)
+
+    for _ in range(warmup):
+        fwd()
+        bwd()
+    torch.cuda.synchronize()
+    out = {}
+    for name, fn in (("forward_train", fwd), ("backward", bwd)):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        out[name + "_ms"] = e0.elapsed_time(e1) / steps
+    B.profile_enable(True)
+    for _ in range(steps):
+        bwd()
+    torch.cuda.synchronize()
+    prof = B.profile_read()
+    B.profile_enable(False)
+    kern = {k: v[0] / max(v[1], 1) for k, v in prof.items()}
+    total, per = backward_work(w, counts)
+    out["tflops"] = total / (out["backward_ms"] * 1e-3) / 1e12
+    out["frac_of_bf16_peak"] = out["tflops"] / PEAK_BF16_TFLOPS
+    out["step_tokens_per_s"] = w.T / ((out["forward_train_ms"] + out["backward_ms"]) * 1e-3)
+    out["kernels_ms"] = {k: round(v, 5) for k, v in sorted(kern.items())}
+    gemms = {}
+    for k, fl in per.items():
+        if k in kern and kern[k] > 0:
+            tf = fl / (kern[k] * 1e-3) / 1e12
+            gemms[k] = {"ms": kern[k], "tflops": tf, "frac": tf / PEAK_BF16_TFLOPS}
+    out["gemms"] = gemms
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -147,6 +221,8 @@ def main():
     ap.add_argument("--cold-runs", type=int, default=20,
                     help="extra single-step runs, each after writing 1 GiB to flush L2 and "
                          "the Infinity Cache (median / min / p90 reported; 0 = skip)")
+    ap.add_argument("--no-backward", action="store_true",
+                    help="skip the training-step measurement (forward_train + backward)")
     ap.add_argument("--copy-calib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -336,6 +412,9 @@ def main():
         "next_rows": next_rows,
         "cold": cold,
     }
+    if w.dtype == "bf16" and not args.no_backward:
+        next_rows["backward"] = measure_backward(B, w, inp, cfg, kept_counts, args.steps,
+                                                 args.warmup)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, inp, work["flops"] / w.T)
     print(json.dumps(res), flush=True)
