@@ -163,67 +163,68 @@ __global__ __launch_bounds__(64 * GB_NW) void bwd_gemm_kernel(GemmArgs a) {
   const int N = a.N;
 
   // Per-lane load sources.  P: DP instructions of 8 lines; Q: DQ instructions
-  // (8 rows of 64 k, or 8 lines of an MN-major tile).
-  int p_k[DP], p_col[DP];
+  // (8 rows of 64 k, or 8 lines of an MN-major tile).  Instruction i of a
+  // wave fills lines L = (wave + i NW) 8 + lane/8, i.e. k-row k0 + i KSTEP and
+  // line lane/8 % NL of it: the column and the chunk swizzle (k & 3) are the
+  // same for every i.
+  static_assert(8 % NLP == 0 && 8 % NLQ == 0, "lines per k-row");
+  constexpr int KSP = NW * 8 / NLP, KSQ = NW * 8 / NLQ;
+  static_assert(KSP % 4 == 0 && KSQ % 4 == 0, "swizzle must repeat across instructions");
+  const int pk0 = wave * (8 / NLP) + (lane >> 3) / NLP;
+  int pcol = n0 + ((lane >> 3) % NLP) * 64;
+  if (pcol > N - 64) pcol = N - 64;            // past the last column: any valid line
+  pcol += mn_chunk(lane, pk0) * 8;
+  int qk0 = 0, qcol = 0;
+  int64_t q_off[QMN ? 1 : DQ];   // K-major Q: element offset of this lane's row and chunk
+  if constexpr (QMN) {
+    qk0 = wave * (8 / NLQ) + (lane >> 3) / NLQ;
+    qcol = m0 + ((lane >> 3) % NLQ) * 64;
+    if (qcol > a.M - 64) qcol = a.M - 64;
+    qcol += mn_chunk(lane, qk0) * 8;
+    q_off[0] = 0;
+  } else {
 #pragma unroll
-  for (int i = 0; i < DP; ++i) {
-    const int L = (wave + i * NW) * 8 + (lane >> 3);
-    p_k[i] = L / NLP;
-    int col = n0 + (L % NLP) * 64;
-    if (col > N - 64) col = N - 64;            // past the last column: any valid line
-    p_col[i] = col + mn_chunk(lane, p_k[i]) * 8;
-  }
-  int q_k[DQ], q_col[DQ];
-  int64_t q_off[DQ];   // K-major Q: element offset of this lane's row and chunk
-#pragma unroll
-  for (int i = 0; i < DQ; ++i) {
-    if constexpr (QMN) {
-      const int L = (wave + i * NW) * 8 + (lane >> 3);
-      q_k[i] = L / NLQ;
-      int col = m0 + (L % NLQ) * 64;
-      if (col > a.M - 64) col = a.M - 64;
-      q_col[i] = col + mn_chunk(lane, q_k[i]) * 8;
-      q_off[i] = 0;
-    } else {
+    for (int i = 0; i < DQ; ++i) {
       int r = m0 + (wave + i * NW) * 8 + dma_row(lane);
       if (r > m1 - 1) r = m1 - 1;
-      q_k[i] = 0;
-      q_col[i] = 0;
       q_off[i] = (qrow0 + r) * a.ldq + dma_chunk(lane) * 8;
     }
   }
-  const uint16_t* const pw = a.P + (int64_t)g * a.p_seg;
-  const uint16_t* const pw2 = a.P2 ? a.P2 + (int64_t)g * a.p_seg : pw;
+  // Each lane's sources are a base pointer (its k-row k0 and column folded
+  // in) plus a wave-uniform offset per slab and instruction.
+  const int64_t ldp = a.ldp, ldq = a.ldq;
+  const uint16_t* const zp = a.zero + 8 * (lane & 7);
+  const uint16_t* pb;    // P at k-row pk0 of slab 0
+  const uint16_t* pb2 = nullptr;
+  if constexpr (KIND == BG_DW) {
+    pb = a.P + (prow0 + pk0) * ldp + pcol;
+  } else {
+    pb = a.P + (int64_t)g * a.p_seg + pk0 * ldp + pcol;
+    if constexpr (KIND == BG_DX) pb2 = (a.P2 ? a.P2 : a.P) + (int64_t)g * a.p_seg + pk0 * ldp + pcol;
+  }
+  const uint16_t* qb = QMN ? a.Q + (qrow0 + qk0) * ldq + qcol : a.Q;
+  const int klen32 = (int)klen;
 
   auto issue = [&](int kt, int stage) {
     uint16_t* sp = ring + stage * (SP + SQ);
     uint16_t* sq = sp + SP;
+    const bool second = KIND == BG_DX && kt >= a.nk1;
+    const int kb = (second ? kt - a.nk1 : kt) * BK;      // first k-row of the slab
 #pragma unroll
     for (int i = 0; i < DP; ++i) {
-      const uint16_t* src;
-      if constexpr (KIND == BG_DW) {
-        const int64_t r = (int64_t)kt * BK + p_k[i];
-        src = r < klen ? a.P + (prow0 + r) * a.ldp + p_col[i] : a.zero + 8 * (lane & 7);
-      } else if constexpr (KIND == BG_DX) {
-        const bool second = kt >= a.nk1;
-        const int kk = (second ? kt - a.nk1 : kt) * BK + p_k[i];
-        src = (second ? pw2 : pw) + (int64_t)kk * a.ldp + p_col[i];
-      } else {
-        src = pw + (int64_t)(kt * BK + p_k[i]) * a.ldp + p_col[i];
-      }
+      const int kr = kb + i * KSP;                         // uniform
+      const uint16_t* src = (second ? pb2 : pb) + (int64_t)kr * ldp;
+      if constexpr (KIND == BG_DW) src = pk0 + kr < klen32 ? src : zp;
       dma_rows(src, sp + (wave + i * NW) * 512);
     }
 #pragma unroll
     for (int i = 0; i < DQ; ++i) {
       const uint16_t* src;
       if constexpr (QMN) {
-        const int64_t r = (int64_t)kt * BK + q_k[i];
-        src = r < klen ? a.Q + (qrow0 + r) * a.ldq + q_col[i] : a.zero + 8 * (lane & 7);
-      } else if constexpr (KIND == BG_DX) {
-        const bool second = kt >= a.nk1;
-        src = (second ? a.Q2 : a.Q) + q_off[i] + (int64_t)(second ? kt - a.nk1 : kt) * BK;
+        const int kr = kb + i * KSQ;
+        src = qk0 + kr < klen32 ? qb + (int64_t)kr * ldq : zp;
       } else {
-        src = a.Q + q_off[i] + (int64_t)kt * BK;
+        src = (second ? a.Q2 : a.Q) + q_off[i] + kb;
       }
       dma_rows(src, sq + (wave + i * NW) * 512);
     }
@@ -235,42 +236,98 @@ __global__ __launch_bounds__(64 * GB_NW) void bwd_gemm_kernel(GemmArgs a) {
 #pragma unroll
     for (int j = 0; j < TN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  if (nk > 0) issue(0, 0);
-  for (int kt = 0; kt < nk; ++kt) {
-    wait_vm_lgkm0<0>();
-    ring_barrier();
-    if (kt + 1 < nk) issue(kt + 1, (kt + 1) & 1);
-    const uint16_t* sp = ring + (kt & 1) * (SP + SQ);
+  // Software pipeline over 64-k slabs in a 2-stage LDS ring, each slab used
+  // in two halves of 32 k.  Step kt: (A) MFMAs of half 0 of slab kt with the
+  // reads of half 1 spread between them; (B) wait for slab kt+1, barrier,
+  // request slab kt+2 into the stage slab kt held; (C) MFMAs of half 1 with
+  // the reads of half 0 of slab kt+1 (and the new requests) spread between
+  // them.  Past the last slab the requests reload it (harmless).
+  constexpr int NRD = 2 * TN + (QMN ? 2 : 1) * TM;   // LDS read instructions per half
+  constexpr int NM = TM * TN, PER = NM / NRD > 0 ? NM / NRD : 1;
+  constexpr int DPW = DP + DQ;
+  auto read_half = [&](const uint16_t* sp, int kk, bf16x8_t* fp, bf16x8_t* fq) {
     const uint16_t* sq = sp + SP;
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      bf16x8_t fp[TN], fq[TM];
+    for (int j = 0; j < TN; ++j) fp[j] = read_mn<NLP>(sp, wn * BNW + j * 16, kk * 32, lane);
 #pragma unroll
-      for (int j = 0; j < TN; ++j) fp[j] = read_mn<NLP>(sp, wn * BNW + j * 16, kk * 32, lane);
-#pragma unroll
-      for (int i = 0; i < TM; ++i) {
-        if constexpr (QMN) {
-          fq[i] = read_mn<NLQ>(sq, wm * BMW + i * 16, kk * 32, lane);
-        } else {
-          const int ch = kk * 4 + (lane >> 4);
-          fq[i] = *reinterpret_cast<const bf16x8_t*>(sq + swz(wm * BMW + i * 16 + (lane & 15), ch));
-        }
+    for (int i = 0; i < TM; ++i) {
+      if constexpr (QMN) {
+        fq[i] = read_mn<NLQ>(sq, wm * BMW + i * 16, kk * 32, lane);
+      } else {
+        const int ch = kk * 4 + (lane >> 4);
+        fq[i] = *reinterpret_cast<const bf16x8_t*>(sq + swz(wm * BMW + i * 16 + (lane & 15), ch));
       }
+    }
+  };
+  auto mfma_half = [&](const bf16x8_t* fp, const bf16x8_t* fq) {
 #pragma unroll
-      for (int i = 0; i < TM; ++i)
+    for (int i = 0; i < TM; ++i)
 #pragma unroll
-        for (int j = 0; j < TN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fp[j], fq[i], acc[i][j], 0, 0, 0);
+      for (int j = 0; j < TN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fp[j], fq[i], acc[i][j], 0, 0, 0);
+  };
+  if (nk > 0) {
+    issue(0, 0);
+    issue(1 < nk ? 1 : 0, 1);
+    wait_vm_lgkm0<DPW>();      // slab 0 has landed (slab 1 may be in flight)
+    ring_barrier();
+    bf16x8_t p0[TN], q0[TM], p1[TN], q1[TM];
+    read_half(ring, 0, p0, q0);
+    for (int kt = 0; kt < nk; ++kt) {
+      const uint16_t* cur = ring + (kt & 1) * (SP + SQ);
+      const uint16_t* nxt = ring + ((kt + 1) & 1) * (SP + SQ);
+      // (A)
+      read_half(cur, 1, p1, q1);
+      mfma_half(p0, q0);
+#pragma unroll
+      for (int r = 0; r < NRD; ++r) {
+        __builtin_amdgcn_sched_group_barrier(0x008, PER, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      if (NM > NRD * PER) __builtin_amdgcn_sched_group_barrier(0x008, NM - NRD * PER, 0);
+      // (B)
+      wait_vm_lgkm0<0>();
+      ring_barrier();
+      issue(kt + 2 < nk ? kt + 2 : nk - 1, kt & 1);
+      // (C)
+      read_half(nxt, 0, p0, q0);
+      mfma_half(p1, q1);
+#pragma unroll
+      for (int r = 0; r < NRD; ++r) {
+        if (r < DPW) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, PER, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      if (NM > NRD * PER) __builtin_amdgcn_sched_group_barrier(0x008, NM - NRD * PER, 0);
     }
   }
   wait_vm_lgkm0<0>();
 
   // epilogue: lane holds output columns 4*(lane/16)+q of tile j, row lane%16
-  // of tile i
+  // of tile i.  dH: the saved pre-activations of row block i+1 are requested
+  // before block i is finished, so their latency overlaps the stores.
   const int64_t crow0 = KIND == BG_DW ? 0 : (int64_t)g * a.c_row_seg;
   uint16_t* const cbase = a.C + (KIND == BG_DW ? (int64_t)g * a.c_seg : 0);
+  constexpr bool LOADS = KIND == BG_DH && EPI != 0;
+  uint2 s1v[2][TN], s2v[2][TN];
+  auto load_saved = [&](int i, int buf) {
+    const int m = m0 + wm * BMW + i * 16 + (lane & 15);
+    const int64_t row = (crow0 + m) * a.ldc;
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const int col = n0 + wn * BNW + j * 16 + 4 * (lane >> 4);
+      const bool ok = m < m1 && col < N;
+      s1v[buf][j] = ok ? *reinterpret_cast<const uint2*>(a.S1 + row + col) : uint2{0u, 0u};
+      if constexpr (EPI == 3)
+        s2v[buf][j] = ok ? *reinterpret_cast<const uint2*>(a.S2 + row + col) : uint2{0u, 0u};
+    }
+  };
+  if constexpr (LOADS) load_saved(0, 0);
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
+    if constexpr (LOADS) {
+      if (i + 1 < TM) load_saved(i + 1, (i + 1) & 1);
+    }
     const int m = m0 + wm * BMW + i * 16 + (lane & 15);
     if (m >= m1) continue;
     const int64_t row = (crow0 + m) * a.ldc;
@@ -279,12 +336,12 @@ __global__ __launch_bounds__(64 * GB_NW) void bwd_gemm_kernel(GemmArgs a) {
       const int col = n0 + wn * BNW + j * 16 + 4 * (lane >> 4);
       if (col >= N) continue;
       float v[4] = {acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]};
-      if constexpr (KIND == BG_DH && EPI != 0) {
+      if constexpr (LOADS) {
         // activation backward with the saved pre-activations
-        const uint2 s1 = *reinterpret_cast<const uint2*>(a.S1 + row + col);
+        const uint2 s1 = s1v[i & 1][j];
         const uint32_t z32[4] = {s1.x & 0xffffu, s1.x >> 16, s1.y & 0xffffu, s1.y >> 16};
         if constexpr (EPI == 3) {
-          const uint2 s2 = *reinterpret_cast<const uint2*>(a.S2 + row + col);
+          const uint2 s2 = s2v[i & 1][j];
           const uint32_t u32[4] = {s2.x & 0xffffu, s2.x >> 16, s2.y & 0xffffu, s2.y >> 16};
           float dg[4], du[4];
 #pragma unroll
