@@ -724,7 +724,7 @@ hipError_t launch_gate_bwd(const GateBwdArgs& a, hipStream_t s) {
 
 hipError_t launch_dx(const DxArgs& a, hipStream_t s) {
   if (a.T == 0) return hipSuccess;
-  prof_before("bwd_dx", s);
+  prof_before("bwd_dx_sum", s);
   dx_kernel<<<(unsigned)((a.T + 3) / 4), 256, 0, s>>>(a);
   prof_after(s);
   return hipGetLastError();

@@ -172,3 +172,72 @@ def test_backward_rejects_fp32_and_bad_alpha():
     with pytest.raises(B.MoeError):
         B.backward(cfg, inp["x"], inp["w_router"], inp["w1"], inp["w2"], inp["w3"],
                    saved[: saved.numel() // 2], dy)
+
+
+def test_backward_full_size_mixtral_sampled():
+    """The Mixtral shape at full size (T=4096, d=4096, d_ff=14336, E=8, k=2),
+    the configuration bench.py times, checked on samples the oracle can
+    compute one at a time: dx, d_gate and d_logits of 24 tokens; for three
+    experts, eight hidden units each, the matching rows of dW1 / dW3 and
+    columns of dW2 (hidden units are independent, so the oracle's expert
+    backward on the sliced weights gives exactly those slices); dW_r in full
+    from the GPU's own score gradients."""
+    from oracle import moe_backward as BW
+    from oracle import moe_oracle as O
+    w = W["mixtral_bf16"]
+    print(f"[bwd-full] {w.name} T={w.T}", flush=True)
+    inp = make_inputs(w, "cuda")
+    dy = make_output_grad(w, "cuda")
+    cfg = B.config_for(w)
+    y, saved = B.forward_train_inputs(cfg, inp)
+    g = B.backward(cfg, inp["x"], inp["w_router"], inp["w1"], inp["w2"], inp["w3"], saved, dy,
+                   want_gate_grads=True)
+    torch.cuda.synchronize()
+    r = B.saved_routing(cfg, w.T, saved)
+    idx = r["topk_idx"].cpu().numpy().astype(np.int64)
+    kept = (r["slot_pos"].cpu().numpy() >= 0).reshape(w.T, w.k)
+    s = f64(r["logits"])
+    x, DY, wr = f64(inp["x"]), f64(dy), f64(inp["w_router"])
+    gates = O.gate_values(s, idx, w.gating)
+    rng = np.random.default_rng(7)
+    toks = np.unique(np.concatenate([[0, w.T - 1], rng.choice(w.T, 22, replace=False)]))
+    gx, gdg, gds = f64(g["dx"]), f64(g["d_gate"]), f64(g["d_logits"])
+    dx_ref = {t: np.zeros(w.d) for t in toks}
+    dg_ref = np.zeros((len(toks), w.k))
+    sample_experts = {0, 3, 7}
+    for e in range(w.E):
+        rows_t = [(i, t, j) for i, t in enumerate(toks) for j in range(w.k)
+                  if idx[t, j] == e and kept[t, j]]
+        if not rows_t and e not in sample_experts:
+            continue
+        w1, w2, w3 = (f64(inp[n][e]) for n in ("w1", "w2", "w3"))
+        for i, t, j in rows_t:
+            out = O.expert_ffn(x[t][None], w1, w2, w3, w.act)[0]
+            dg_ref[i, j] = float(DY[t] @ out)
+            dxr, *_ = BW.expert_backward(x[t][None], w1, w2, w3, w.act,
+                                         gates[t, j] * DY[t][None])
+            dx_ref[t] += dxr[0]
+        if e in sample_experts:
+            sel_t, sel_j = np.nonzero((idx == e) & kept)
+            F = np.sort(rng.choice(w.d_ff, 8, replace=False))
+            _, a1, a2, a3 = BW.expert_backward(x[sel_t], w1[F], w2[:, F], w3[F], w.act,
+                                               gates[sel_t, sel_j][:, None] * DY[sel_t])
+            for name, ref, got in (("dw1", a1, f64(g["dw1"][e][F])),
+                                   ("dw3", a3, f64(g["dw3"][e][F])),
+                                   ("dw2", a2, f64(g["dw2"][e][:, F]))):
+                err = np.abs(got - ref).max() / np.abs(ref).max()
+                print(f"[bwd-full] expert {e} {name} rows {len(sel_t)} err {err:.2e}", flush=True)
+                assert err <= TOL, (e, name, err)
+    ds_ref = BW.gate_backward(s[toks], idx[toks], dg_ref, w.gating)
+    for i, t in enumerate(toks):
+        dx_ref[t] += ds_ref[i] @ wr
+    dx_err = max(np.abs(gx[t] - dx_ref[t]).max() / np.abs(dx_ref[t]).max() for t in toks)
+    dg_err = np.abs(gdg[toks] - dg_ref).max() / np.abs(gdg).max()
+    ds_err = np.abs(gds[toks] - ds_ref).max() / np.abs(gds).max()
+    dwr_own, _ = BW.router_backward(x, wr, gds)
+    dwr_err = float((np.abs(f64(g["dw_router"]) - dwr_own).max(axis=1)
+                     / np.abs(dwr_own).max(axis=1)).max())
+    print(f"[bwd-full] dx {dx_err:.2e} d_gate {dg_err:.2e} d_logits {ds_err:.2e} "
+          f"dW_r(own ds) {dwr_err:.2e}", flush=True)
+    assert dx_err <= TOL and dg_err <= TOL and ds_err <= TOL
+    assert dwr_err <= 1e-5
