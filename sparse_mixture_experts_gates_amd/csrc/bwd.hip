@@ -99,6 +99,9 @@ struct GemmArgs {
   int K, N, M;                // dH/dX: K per operand pair; N output cols; dW: M output rows
   int nk1;                    // dX: slabs of the first operand pair
   int G, MT, NT;              // dW tile grid
+  int split;                  // dX: K parts (plan entries carry the part)
+  float* part;                // dX with split > 1: fp32 partials [split][rows, N]
+  int64_t part_stride;
 };
 
 __device__ __forceinline__ int xcd_remap_b(int P, int V) {
@@ -132,7 +135,7 @@ __global__ __launch_bounds__(64 * GB_NW) void bwd_gemm_kernel(GemmArgs a) {
   const int lane = tid & 63;
   const int wm = wave / WN, wn = wave % WN;
 
-  int g, m0, m1, n0, nk;
+  int g, m0, m1, n0, nk, ks = 0, kb0 = 0;
   int64_t prow0 = 0, qrow0 = 0, klen = 0;
   if constexpr (KIND == BG_DW) {
     const int V = a.G * a.MT * a.NT;
@@ -156,9 +159,13 @@ __global__ __launch_bounds__(64 * GB_NW) void bwd_gemm_kernel(GemmArgs a) {
     g = pe.g;
     m0 = pe.m0;
     m1 = pe.m1;
-    n0 = pe.nt * BN;
+    n0 = (pe.nt & ((1 << 24) - 1)) * BN;
+    ks = pe.nt >> 24;
     qrow0 = (int64_t)g * a.q_row_seg;
-    nk = KIND == BG_DX && EPI == 1 ? 2 * a.nk1 : a.K / BK;
+    // the slabs of this entry: all of them, or part ks of a split pass
+    const int nk_all = KIND == BG_DX && EPI == 1 ? 2 * a.nk1 : a.K / BK;
+    kb0 = (int)((int64_t)nk_all * ks / a.split);
+    nk = (int)((int64_t)nk_all * (ks + 1) / a.split) - kb0;
   }
   const int N = a.N;
 
@@ -205,9 +212,10 @@ __global__ __launch_bounds__(64 * GB_NW) void bwd_gemm_kernel(GemmArgs a) {
   const uint16_t* qb = QMN ? a.Q + (qrow0 + qk0) * ldq + qcol : a.Q;
   const int klen32 = (int)klen;
 
-  auto issue = [&](int kt, int stage) {
+  auto issue = [&](int ktr, int stage) {
     uint16_t* sp = ring + stage * (SP + SQ);
     uint16_t* sq = sp + SP;
+    const int kt = ktr + kb0;                              // slab index within K
     const bool second = KIND == BG_DX && kt >= a.nk1;
     const int kb = (second ? kt - a.nk1 : kt) * BK;      // first k-row of the slab
 #pragma unroll
@@ -336,6 +344,13 @@ __global__ __launch_bounds__(64 * GB_NW) void bwd_gemm_kernel(GemmArgs a) {
       const int col = n0 + wn * BNW + j * 16 + 4 * (lane >> 4);
       if (col >= N) continue;
       float v[4] = {acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]};
+      if constexpr (KIND == BG_DX) {
+        if (a.part) {   // split pass: fp32 partial of part ks, added by the dx kernel
+          *reinterpret_cast<f32x4_t*>(a.part + ks * a.part_stride + row + col) =
+              f32x4_t{v[0], v[1], v[2], v[3]};
+          continue;
+        }
+      }
       if constexpr (LOADS) {
         // activation backward with the saved pre-activations
         const uint2 s1 = s1v[i & 1][j];
@@ -545,6 +560,19 @@ __global__ __launch_bounds__(256) void dx_kernel(DxArgs a) {
     for (int j = 0; j < k; ++j) {
       const int r = a.slot_pos[t * k + j];
       if (r < 0) continue;
+      if (a.part) {   // the dX GEMM ran in K parts: add them in order
+        for (int p = 0; p < a.nparts; ++p) {
+          const float* src = a.part + p * a.part_stride + (int64_t)r * d + c * 8;
+          const f32x4_t u0 = *reinterpret_cast<const f32x4_t*>(src);
+          const f32x4_t u1 = *reinterpret_cast<const f32x4_t*>(src + 4);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            acc[q] += u0[q];
+            acc[4 + q] += u1[q];
+          }
+        }
+        continue;
+      }
       const u32x4_t v = *reinterpret_cast<const u32x4_t*>(a.dxp + (int64_t)r * d + c * 8);
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
@@ -650,6 +678,29 @@ int64_t bwd_dw_blocks(int G, int M, int N) {
   return (int64_t)G * ((M + GB_BM - 1) / GB_BM) * ((N + GB_BN - 1) / GB_BN);
 }
 
+// K parts of a routed dX pass: the plan has about (ceil(rows / BM) + G / 2)
+// row tiles per column tile; with few rounds over the CUs the last round runs
+// mostly empty, so split K into S parts (fp32 partials, added by the dx
+// kernel) where ceil(V S / CUs) / S, with 3 % per extra part for the partials'
+// traffic, is smallest.  Each part keeps at least 16 slabs.
+int bwd_dx_split(int64_t rows, int G, int N, int K_all) {
+  const int64_t NT = (N + GB_BN - 1) / GB_BN;
+  const int64_t V = ((rows + GB_BM - 1) / GB_BM + G / 2) * NT;
+  const int CUs = 256;
+  if (V <= 0 || V >= 4 * CUs) return 1;
+  int best = 1;
+  double best_cost = 1e30;
+  for (int S = 1; S <= 4; ++S) {
+    if (K_all / BK / S < 16) break;
+    const double cost = (double)((V * S + CUs - 1) / CUs) / S * (1.0 + 0.03 * (S - 1));
+    if (cost < best_cost * 0.999) {
+      best_cost = cost;
+      best = S;
+    }
+  }
+  return best;
+}
+
 int bwd_tile_rows() { return GB_BM; }
 int bwd_tile_cols() { return GB_BN; }
 
@@ -683,6 +734,10 @@ hipError_t launch_bwd_gemm(const BwdGemm& b, hipStream_t s) {
   a.N = b.N;
   a.M = b.M;
   a.nk1 = b.K / BK;
+  a.split = b.split > 1 ? b.split : 1;
+  a.part = a.split > 1 ? b.part : nullptr;
+  a.part_stride = b.part_stride;
+  if (a.split > 1 && (b.kind != BG_DX || !b.part)) return hipErrorInvalidValue;
   a.G = b.G;
   a.MT = (b.M + GB_BM - 1) / GB_BM;
   a.NT = (b.N + GB_BN - 1) / GB_BN;

@@ -169,7 +169,12 @@ struct BwdGemm {
   int64_t dense_rows;
   const void* zero;        // BG_DW: >= 64 zero bf16 elements (16-byte aligned)
   int K, N, M, G;
+  int split;               // BG_DX: K parts (the plan lists each row tile per part)
+  float* part;             // BG_DX with split > 1: fp32 partials [split][rows, N]
+  int64_t part_stride;     // rows * N
 };
+// K parts of a routed dX pass of this shape (K_all = both operand pairs).
+int bwd_dx_split(int64_t rows, int G, int N, int K_all);
 int bwd_tile_rows();
 int bwd_tile_cols();
 int64_t bwd_dw_blocks(int G, int M, int N);
@@ -205,6 +210,9 @@ struct DxArgs {
   int64_t T;
   int d, k, E, S;
   int sparse_ds;            // ds is zero outside the selected experts
+  const float* part;        // or: per-row dX as nparts fp32 K parts (stride part_stride)
+  int nparts;
+  int64_t part_stride;
 };
 hipError_t launch_dx(const DxArgs& a, hipStream_t s);
 

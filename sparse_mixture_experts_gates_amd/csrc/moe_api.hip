@@ -197,12 +197,20 @@ int64_t bwd_entries(int64_t rows, int G, int N) {
   if (mt > rows) mt = rows;
   return mt * ((N + BN - 1) / BN);
 }
-size_t bwd_plan_bytes(int64_t rows, int G, int N) {
-  return up(kPlanHeader + 16 * (size_t)bwd_entries(rows, G, N));
+size_t bwd_plan_bytes(int64_t rows, int G, int N, int parts = 1) {
+  return up(kPlanHeader + 16 * (size_t)parts * (size_t)bwd_entries(rows, G, N));
+}
+
+// K parts of the routed dX GEMM (both operand pairs for SwiGLU)
+int dx_split(const moe_config_t* c, int64_t T) {
+  const int K_all = c->d_ff * (c->act == MOE_ACT_SWIGLU ? 2 : 1);
+  return bwd_dx_split(T * c->top_k, c->num_experts, c->d, K_all);
 }
 
 struct BwdWs {
-  size_t zero, dO, dG, dU, dXp, dlogits, dGs, dUs, dXs, plan_h, plan_x, splan_h, splan_x, wr, total;
+  size_t zero, dO, dG, dU, dXp, dXpart, dlogits, dGs, dUs, dXs, plan_h, plan_x, splan_h, splan_x,
+      wr, total;
+  int split;   // K parts of the routed dX GEMM
 };
 BwdWs bwd_ws(const moe_config_t* c, int64_t T) {
   BwdWs w;
@@ -215,13 +223,15 @@ BwdWs bwd_ws(const moe_config_t* c, int64_t T) {
   w.dO = o; o += up((size_t)R * c->d * 2);
   w.dG = o; o += up((size_t)R * c->d_ff * 2);
   w.dU = o; o += glu ? up((size_t)R * c->d_ff * 2) : 0;
-  w.dXp = o; o += up((size_t)R * c->d * 2);
+  w.split = dx_split(c, T);
+  w.dXp = o; o += w.split > 1 ? 0 : up((size_t)R * c->d * 2);
+  w.dXpart = o; o += w.split > 1 ? up((size_t)w.split * R * c->d * 4) : 0;
   w.dlogits = o; o += up((size_t)T * c->num_experts * 4);
   w.dGs = o; o += up((size_t)ST * (S ? c->d_ff_shared : 0) * 2);
   w.dUs = o; o += up((size_t)ST * (S ? c->d_ff_shared : 0) * 2);
   w.dXs = o; o += up((size_t)ST * c->d * 2);
   w.plan_h = o; o += bwd_plan_bytes(R, c->num_experts, c->d_ff);
-  w.plan_x = o; o += bwd_plan_bytes(R, c->num_experts, c->d);
+  w.plan_x = o; o += bwd_plan_bytes(R, c->num_experts, c->d, w.split);
   w.splan_h = w.splan_x = o;
   if (S) {
     o += bwd_plan_bytes(ST, S, c->d_ff_shared);
@@ -822,7 +832,8 @@ moe_status_t moe_backward(const moe_config_t* cfg, int64_t T, const void* x, con
     ps.BM = bwd_tile_rows();
     ps.NT = (f + bwd_tile_cols() - 1) / bwd_tile_cols();
     ps.NT2 = (d + bwd_tile_cols() - 1) / bwd_tile_cols();
-    ps.S2 = 1;
+    const int split = shared ? 1 : bw.split;
+    ps.S2 = split;
     ps.plan = static_cast<int32_t*>(plan_h);
     ps.plan2 = static_cast<int32_t*>(plan_x);
     if (launch_plan_kernel(seg, G, T, ps, s) != hipSuccess) return MOE_ERR_HIP;
@@ -897,10 +908,13 @@ moe_status_t moe_backward(const moe_config_t* cfg, int64_t T, const void* x, con
     b.ldc = d;
     b.c_row_seg = shared ? T : 0;
     b.plan = plan_x;
-    b.max_entries = bwd_entries(rows, G, d);
+    b.max_entries = bwd_entries(rows, G, d) * split;
     b.K = f;
     b.N = d;
     b.G = G;
+    b.split = split;
+    b.part = split > 1 ? reinterpret_cast<float*>(at(workspace, bw.dXpart)) : nullptr;
+    b.part_stride = rows * (int64_t)d;
     if (launch_bwd_gemm(b, s) != hipSuccess) return MOE_ERR_HIP;
     // dW1 = dG^T X, dW3 = dU^T X
     for (int u = 0; u < (g2 ? 2 : 1); ++u) {
@@ -947,6 +961,9 @@ moe_status_t moe_backward(const moe_config_t* cfg, int64_t T, const void* x, con
   xa.E = E;
   xa.S = S;
   xa.sparse_ds = cfg->gating != MOE_GATE_SOFTMAX_FULL && aux_alpha == 0.f;
+  xa.part = bw.split > 1 ? reinterpret_cast<const float*>(at(workspace, bw.dXpart)) : nullptr;
+  xa.nparts = bw.split;
+  xa.part_stride = R * (int64_t)d;
   if (launch_dx(xa, s) != hipSuccess) return MOE_ERR_HIP;
 
   WrArgs wa;
