@@ -94,6 +94,7 @@ struct GemmArgs {
   const PlanEntry* plan;      // dH/dX row tiles
   const int32_t* count;
   const int32_t* seg;         // dW: [G+1] row offsets, or null (dense)
+  const int32_t* order;       // dW: segments by descending row count (or null: natural)
   int64_t dense_rows;
   const uint16_t* zero;       // >= 256 zero elements
   int K, N, M;                // dH/dX: K per operand pair; N output cols; dW: M output rows
@@ -103,11 +104,6 @@ struct GemmArgs {
   float* part;                // dX with split > 1: fp32 partials [split][rows, N]
   int64_t part_stride;
 };
-
-__device__ __forceinline__ int xcd_remap_b(int P, int V) {
-  const int x = P & 7, i = P >> 3, q = V >> 3, r = V & 7;
-  return (x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q) + i;
-}
 
 __device__ __forceinline__ float sigm(float z) { return 1.0f / (1.0f + __expf(-z)); }
 
@@ -138,11 +134,16 @@ __global__ __launch_bounds__(64 * GB_NW) void bwd_gemm_kernel(GemmArgs a) {
   int g, m0, m1, n0, nk, ks = 0, kb0 = 0;
   int64_t prow0 = 0, qrow0 = 0, klen = 0;
   if constexpr (KIND == BG_DW) {
+    // Longest segments first, so the costliest tiles start first and the
+    // short ones fill in at the end; blocks are dealt round-robin over the
+    // XCDs, so each XCD holds every eighth row block of a segment (its own
+    // slice of the Q operand) while the column blocks stream past.
     const int V = a.G * a.MT * a.NT;
     if ((int)blockIdx.x >= V) return;
-    const int e = xcd_remap_b(blockIdx.x, V);
-    g = e / (a.MT * a.NT);
-    const int rem = e - g * a.MT * a.NT;
+    const int e = blockIdx.x;
+    const int rank = e / (a.MT * a.NT);
+    g = a.order ? a.order[rank] : rank;
+    const int rem = e - rank * a.MT * a.NT;
     const int nt = rem / a.MT, mt = rem - nt * a.MT;
     m0 = mt * BM;
     m1 = m0 + BM < a.M ? m0 + BM : a.M;
@@ -155,7 +156,10 @@ __global__ __launch_bounds__(64 * GB_NW) void bwd_gemm_kernel(GemmArgs a) {
   } else {
     const int V = a.count[0];
     if ((int)blockIdx.x >= V) return;
-    const PlanEntry pe = a.plan[xcd_remap_b(blockIdx.x, V)];
+    // plan order, dealt round-robin over the XCDs: each XCD takes every
+    // eighth row tile of a column tile, so a skewed segment's tiles spread
+    // over the whole chip and each L2 keeps its own slice of the rows
+    const PlanEntry pe = a.plan[blockIdx.x];
     g = pe.g;
     m0 = pe.m0;
     m1 = pe.m1;
@@ -650,6 +654,18 @@ __global__ __launch_bounds__(256) void wr_reduce_kernel(WrArgs a, int nchunks) {
   a.dw_router[idx] = s;
 }
 
+// order[r] = the segment with the r-th largest row count (ties: lower index).
+__global__ __launch_bounds__(256) void seg_order_kernel(const int32_t* seg, int G, int32_t* order) {
+  __shared__ int len[1024];
+  for (int g = threadIdx.x; g < G; g += 256) len[g] = seg[g + 1] - seg[g];
+  __syncthreads();
+  for (int g = threadIdx.x; g < G; g += 256) {
+    int r = 0;
+    for (int h = 0; h < G; ++h) r += len[h] > len[g] || (len[h] == len[g] && h < g);
+    order[r] = g;
+  }
+}
+
 __global__ __launch_bounds__(256) void zero_kernel(uint32_t* p, int64_t n) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (i < n) p[i] = 0u;
@@ -728,6 +744,11 @@ hipError_t launch_bwd_gemm(const BwdGemm& b, hipStream_t s) {
   a.plan = b.plan ? reinterpret_cast<const PlanEntry*>(static_cast<const char*>(b.plan) + kPlanHeader)
                   : nullptr;
   a.seg = b.seg;
+  a.order = b.seg ? b.order : nullptr;
+  if (b.seg && b.order) {
+    if (b.G > 1024) return hipErrorInvalidValue;
+    seg_order_kernel<<<1, 256, 0, s>>>(b.seg, b.G, b.order);
+  }
   a.dense_rows = b.dense_rows;
   a.zero = static_cast<const uint16_t*>(b.zero);
   a.K = b.K;

@@ -209,7 +209,7 @@ int dx_split(const moe_config_t* c, int64_t T) {
 
 struct BwdWs {
   size_t zero, dO, dG, dU, dXp, dXpart, dlogits, dGs, dUs, dXs, plan_h, plan_x, splan_h, splan_x,
-      wr, total;
+      wr, order, total;
   int split;   // K parts of the routed dX GEMM
 };
 BwdWs bwd_ws(const moe_config_t* c, int64_t T) {
@@ -239,6 +239,7 @@ BwdWs bwd_ws(const moe_config_t* c, int64_t T) {
     o += bwd_plan_bytes(ST, S, c->d);
   }
   w.wr = o; o += up(wr_ws_bytes(T, c->num_experts, c->d));
+  w.order = o; o += up((size_t)c->num_experts * 4);
   w.total = o;
   return w;
 }
@@ -885,6 +886,7 @@ moe_status_t moe_backward(const moe_config_t* cfg, int64_t T, const void* x, con
     b.ldc = f;
     b.c_seg = (int64_t)d * f;
     b.seg = seg;
+    b.order = reinterpret_cast<int32_t*>(at(workspace, bw.order));
     b.dense_rows = T;
     b.zero = zero;
     b.M = d;
@@ -931,6 +933,7 @@ moe_status_t moe_backward(const moe_config_t* cfg, int64_t T, const void* x, con
       b.ldc = d;
       b.c_seg = (int64_t)f * d;
       b.seg = seg;
+      b.order = reinterpret_cast<int32_t*>(at(workspace, bw.order));
       b.dense_rows = T;
       b.zero = zero;
       b.M = f;
