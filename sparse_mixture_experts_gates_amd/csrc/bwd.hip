@@ -95,6 +95,7 @@ struct GemmArgs {
   const int32_t* count;
   const int32_t* seg;         // dW: [G+1] row offsets, or null (dense)
   const int32_t* order;       // dW: segments by descending row count (or null: natural)
+  int* counter;               // dW: tile counter of a persistent launch (or null)
   int64_t dense_rows;
   const uint16_t* zero;       // >= 256 zero elements
   int K, N, M;                // dH/dX: K per operand pair; N output cols; dW: M output rows
@@ -124,13 +125,33 @@ __global__ __launch_bounds__(64 * GB_NW) void bwd_gemm_kernel(GemmArgs a) {
   constexpr int DP = BK * NLP / 8 / NW;     // P load instructions per wave per slab
   constexpr int DQ = (QMN ? BK * NLQ : BM) / 8 / NW;
   static_assert(DP * NW * 8 == BK * NLP && DQ * NW * 8 == (QMN ? BK * NLQ : BM), "load split");
-  __shared__ __attribute__((aligned(1024))) uint16_t ring[2 * (SP + SQ)];
+  // the ring, then two int slots that pass a claimed tile to every wave (one
+  // LDS object: a second one makes the compiler wait for in-flight
+  // direct-to-LDS writes before every operand read)
+  __shared__ __attribute__((aligned(1024))) uint16_t ring[2 * (SP + SQ) + 4];
+  int* const tile_slot = reinterpret_cast<int*>(ring + 2 * (SP + SQ));
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int lane = tid & 63;
   const int wm = wave / WN, wn = wave % WN;
 
+  // Weight gradients with a tile counter run persistent: one workgroup per CU
+  // claims tiles in order until none is left.  Otherwise one tile per block.
+  for (int it = 0;; ++it) {
+  int e;
+  if (KIND == BG_DW && a.counter) {
+    if (tid == 0) tile_slot[it & 1] = atomicAdd(a.counter, 1);
+    wait_lgkm0();
+    ring_barrier();    // also: every wave is done with the previous tile's LDS
+    e = __builtin_amdgcn_readfirstlane(tile_slot[it & 1]);
+  } else {
+    if (it > 0) break;
+    e = blockIdx.x;
+  }
+  // lane id, opaque to the optimiser so that nothing derived from it is
+  // hoisted out of the tile loop (it would stay live across every slab)
+  int lane = tid & 63;
+  asm volatile("" : "+v"(lane));
   int g, m0, m1, n0, nk, ks = 0, kb0 = 0;
   int64_t prow0 = 0, qrow0 = 0, klen = 0;
   if constexpr (KIND == BG_DW) {
@@ -139,8 +160,7 @@ __global__ __launch_bounds__(64 * GB_NW) void bwd_gemm_kernel(GemmArgs a) {
     // XCDs, so each XCD holds every eighth row block of a segment (its own
     // slice of the Q operand) while the column blocks stream past.
     const int V = a.G * a.MT * a.NT;
-    if ((int)blockIdx.x >= V) return;
-    const int e = blockIdx.x;
+    if (e >= V) break;
     const int rank = e / (a.MT * a.NT);
     g = a.order ? a.order[rank] : rank;
     const int rem = e - rank * a.MT * a.NT;
@@ -155,11 +175,11 @@ __global__ __launch_bounds__(64 * GB_NW) void bwd_gemm_kernel(GemmArgs a) {
     nk = (int)((klen + BK - 1) / BK);
   } else {
     const int V = a.count[0];
-    if ((int)blockIdx.x >= V) return;
+    if (e >= V) break;
     // plan order, dealt round-robin over the XCDs: each XCD takes every
     // eighth row tile of a column tile, so a skewed segment's tiles spread
     // over the whole chip and each L2 keeps its own slice of the rows
-    const PlanEntry pe = a.plan[blockIdx.x];
+    const PlanEntry pe = a.plan[e];
     g = pe.g;
     m0 = pe.m0;
     m1 = pe.m1;
@@ -204,7 +224,7 @@ __global__ __launch_bounds__(64 * GB_NW) void bwd_gemm_kernel(GemmArgs a) {
   // Each lane's sources are a base pointer (its k-row k0 and column folded
   // in) plus a wave-uniform offset per slab and instruction.
   const int64_t ldp = a.ldp, ldq = a.ldq;
-  const uint16_t* const zp = a.zero + 8 * (lane & 7);
+  const uint16_t* const zp = a.zero;   // every lane may read the same zeros
   const uint16_t* pb;    // P at k-row pk0 of slab 0
   const uint16_t* pb2 = nullptr;
   if constexpr (KIND == BG_DW) {
@@ -391,6 +411,7 @@ __global__ __launch_bounds__(64 * GB_NW) void bwd_gemm_kernel(GemmArgs a) {
       *reinterpret_cast<uint2*>(cbase + row + col) = pk;
     }
   }
+  }  // tiles
 }
 
 // ---------------------------------------------------------------- gate step
@@ -655,8 +676,10 @@ __global__ __launch_bounds__(256) void wr_reduce_kernel(WrArgs a, int nchunks) {
 }
 
 // order[r] = the segment with the r-th largest row count (ties: lower index).
-__global__ __launch_bounds__(256) void seg_order_kernel(const int32_t* seg, int G, int32_t* order) {
+__global__ __launch_bounds__(256) void seg_order_kernel(const int32_t* seg, int G, int32_t* order,
+                                                        int* counter) {
   __shared__ int len[1024];
+  if (threadIdx.x == 0) *counter = 0;
   for (int g = threadIdx.x; g < G; g += 256) len[g] = seg[g + 1] - seg[g];
   __syncthreads();
   for (int g = threadIdx.x; g < G; g += 256) {
@@ -717,6 +740,20 @@ int bwd_dx_split(int64_t rows, int G, int N, int K_all) {
   return best;
 }
 
+// Compute units of the current device (one persistent workgroup each).
+int cu_count() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
 int bwd_tile_rows() { return GB_BM; }
 int bwd_tile_cols() { return GB_BN; }
 
@@ -745,9 +782,10 @@ hipError_t launch_bwd_gemm(const BwdGemm& b, hipStream_t s) {
                   : nullptr;
   a.seg = b.seg;
   a.order = b.seg ? b.order : nullptr;
-  if (b.seg && b.order) {
+  a.counter = b.seg && b.order ? b.order + b.G : nullptr;   // the int after the order
+  if (a.order) {
     if (b.G > 1024) return hipErrorInvalidValue;
-    seg_order_kernel<<<1, 256, 0, s>>>(b.seg, b.G, b.order);
+    seg_order_kernel<<<1, 256, 0, s>>>(b.seg, b.G, b.order, a.counter);
   }
   a.dense_rows = b.dense_rows;
   a.zero = static_cast<const uint16_t*>(b.zero);
@@ -767,7 +805,7 @@ hipError_t launch_bwd_gemm(const BwdGemm& b, hipStream_t s) {
   if (b.kind == BG_DW) {
     const int64_t V = (int64_t)a.G * a.MT * a.NT;
     if (V == 0) return hipSuccess;
-    grid = (unsigned)V;
+    grid = (unsigned)(a.counter && V > cu_count() ? cu_count() : V);
     prof_before(b.name, s);
     bwd_gemm_kernel<BG_DW, 0><<<grid, TH, 0, s>>>(a);
   } else {

@@ -166,7 +166,8 @@ struct BwdGemm {
   const void* plan;        // BG_DH / BG_DX: plan buffer (header + entries)
   int64_t max_entries;     // grid of a plan-driven launch
   const int32_t* seg;      // BG_DW: [G+1] row offsets or null (dense_rows each)
-  int32_t* order;          // BG_DW with seg: [G] scratch for the longest-first segment order
+  int32_t* order;          // BG_DW with seg: [G + 1] scratch: the longest-first segment
+                           // order, then the tile counter of the persistent launch
   int64_t dense_rows;
   const void* zero;        // BG_DW: >= 64 zero bf16 elements (16-byte aligned)
   int K, N, M, G;

@@ -239,7 +239,7 @@ BwdWs bwd_ws(const moe_config_t* c, int64_t T) {
     o += bwd_plan_bytes(ST, S, c->d);
   }
   w.wr = o; o += up(wr_ws_bytes(T, c->num_experts, c->d));
-  w.order = o; o += up((size_t)c->num_experts * 4);
+  w.order = o; o += up((size_t)(c->num_experts + 1) * 4);
   w.total = o;
   return w;
 }
