@@ -96,6 +96,7 @@ struct GemmArgs {
   const int32_t* seg;         // dW: [G+1] row offsets, or null (dense)
   const int32_t* order;       // dW: segments by descending row count (or null: natural)
   int* counter;               // dW: tile counter of a persistent launch (or null)
+  const int32_t* poff;        // dW from transposed operands: [G+1] padded column offsets
   int64_t dense_rows;
   const uint16_t* zero;       // >= 256 zero elements
   int K, N, M;                // dH/dX: K per operand pair; N output cols; dW: M output rows
@@ -121,10 +122,13 @@ __global__ __launch_bounds__(64 * GB_NW) void bwd_gemm_kernel(GemmArgs a) {
   constexpr int TM = BMW / 16, TN = BNW / 16;
   constexpr int NLP = BN / 64, NLQ = BM / 64;
   constexpr int SP = BK * BN, SQ = BK * BM;
-  constexpr bool QMN = KIND == BG_DW;
-  constexpr int DP = BK * NLP / 8 / NW;     // P load instructions per wave per slab
+  constexpr bool QMN = KIND == BG_DW;       // Q stored k-strided (read transposed)
+  constexpr bool PKM = KIND == BG_DWT;      // P stored K-contiguous (read like Q)
+  constexpr bool WGRAD = KIND == BG_DW || KIND == BG_DWT;
+  constexpr int DP = (PKM ? BN : BK * NLP) / 8 / NW;   // P load instructions per wave per slab
   constexpr int DQ = (QMN ? BK * NLQ : BM) / 8 / NW;
-  static_assert(DP * NW * 8 == BK * NLP && DQ * NW * 8 == (QMN ? BK * NLQ : BM), "load split");
+  static_assert(DP * NW * 8 == (PKM ? BN : BK * NLP) && DQ * NW * 8 == (QMN ? BK * NLQ : BM),
+                "load split");
   // the ring, then two int slots that pass a claimed tile to every wave (one
   // LDS object: a second one makes the compiler wait for in-flight
   // direct-to-LDS writes before every operand read)
@@ -139,7 +143,7 @@ __global__ __launch_bounds__(64 * GB_NW) void bwd_gemm_kernel(GemmArgs a) {
   // claims tiles in order until none is left.  Otherwise one tile per block.
   for (int it = 0;; ++it) {
   int e;
-  if (KIND == BG_DW && a.counter) {
+  if (WGRAD && a.counter) {
     if (tid == 0) tile_slot[it & 1] = atomicAdd(a.counter, 1);
     wait_lgkm0();
     ring_barrier();    // also: every wave is done with the previous tile's LDS
@@ -154,7 +158,7 @@ __global__ __launch_bounds__(64 * GB_NW) void bwd_gemm_kernel(GemmArgs a) {
   asm volatile("" : "+v"(lane));
   int g, m0, m1, n0, nk, ks = 0, kb0 = 0;
   int64_t prow0 = 0, qrow0 = 0, klen = 0;
-  if constexpr (KIND == BG_DW) {
+  if constexpr (WGRAD) {
     // Longest segments first, so the costliest tiles start first and the
     // short ones fill in at the end; blocks are dealt round-robin over the
     // XCDs, so each XCD holds every eighth row block of a segment (its own
@@ -168,10 +172,17 @@ __global__ __launch_bounds__(64 * GB_NW) void bwd_gemm_kernel(GemmArgs a) {
     m0 = mt * BM;
     m1 = m0 + BM < a.M ? m0 + BM : a.M;
     n0 = nt * BN;
-    const int64_t r0 = a.seg ? a.seg[g] : 0;
-    klen = a.seg ? a.seg[g + 1] - r0 : a.dense_rows;
-    prow0 = (int64_t)g * a.p_row_seg + r0;
-    qrow0 = (int64_t)g * a.q_row_seg + r0;
+    if constexpr (PKM) {
+      // transposed operands: the segment's columns start at a multiple of 64
+      // and its padding columns hold zeros
+      prow0 = qrow0 = a.poff[g];
+      klen = a.poff[g + 1] - prow0;
+    } else {
+      const int64_t r0 = a.seg ? a.seg[g] : 0;
+      klen = a.seg ? a.seg[g + 1] - r0 : a.dense_rows;
+      prow0 = (int64_t)g * a.p_row_seg + r0;
+      qrow0 = (int64_t)g * a.q_row_seg + r0;
+    }
     nk = (int)((klen + BK - 1) / BK);
   } else {
     const int V = a.count[0];
@@ -205,6 +216,17 @@ __global__ __launch_bounds__(64 * GB_NW) void bwd_gemm_kernel(GemmArgs a) {
   int pcol = n0 + ((lane >> 3) % NLP) * 64;
   if (pcol > N - 64) pcol = N - 64;            // past the last column: any valid line
   pcol += mn_chunk(lane, pk0) * 8;
+  int64_t p_off[PKM ? DP : 1];   // K-major P: element offset of this lane's row and chunk
+  if constexpr (PKM) {
+#pragma unroll
+    for (int i = 0; i < DP; ++i) {
+      int r = n0 + (wave + i * NW) * 8 + dma_row(lane);
+      if (r > N - 1) r = N - 1;
+      p_off[i] = r * a.ldp + dma_chunk(lane) * 8 + prow0;
+    }
+  } else {
+    p_off[0] = 0;
+  }
   int qk0 = 0, qcol = 0;
   int64_t q_off[QMN ? 1 : DQ];   // K-major Q: element offset of this lane's row and chunk
   if constexpr (QMN) {
@@ -218,7 +240,8 @@ __global__ __launch_bounds__(64 * GB_NW) void bwd_gemm_kernel(GemmArgs a) {
     for (int i = 0; i < DQ; ++i) {
       int r = m0 + (wave + i * NW) * 8 + dma_row(lane);
       if (r > m1 - 1) r = m1 - 1;
-      q_off[i] = (qrow0 + r) * a.ldq + dma_chunk(lane) * 8;
+      q_off[i] = PKM ? r * a.ldq + dma_chunk(lane) * 8 + qrow0
+                     : (qrow0 + r) * a.ldq + dma_chunk(lane) * 8;
     }
   }
   // Each lane's sources are a base pointer (its k-row k0 and column folded
@@ -227,7 +250,9 @@ __global__ __launch_bounds__(64 * GB_NW) void bwd_gemm_kernel(GemmArgs a) {
   const uint16_t* const zp = a.zero;   // every lane may read the same zeros
   const uint16_t* pb;    // P at k-row pk0 of slab 0
   const uint16_t* pb2 = nullptr;
-  if constexpr (KIND == BG_DW) {
+  if constexpr (PKM) {
+    pb = a.P;
+  } else if constexpr (KIND == BG_DW) {
     pb = a.P + (prow0 + pk0) * ldp + pcol;
   } else {
     pb = a.P + (int64_t)g * a.p_seg + pk0 * ldp + pcol;
@@ -245,7 +270,7 @@ __global__ __launch_bounds__(64 * GB_NW) void bwd_gemm_kernel(GemmArgs a) {
 #pragma unroll
     for (int i = 0; i < DP; ++i) {
       const int kr = kb + i * KSP;                         // uniform
-      const uint16_t* src = (second ? pb2 : pb) + (int64_t)kr * ldp;
+      const uint16_t* src = PKM ? pb + p_off[i] + kb : (second ? pb2 : pb) + (int64_t)kr * ldp;
       if constexpr (KIND == BG_DW) src = pk0 + kr < klen32 ? src : zp;
       dma_rows(src, sp + (wave + i * NW) * 512);
     }
@@ -274,13 +299,20 @@ __global__ __launch_bounds__(64 * GB_NW) void bwd_gemm_kernel(GemmArgs a) {
   // request slab kt+2 into the stage slab kt held; (C) MFMAs of half 1 with
   // the reads of half 0 of slab kt+1 (and the new requests) spread between
   // them.  Past the last slab the requests reload it (harmless).
-  constexpr int NRD = 2 * TN + (QMN ? 2 : 1) * TM;   // LDS read instructions per half
+  constexpr int NRD = (PKM ? 1 : 2) * TN + (QMN ? 2 : 1) * TM;   // LDS read instructions per half
   constexpr int NM = TM * TN, PER = NM / NRD > 0 ? NM / NRD : 1;
   constexpr int DPW = DP + DQ;
   auto read_half = [&](const uint16_t* sp, int kk, bf16x8_t* fp, bf16x8_t* fq) {
     const uint16_t* sq = sp + SP;
 #pragma unroll
-    for (int j = 0; j < TN; ++j) fp[j] = read_mn<NLP>(sp, wn * BNW + j * 16, kk * 32, lane);
+    for (int j = 0; j < TN; ++j) {
+      if constexpr (PKM) {
+        const int ch = kk * 4 + (lane >> 4);
+        fp[j] = *reinterpret_cast<const bf16x8_t*>(sp + swz(wn * BNW + j * 16 + (lane & 15), ch));
+      } else {
+        fp[j] = read_mn<NLP>(sp, wn * BNW + j * 16, kk * 32, lane);
+      }
+    }
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
       if constexpr (QMN) {
@@ -338,8 +370,8 @@ __global__ __launch_bounds__(64 * GB_NW) void bwd_gemm_kernel(GemmArgs a) {
   // epilogue: lane holds output columns 4*(lane/16)+q of tile j, row lane%16
   // of tile i.  dH: the saved pre-activations of row block i+1 are requested
   // before block i is finished, so their latency overlaps the stores.
-  const int64_t crow0 = KIND == BG_DW ? 0 : (int64_t)g * a.c_row_seg;
-  uint16_t* const cbase = a.C + (KIND == BG_DW ? (int64_t)g * a.c_seg : 0);
+  const int64_t crow0 = WGRAD ? 0 : (int64_t)g * a.c_row_seg;
+  uint16_t* const cbase = a.C + (WGRAD ? (int64_t)g * a.c_seg : 0);
   constexpr bool LOADS = KIND == BG_DH && EPI != 0;
   uint2 s1v[2][TN], s2v[2][TN];
   auto load_saved = [&](int i, int buf) {
@@ -675,6 +707,63 @@ __global__ __launch_bounds__(256) void wr_reduce_kernel(WrArgs a, int nchunks) {
   a.dw_router[idx] = s;
 }
 
+// Padded column offsets of the transposed operands: segment g's rows become
+// columns [poff[g], poff[g] + rows_g) of a row of the transposed matrix, and
+// every segment starts at a multiple of 64.
+__global__ __launch_bounds__(64) void pad_offsets_kernel(const int32_t* seg, int G, int32_t* poff) {
+  if (threadIdx.x != 0) return;
+  int acc = 0;
+  for (int g = 0; g < G; ++g) {
+    poff[g] = acc;
+    acc += (seg[g + 1] - seg[g] + 63) & ~63;
+  }
+  poff[G] = acc;
+}
+
+// AT[m, poff[g] + (r - seg[g])] = A[r, m] for the rows r of every segment g,
+// zeros in the padding columns.  Workgroup: 64 columns of AT (inside one
+// segment) x 64 of its rows, staged through LDS; 16-byte loads and stores.
+__global__ __launch_bounds__(256) void transpose_pad_kernel(const uint16_t* __restrict__ A,
+                                                            int64_t lda, const int32_t* seg,
+                                                            const int32_t* poff, int G,
+                                                            uint16_t* __restrict__ AT,
+                                                            int64_t ldt) {
+  __shared__ uint16_t tile[64][72];
+  const int p0 = blockIdx.x * 64;
+  if (p0 >= poff[G]) return;
+  int lo = 0, hi = G - 1;          // the segment holding column p0: last g with poff[g] <= p0
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (poff[mid] <= p0) lo = mid; else hi = mid - 1;
+  }
+  const int g = lo;
+  const int64_t r0 = seg[g] + (p0 - poff[g]);
+  const int64_t r_end = seg[g + 1];
+  const int m0 = blockIdx.y * 64;
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int idx = tid + 256 * i, row = idx >> 3, c8 = idx & 7;
+    u32x4_t v = {0u, 0u, 0u, 0u};
+    if (r0 + row < r_end) v = *reinterpret_cast<const u32x4_t*>(A + (r0 + row) * lda + m0 + c8 * 8);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      tile[row][c8 * 8 + 2 * q] = (uint16_t)(v[q] & 0xffffu);
+      tile[row][c8 * 8 + 2 * q + 1] = (uint16_t)(v[q] >> 16);
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int idx = tid + 256 * i, m = idx >> 3, p8 = idx & 7;
+    u32x4_t o;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      o[q] = (uint32_t)tile[p8 * 8 + 2 * q][m] | ((uint32_t)tile[p8 * 8 + 2 * q + 1][m] << 16);
+    *reinterpret_cast<u32x4_t*>(AT + (int64_t)(m0 + m) * ldt + p0 + p8 * 8) = o;
+  }
+}
+
 // order[r] = the segment with the r-th largest row count (ties: lower index).
 __global__ __launch_bounds__(256) void seg_order_kernel(const int32_t* seg, int G, int32_t* order,
                                                         int* counter) {
@@ -781,6 +870,7 @@ hipError_t launch_bwd_gemm(const BwdGemm& b, hipStream_t s) {
   a.plan = b.plan ? reinterpret_cast<const PlanEntry*>(static_cast<const char*>(b.plan) + kPlanHeader)
                   : nullptr;
   a.seg = b.seg;
+  a.poff = b.poff;
   a.order = b.seg ? b.order : nullptr;
   a.counter = b.seg && b.order ? b.order + b.G : nullptr;   // the int after the order
   if (a.order) {
@@ -802,12 +892,14 @@ hipError_t launch_bwd_gemm(const BwdGemm& b, hipStream_t s) {
   a.NT = (b.N + GB_BN - 1) / GB_BN;
   constexpr int TH = 64 * GB_NW;
   unsigned grid;
-  if (b.kind == BG_DW) {
+  if (b.kind == BG_DW || b.kind == BG_DWT) {
     const int64_t V = (int64_t)a.G * a.MT * a.NT;
     if (V == 0) return hipSuccess;
+    if (b.kind == BG_DWT && (!b.poff || !a.counter)) return hipErrorInvalidValue;
     grid = (unsigned)(a.counter && V > cu_count() ? cu_count() : V);
     prof_before(b.name, s);
-    bwd_gemm_kernel<BG_DW, 0><<<grid, TH, 0, s>>>(a);
+    if (b.kind == BG_DWT) bwd_gemm_kernel<BG_DWT, 0><<<grid, TH, 0, s>>>(a);
+    else bwd_gemm_kernel<BG_DW, 0><<<grid, TH, 0, s>>>(a);
   } else {
     if (b.max_entries == 0) return hipSuccess;
     grid = (unsigned)b.max_entries;
@@ -854,6 +946,24 @@ hipError_t launch_router_bwd(const WrArgs& in, hipStream_t s) {
   wr_partial_kernel<<<grid, 256, 0, s>>>(a);
   const int64_t n = (int64_t)a.E * a.d;
   wr_reduce_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(a, nch);
+  prof_after(s);
+  return hipGetLastError();
+}
+
+hipError_t launch_pad_offsets(const int32_t* seg, int G, int32_t* poff, hipStream_t s) {
+  pad_offsets_kernel<<<1, 64, 0, s>>>(seg, G, poff);
+  return hipGetLastError();
+}
+
+hipError_t launch_transpose_pad(const void* A, int64_t lda, int M, const int32_t* seg,
+                                const int32_t* poff, int G, int64_t max_cols, void* AT,
+                                int64_t ldt, hipStream_t s) {
+  if (M % 64 || ldt % 64 || lda % 8 || max_cols > ldt) return hipErrorInvalidValue;
+  const int64_t nx = (max_cols + 63) / 64;
+  if (nx == 0) return hipSuccess;
+  prof_before("bwd_transpose", s);
+  transpose_pad_kernel<<<dim3((unsigned)nx, (unsigned)(M / 64)), 256, 0, s>>>(
+      static_cast<const uint16_t*>(A), lda, seg, poff, G, static_cast<uint16_t*>(AT), ldt);
   prof_after(s);
   return hipGetLastError();
 }
