@@ -721,46 +721,46 @@ __global__ __launch_bounds__(64) void pad_offsets_kernel(const int32_t* seg, int
 }
 
 // AT[m, poff[g] + (r - seg[g])] = A[r, m] for the rows r of every segment g,
-// zeros in the padding columns.  Workgroup: 64 columns of AT (inside one
-// segment) x 64 of its rows, staged through LDS; 16-byte loads and stores.
+// zeros in the padding columns.  A wave transposes a 64 x 64 block in
+// registers: lane (pc, mc) loads the 8 x 8 sub-block of rows 8 pc.. and
+// columns 8 mc.. (eight 16-byte loads; the 8 lanes of one pc cover a whole
+// 128-byte row segment), repacks it, and stores its 8 columns as 16-byte
+// pieces of 8 consecutive AT columns (the 8 lanes of one mc cover a whole
+// 128-byte segment of an AT row).  A workgroup (4 waves) covers 64 columns of
+// AT inside one segment and 256 of its rows.
 __global__ __launch_bounds__(256) void transpose_pad_kernel(const uint16_t* __restrict__ A,
-                                                            int64_t lda, const int32_t* seg,
+                                                            int64_t lda, int M,
+                                                            const int32_t* seg,
                                                             const int32_t* poff, int G,
                                                             uint16_t* __restrict__ AT,
                                                             int64_t ldt) {
-  __shared__ uint16_t tile[64][72];
   const int p0 = blockIdx.x * 64;
-  if (p0 >= poff[G]) return;
+  const int m0 = (blockIdx.y * 4 + (threadIdx.x >> 6)) * 64;
+  if (p0 >= poff[G] || m0 >= M) return;
   int lo = 0, hi = G - 1;          // the segment holding column p0: last g with poff[g] <= p0
   while (lo < hi) {
     const int mid = (lo + hi + 1) >> 1;
     if (poff[mid] <= p0) lo = mid; else hi = mid - 1;
   }
-  const int g = lo;
-  const int64_t r0 = seg[g] + (p0 - poff[g]);
-  const int64_t r_end = seg[g + 1];
-  const int m0 = blockIdx.y * 64;
-  const int tid = threadIdx.x;
+  const int64_t r0 = seg[lo] + (p0 - poff[lo]);
+  const int64_t r_end = seg[lo + 1];
+  const int lane = threadIdx.x & 63, mc = lane & 7, pc = lane >> 3;
+  u32x4_t v[8];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int idx = tid + 256 * i, row = idx >> 3, c8 = idx & 7;
-    u32x4_t v = {0u, 0u, 0u, 0u};
-    if (r0 + row < r_end) v = *reinterpret_cast<const u32x4_t*>(A + (r0 + row) * lda + m0 + c8 * 8);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      tile[row][c8 * 8 + 2 * q] = (uint16_t)(v[q] & 0xffffu);
-      tile[row][c8 * 8 + 2 * q + 1] = (uint16_t)(v[q] >> 16);
-    }
+  for (int i = 0; i < 8; ++i) {
+    const int64_t r = r0 + 8 * pc + i;
+    v[i] = r < r_end ? *reinterpret_cast<const u32x4_t*>(A + r * lda + m0 + 8 * mc)
+                     : u32x4_t{0u, 0u, 0u, 0u};
   }
-  __syncthreads();
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int idx = tid + 256 * i, m = idx >> 3, p8 = idx & 7;
+  for (int c = 0; c < 8; ++c) {
     u32x4_t o;
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
-      o[q] = (uint32_t)tile[p8 * 8 + 2 * q][m] | ((uint32_t)tile[p8 * 8 + 2 * q + 1][m] << 16);
-    *reinterpret_cast<u32x4_t*>(AT + (int64_t)(m0 + m) * ldt + p0 + p8 * 8) = o;
+    for (int q = 0; q < 4; ++q) {
+      const uint32_t lo16 = v[2 * q][c >> 1], hi16 = v[2 * q + 1][c >> 1];
+      o[q] = (c & 1) ? (lo16 >> 16) | (hi16 & 0xffff0000u) : (lo16 & 0xffffu) | (hi16 << 16);
+    }
+    *reinterpret_cast<u32x4_t*>(AT + (int64_t)(m0 + 8 * mc + c) * ldt + p0 + 8 * pc) = o;
   }
 }
 
@@ -962,8 +962,8 @@ hipError_t launch_transpose_pad(const void* A, int64_t lda, int M, const int32_t
   const int64_t nx = (max_cols + 63) / 64;
   if (nx == 0) return hipSuccess;
   prof_before("bwd_transpose", s);
-  transpose_pad_kernel<<<dim3((unsigned)nx, (unsigned)(M / 64)), 256, 0, s>>>(
-      static_cast<const uint16_t*>(A), lda, seg, poff, G, static_cast<uint16_t*>(AT), ldt);
+  transpose_pad_kernel<<<dim3((unsigned)nx, (unsigned)((M + 255) / 256)), 256, 0, s>>>(
+      static_cast<const uint16_t*>(A), lda, M, seg, poff, G, static_cast<uint16_t*>(AT), ldt);
   prof_after(s);
   return hipGetLastError();
 }
