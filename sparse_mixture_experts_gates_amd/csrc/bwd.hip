@@ -664,21 +664,25 @@ __global__ __launch_bounds__(256) void dx_kernel(DxArgs a) {
 }
 
 // -------------------------------------------------------------- router dW_r
-// dW_r[e, i] = sum_t ds[t, e] x[t, i].  Workgroup (column block of 256, expert
-// block of 32, token chunk): thread i sums its column over the chunk's tokens
-// for 32 experts; the chunks are then added in order.
+// dW_r[e, i] = sum_t ds[t, e] x[t, i].  Workgroup (1024 columns, 32 experts,
+// a chunk of tokens): thread c sums columns 4c..4c+3 over the chunk's tokens
+// for the 32 experts, reading each token's 32 score gradients from LDS four
+// at a time; the chunks are then added in order.
 constexpr int WR_EB = 32;
+constexpr int WR_COLS = 1024;
 __global__ __launch_bounds__(256) void wr_partial_kernel(WrArgs a) {
-  __shared__ float dsl[64][WR_EB];
-  const int i = blockIdx.x * 256 + threadIdx.x;
-  const bool col_ok = i < a.d;
+  __shared__ __attribute__((aligned(16))) float dsl[64][WR_EB];
+  const int i = blockIdx.x * WR_COLS + threadIdx.x * 4;
+  const bool col_ok = i < a.d;                 // d is a multiple of 64: 4 columns in or out
   const int e0 = blockIdx.y * WR_EB;
   const int64_t t0 = (int64_t)blockIdx.z * a.chunk;
   const int64_t t1 = t0 + a.chunk < a.T ? t0 + a.chunk : a.T;
   const int ne = a.E - e0 < WR_EB ? a.E - e0 : WR_EB;
-  float acc[WR_EB];
+  float acc[WR_EB][4];
 #pragma unroll
-  for (int e = 0; e < WR_EB; ++e) acc[e] = 0.f;
+  for (int e = 0; e < WR_EB; ++e)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) acc[e][c] = 0.f;
   for (int64_t tb = t0; tb < t1; tb += 64) {
     __syncthreads();
     for (int q = threadIdx.x; q < 64 * WR_EB; q += 256) {
@@ -687,15 +691,36 @@ __global__ __launch_bounds__(256) void wr_partial_kernel(WrArgs a) {
     }
     __syncthreads();
     const int nt = t1 - tb < 64 ? (int)(t1 - tb) : 64;
-    for (int tt = 0; tt < nt && col_ok; ++tt) {
-      const float xv = bf16_to_f32(a.x[(tb + tt) * a.d + i]);
+    // x of 8 tokens in flight before the first is used (tokens past nt read
+    // the chunk's last token and add zero: their ds rows are zero in LDS)
+    for (int tt = 0; tt < nt && col_ok; tt += 8) {
+      uint2 xv[8];
 #pragma unroll
-      for (int e = 0; e < WR_EB; ++e) acc[e] += dsl[tt][e] * xv;
+      for (int v = 0; v < 8; ++v) {
+        const int t = tt + v < nt ? tt + v : nt - 1;
+        xv[v] = *reinterpret_cast<const uint2*>(a.x + (tb + t) * a.d + i);
+      }
+#pragma unroll
+      for (int v = 0; v < 8; ++v) {
+        const float x4[4] = {bf16_to_f32(xv[v].x & 0xffffu), bf16_to_f32(xv[v].x >> 16),
+                             bf16_to_f32(xv[v].y & 0xffffu), bf16_to_f32(xv[v].y >> 16)};
+#pragma unroll
+        for (int e4 = 0; e4 < WR_EB; e4 += 4) {
+          const f32x4_t d4 = *reinterpret_cast<const f32x4_t*>(&dsl[tt + v][e4]);
+#pragma unroll
+          for (int u = 0; u < 4; ++u)
+#pragma unroll
+            for (int c = 0; c < 4; ++c) acc[e4 + u][c] += d4[u] * x4[c];
+        }
+      }
     }
   }
   if (!col_ok) return;
   float* out = a.partial + ((int64_t)blockIdx.z * a.E + e0) * a.d + i;
-  for (int e = 0; e < ne; ++e) out[(int64_t)e * a.d] = acc[e];
+#pragma unroll
+  for (int e = 0; e < WR_EB; ++e)
+    if (e < ne)
+      *reinterpret_cast<f32x4_t*>(out + (int64_t)e * a.d) = f32x4_t{acc[e][0], acc[e][1], acc[e][2], acc[e][3]};
 }
 
 __global__ __launch_bounds__(256) void wr_reduce_kernel(WrArgs a, int nchunks) {
@@ -785,7 +810,7 @@ __global__ __launch_bounds__(256) void zero_kernel(uint32_t* p, int64_t n) {
 
 int wr_chunk(int64_t T, int E, int d) {
   // enough workgroups to cover the chip about four times over
-  const int64_t per = (int64_t)((d + 255) / 256) * ((E + WR_EB - 1) / WR_EB);
+  const int64_t per = (int64_t)((d + WR_COLS - 1) / WR_COLS) * ((E + WR_EB - 1) / WR_EB);
   int64_t chunks = (4 * 256 + per - 1) / per;
   if (chunks > (T + 63) / 64) chunks = (T + 63) / 64;
   if (chunks < 1) chunks = 1;
@@ -942,7 +967,7 @@ hipError_t launch_router_bwd(const WrArgs& in, hipStream_t s) {
   a.chunk = wr_chunk(a.T, a.E, a.d);
   const int nch = (int)((a.T + a.chunk - 1) / a.chunk);
   prof_before("bwd_router", s);
-  dim3 grid((a.d + 255) / 256, (a.E + WR_EB - 1) / WR_EB, nch);
+  dim3 grid((a.d + WR_COLS - 1) / WR_COLS, (a.E + WR_EB - 1) / WR_EB, nch);
   wr_partial_kernel<<<grid, 256, 0, s>>>(a);
   const int64_t n = (int64_t)a.E * a.d;
   wr_reduce_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(a, nch);
