@@ -603,16 +603,19 @@ __global__ __launch_bounds__(256) void gate_bwd_kernel(GateBwdArgs a) {
 }
 
 // ------------------------------------------------------------------ dx step
-// One wave per token, 8 columns per lane and step: the kept slots' dX rows in
-// slot order, then the shared experts', then the router term sum_e ds_e W_r[e]
-// (only the selected experts' when the score gradient is zero elsewhere).
+// One wave per (token, 512 columns), 8 columns per lane: the kept slots' dX
+// rows in slot order, then the shared experts', then the router term
+// sum_e ds_e W_r[e] (only the selected experts' when the score gradient is
+// zero elsewhere).
 __global__ __launch_bounds__(256) void dx_kernel(DxArgs a) {
   const int lane = threadIdx.x & 63;
   const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= a.T) return;
   const int d = a.d, k = a.k, E = a.E;
   const float* ds = a.d_logits + t * E;
-  for (int c = lane; c < (d >> 3); c += 64) {
+  {
+    const int c = blockIdx.y * 64 + lane;
+    if (c >= (d >> 3)) return;
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     for (int j = 0; j < k; ++j) {
       const int r = a.slot_pos[t * k + j];
@@ -956,7 +959,7 @@ hipError_t launch_gate_bwd(const GateBwdArgs& a, hipStream_t s) {
 hipError_t launch_dx(const DxArgs& a, hipStream_t s) {
   if (a.T == 0) return hipSuccess;
   prof_before("bwd_dx_sum", s);
-  dx_kernel<<<(unsigned)((a.T + 3) / 4), 256, 0, s>>>(a);
+  dx_kernel<<<dim3((unsigned)((a.T + 3) / 4), (unsigned)((a.d / 8 + 63) / 64)), 256, 0, s>>>(a);
   prof_after(s);
   return hipGetLastError();
 }
