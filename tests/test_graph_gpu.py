@@ -70,3 +70,60 @@ def test_forward_replays_match_eager(name, kw):
     torch.cuda.synchronize()
     assert torch.equal(bits(y), bits(ref))
     print(f"[graph] {name} ok", flush=True)
+
+
+@pytest.mark.parametrize("name,kw", [
+    ("mixtral_small", dict(T=300, d=256, d_ff=320)),
+    ("deepseek_small", dict(T=200, d=192, E=64, d_ff=128, d_ff_shared=192)),
+    ("split_dx", dict(T=300, d=256, d_ff=2048)),                  # dX in K parts
+])
+def test_training_step_replays_match_eager(name, kw):
+    """moe_forward_train + moe_backward captured together: every replay gives
+    the eager y and gradients bit for bit (the backward's fills are kernels,
+    its tile counters are reset by kernels, nothing is allocated)."""
+    from sparse_mixture_experts_gates_amd.workloads import make_output_grad
+    base = {"mixtral_small": "mixtral_bf16", "deepseek_small": "deepseek_v3_bf16",
+            "split_dx": "mixtral_bf16"}[name]
+    w = WORKLOADS[base].scaled(**kw)
+    print(f"[graph-train] {name}", flush=True)
+    inp = make_inputs(w, "cuda")
+    dy = make_output_grad(w, "cuda")
+    cfg = B.config_for(w)
+    y, saved = B.forward_train_inputs(cfg, inp)
+    bws = torch.empty(B.backward_workspace_size(cfg, w.T), dtype=torch.uint8, device="cuda")
+    g = B.backward(cfg, inp["x"], inp["w_router"], inp["w1"], inp["w2"], inp["w3"], saved, dy,
+                   ws1=inp["ws1"], ws3=inp["ws3"], ws2=inp["ws2"], ws=bws, want_gate_grads=True)
+
+    def step():
+        B.forward_train_inputs(cfg, inp, saved=saved, y=y)
+        B.backward(cfg, inp["x"], inp["w_router"], inp["w1"], inp["w2"], inp["w3"], saved, dy,
+                   ws1=inp["ws1"], ws3=inp["ws3"], ws2=inp["ws2"], ws=bws, grads=g,
+                   aux_alpha=0.01)
+
+    step()
+    torch.cuda.synchronize()
+    eager = {"y": y.clone(), **{k: v.clone() for k, v in g.items() if v is not None}}
+
+    graph = torch.cuda.CUDAGraph()
+    cs = torch.cuda.Stream()
+    cs.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(cs):
+        step()
+        torch.cuda.synchronize()
+        with torch.cuda.graph(graph, stream=cs):
+            step()
+    torch.cuda.current_stream().wait_stream(cs)
+    torch.cuda.synchronize()
+
+    for i in range(4):
+        # eager work with its own buffers between replays
+        B.forward_inputs(cfg, inp)
+        y.zero_()
+        for v in g.values():
+            if v is not None:
+                v.zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        got = {"y": y, **{k: v for k, v in g.items() if v is not None}}
+        for k, v in eager.items():
+            assert torch.equal(bits(got[k]), bits(v)), f"replay {i}: {k} differs from eager"
