@@ -60,11 +60,16 @@ CASES = {
     "decode_T8_E128": W["gptoss_decode_bf16"].scaled(d=256, d_ff=192),
     "one_token": small(T=1, E=16, k=3),
     "many_idle_experts": small(T=20, E=64, k=1, d=128, d_ff=64, act="relu"),
+    # capacity 0: every slot is dropped, nothing reaches an expert (all weight
+    # gradients exactly zero, dx and dW_r from the router and shared experts)
+    "all_dropped_shared": W["deepseek_v3_bf16"].scaled(T=200, d=192, E=16, k=2, d_ff=128,
+                                                       d_ff_shared=128, capacity_factor=0.01),
     # few row tiles and a long K: the dX GEMM runs in 4 K parts (fp32 partials)
     "split_k_dx": small(T=300, d=256, d_ff=2048),
     "split_k_dx_gelu": small(T=300, d=320, d_ff=4096, act="gelu", E=4),
 }
-AUX = {"deepseek_like_shared_bias": 0.05, "gelu_sigmoid_capacity": 0.02}
+AUX = {"deepseek_like_shared_bias": 0.05, "gelu_sigmoid_capacity": 0.02,
+       "all_dropped_shared": 0.1}
 
 
 def rows_rel(gpu, ref):
