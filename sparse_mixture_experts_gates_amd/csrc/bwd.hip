@@ -12,7 +12,8 @@
 //   dH GEMM       dH = dO . W2_e over each expert's rows; the epilogue applies
 //                 the activation's derivative with the saved pre-activations
 //                 (SwiGLU: dG = dH u silu'(g), dU = dH silu(g))
-//   dX GEMM       dX = dG . W1_e (+ dU . W3_e) over each expert's rows
+//   dX GEMM       dX = dG . W1_e (+ dU . W3_e) over each expert's rows, in K
+//                 parts (fp32 partials) when it has few row tiles
 //   dW GEMMs      dW2_e = dO_e^T H_e, dW1_e = dG_e^T X_e, dW3_e = dU_e^T X_e:
 //                 the contraction runs over the expert's rows (ragged K)
 //   dx kernel     dx_t = sum over kept slots of dX rows + shared experts'
@@ -21,13 +22,21 @@
 //
 // GEMM layout.  Every backward GEMM has its output's contiguous dimension on
 // the MFMA row side (P) and its other dimension on the column side (Q), as
-// the forward does.  P is always stored with that output dimension
-// contiguous (W2_e rows for dH, W1_e / W3_e rows for dX, H or x rows for the
-// weight gradients), so its K index is strided: P tiles are staged in LDS as
-// k-rows of 64-element lines and read with ds_read_b64_tr_b16, which hands
-// each lane 4 consecutive k of one column (two reads make one 8-k MFMA
-// operand).  Q is K-contiguous (activation rows) for dH / dX, read like the
-// forward's operands, and k-strided for the weight gradients (tr reads too).
+// the forward does.  For dH and dX, P is a weight stored with that dimension
+// contiguous (W2_e for dH, W1_e / W3_e for dX), so its K index is strided: P
+// tiles are staged in LDS as k-rows of 64-element lines and read with
+// ds_read_b64_tr_b16, which hands each lane 4 consecutive k of one column
+// (two reads make one 8-k MFMA operand); Q holds activation rows
+// (K-contiguous), read like the forward's operands.  The weight gradients
+// contract over rows, so both operands are k-strided: for the routed experts
+// they are first transposed (each expert's rows padded to 64 columns, zeros
+// between) and then read K-contiguously on both sides; the shared experts'
+// read both sides transposed from LDS.
+//
+// Scheduling.  Row tiles of dH / dX follow the device-built plans, dealt
+// round-robin over the XCDs.  Weight-gradient tiles run persistent (one
+// workgroup per CU claims tiles from a counter), experts with the most rows
+// first.
 #include <string.h>
 
 #include "common.h"
