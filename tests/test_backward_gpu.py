@@ -64,12 +64,14 @@ CASES = {
     # gradients exactly zero, dx and dW_r from the router and shared experts)
     "all_dropped_shared": W["deepseek_v3_bf16"].scaled(T=200, d=192, E=16, k=2, d_ff=128,
                                                        d_ff_shared=128, capacity_factor=0.01),
+    # the largest routing the library takes: E = 256 experts, k = 16 slots
+    "max_E256_k16": small(T=96, d=128, E=256, k=16, d_ff=64, gating="softmax_full"),
     # few row tiles and a long K: the dX GEMM runs in 4 K parts (fp32 partials)
     "split_k_dx": small(T=300, d=256, d_ff=2048),
     "split_k_dx_gelu": small(T=300, d=320, d_ff=4096, act="gelu", E=4),
 }
 AUX = {"deepseek_like_shared_bias": 0.05, "gelu_sigmoid_capacity": 0.02,
-       "all_dropped_shared": 0.1}
+       "all_dropped_shared": 0.1, "max_E256_k16": 0.03}
 
 
 def rows_rel(gpu, ref):
