@@ -33,10 +33,18 @@
 // between) and then read K-contiguously on both sides; the shared experts'
 // read both sides transposed from LDS.
 //
+// Loads.  Slabs go straight from global memory to LDS (global_load_lds) in
+// a two-stage ring; the kernels that read transposed issue them from asm, so
+// that the compiler does not wait for the newest slab before every
+// ds_read_b64_tr_b16 (it cannot tell the two apart).
+//
 // Scheduling.  Row tiles of dH / dX follow the device-built plans, dealt
-// round-robin over the XCDs.  Weight-gradient tiles run persistent (one
-// workgroup per CU claims tiles from a counter), experts with the most rows
-// first.
+// round-robin over the XCDs.  Weight-gradient tiles run persistent: one
+// workgroup per CU claims tiles one ahead from its XCD's queue (stealing from
+// the next queues once it is empty), experts with the most rows first; the
+// next tile's first two slabs are requested before the current tile's
+// output block is stored, and the block goes out through LDS as whole
+// 128-byte row segments.
 #include <string.h>
 
 #include "common.h"
@@ -51,6 +59,8 @@ constexpr int BK = 64;
 constexpr int GB_BM = 256, GB_BN = 256;     // output tile: Q extent x P extent
 constexpr int GB_WM = 2, GB_WN = 4;         // waves along Q, along P
 constexpr int GB_NW = GB_WM * GB_WN;
+constexpr int GB_MAX_SEGS = 1024;           // segments a weight-gradient launch may hold
+constexpr int GB_QUEUES = 8;                // tile queues of a persistent launch (one per XCD)
 
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
 
@@ -80,6 +90,18 @@ __device__ __forceinline__ bf16x8_t read_mn(const uint16_t* tile, int col0, int 
   return __builtin_bit_cast(bf16x8_t, v);
 }
 
+// dma_rows issued from an asm block with no register outputs, so that the
+// compiler does not know of the direct-to-LDS write.  It cannot tell such a
+// write apart from the LDS reads of ds_read_b64_tr_b16 and would otherwise
+// wait for every load in flight (the slab requested for two steps later
+// included) before the first transposed read of each step; the kernel's own
+// s_waitcnt calls order the slabs instead.
+__device__ __forceinline__ void dma_rows_untracked(const uint16_t* src, uint16_t* lds_group) {
+  const uint32_t lds = (uint32_t)(uintptr_t)MOE_LDS_PTR(lds_group);
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :: "v"(src), "s"(lds) : "memory", "m0");
+}
+
 // Direct-to-LDS load of 8 lines of an MN-major tile (1 KB): lane l fills line
 // l/8, stored chunk l%8, so it fetches logical chunk (l%8) ^ ((k & 3) << 1).
 __device__ __forceinline__ int mn_chunk(int lane, int k) { return (lane & 7) ^ ((k & 3) << 1); }
@@ -104,7 +126,7 @@ struct GemmArgs {
   const int32_t* count;
   const int32_t* seg;         // dW: [G+1] row offsets, or null (dense)
   const int32_t* order;       // dW: segments by descending row count (or null: natural)
-  int* counter;               // dW: tile counter of a persistent launch (or null)
+  int* counter;               // dW: GB_QUEUES tile counters of a persistent launch (or null)
   const int32_t* poff;        // dW from transposed operands: [G+1] padded column offsets
   int64_t dense_rows;
   const uint16_t* zero;       // >= 256 zero elements
@@ -138,137 +160,188 @@ __global__ __launch_bounds__(64 * GB_NW) void bwd_gemm_kernel(GemmArgs a) {
   constexpr int DQ = (QMN ? BK * NLQ : BM) / 8 / NW;
   static_assert(DP * NW * 8 == (PKM ? BN : BK * NLP) && DQ * NW * 8 == (QMN ? BK * NLQ : BM),
                 "load split");
-  // the ring, then two int slots that pass a claimed tile to every wave (one
-  // LDS object: a second one makes the compiler wait for in-flight
-  // direct-to-LDS writes before every operand read)
-  __shared__ __attribute__((aligned(1024))) uint16_t ring[2 * (SP + SQ) + 4];
+  // the ring, then two int slots that pass a claimed tile to every wave, then
+  // (weight gradients) the segment order and row offsets.  One LDS object: a
+  // second one makes the compiler wait for in-flight direct-to-LDS writes
+  // before every operand read.
+  constexpr int TAB = WGRAD ? 2 * GB_MAX_SEGS + 1 : 0;   // ints
+  __shared__ __attribute__((aligned(1024))) uint16_t ring[2 * (SP + SQ) + 4 + 2 * TAB];
   int* const tile_slot = reinterpret_cast<int*>(ring + 2 * (SP + SQ));
+  int* const tab_order = tile_slot + 2;
+  int* const tab_off = tab_order + GB_MAX_SEGS;
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / WN, wn = wave % WN;
 
   // Weight gradients with a tile counter run persistent: one workgroup per CU
-  // claims tiles in order until none is left.  Otherwise one tile per block.
-  for (int it = 0;; ++it) {
-  int e;
-  if (WGRAD && a.counter) {
-    if (tid == 0) tile_slot[it & 1] = atomicAdd(a.counter, 1);
-    wait_lgkm0();
-    ring_barrier();    // also: every wave is done with the previous tile's LDS
-    e = __builtin_amdgcn_readfirstlane(tile_slot[it & 1]);
-  } else {
-    if (it > 0) break;
-    e = blockIdx.x;
-  }
-  // lane id, opaque to the optimiser so that nothing derived from it is
-  // hoisted out of the tile loop (it would stay live across every slab)
-  int lane = tid & 63;
-  asm volatile("" : "+v"(lane));
-  int g, m0, m1, n0, nk, ks = 0, kb0 = 0;
-  int64_t prow0 = 0, qrow0 = 0, klen = 0;
-  if constexpr (WGRAD) {
-    // Longest segments first, so the costliest tiles start first and the
-    // short ones fill in at the end; blocks are dealt round-robin over the
-    // XCDs, so each XCD holds every eighth row block of a segment (its own
-    // slice of the Q operand) while the column blocks stream past.
+  // claims tiles in order until none is left, one tile ahead, so that the
+  // next tile's first two slabs are requested before this tile's stores.
+  // Otherwise one tile per block.
+  const bool persist = WGRAD && a.counter != nullptr;
+  // One tile queue per XCD: workgroups are dispatched round-robin over the
+  // 8 XCDs, so block b runs on XCD b % 8 and takes tiles q, q + 8, q + 16, ...
+  // of queue q = b % 8; the tiles one XCD runs at a time then share their Q
+  // row blocks (and, within a column block, their P block) in its L2.  A
+  // claim is one plain atomic whose result is waited for only where it is
+  // used: the counter's address goes in as a per-lane value, which keeps the
+  // compiler from turning it into a wave-combined atomic that waits for its
+  // own result (and so for every load in flight) at once.
+  // A block whose queue runs dry takes tiles from the next queues.
+  const int nq = gridDim.x < GB_QUEUES ? gridDim.x : GB_QUEUES;
+  int cq = blockIdx.x % nq, hops = 0;
+  int zl = 0;
+  asm volatile("" : "+v"(zl));
+  // the tile of the claim in tile_slot[slot]; every wave calls it after a
+  // barrier that made the claim visible
+  auto claimed_tile = [&](int slot) -> int {
     const int V = a.G * a.MT * a.NT;
-    if (e >= V) break;
-    const int rank = e / (a.MT * a.NT);
-    g = a.order ? a.order[rank] : rank;
-    const int rem = e - rank * a.MT * a.NT;
-    const int nt = rem / a.MT, mt = rem - nt * a.MT;
-    m0 = mt * BM;
-    m1 = m0 + BM < a.M ? m0 + BM : a.M;
-    n0 = nt * BN;
-    if constexpr (PKM) {
-      // transposed operands: the segment's columns start at a multiple of 64
-      // and its padding columns hold zeros
-      prow0 = qrow0 = a.poff[g];
-      klen = a.poff[g + 1] - prow0;
-    } else {
-      const int64_t r0 = a.seg ? a.seg[g] : 0;
-      klen = a.seg ? a.seg[g + 1] - r0 : a.dense_rows;
-      prow0 = (int64_t)g * a.p_row_seg + r0;
-      qrow0 = (int64_t)g * a.q_row_seg + r0;
+    int e = cq + nq * __builtin_amdgcn_readfirstlane(tile_slot[slot]);
+    while (e >= V && hops + 1 < nq) {
+      ++hops;
+      cq = cq + 1 == nq ? 0 : cq + 1;
+      ring_barrier();    // every wave has read the slot
+      if (tid == 0) tile_slot[slot] = atomicAdd(a.counter + cq + zl, 1);
+      wait_lgkm0();
+      ring_barrier();
+      e = cq + nq * __builtin_amdgcn_readfirstlane(tile_slot[slot]);
     }
-    nk = (int)((klen + BK - 1) / BK);
+    return e;
+  };
+  int e0;
+  if (persist) {
+    const int32_t* off = PKM ? a.poff : a.seg;
+    for (int i = tid; i < a.G; i += 64 * NW) tab_order[i] = a.order[i];
+    for (int i = tid; i <= a.G; i += 64 * NW) tab_off[i] = off[i];
+    if (tid == 0) tile_slot[0] = atomicAdd(a.counter + cq + zl, 1);
+    wait_lgkm0();
+    ring_barrier();
+    e0 = claimed_tile(0);
   } else {
-    const int V = a.count[0];
-    if (e >= V) break;
-    // plan order, dealt round-robin over the XCDs: each XCD takes every
-    // eighth row tile of a column tile, so a skewed segment's tiles spread
-    // over the whole chip and each L2 keeps its own slice of the rows
-    const PlanEntry pe = a.plan[e];
-    g = pe.g;
-    m0 = pe.m0;
-    m1 = pe.m1;
-    n0 = (pe.nt & ((1 << 24) - 1)) * BN;
-    ks = pe.nt >> 24;
-    qrow0 = (int64_t)g * a.q_row_seg;
-    // the slabs of this entry: all of them, or part ks of a split pass
-    const int nk_all = KIND == BG_DX && EPI == 1 ? 2 * a.nk1 : a.K / BK;
-    kb0 = (int)((int64_t)nk_all * ks / a.split);
-    nk = (int)((int64_t)nk_all * (ks + 1) / a.split) - kb0;
+    e0 = blockIdx.x;
   }
   const int N = a.N;
+  const int64_t ldp = a.ldp, ldq = a.ldq;
+  const uint16_t* const zp = a.zero;   // every lane may read the same zeros
 
-  // Per-lane load sources.  P: DP instructions of 8 lines; Q: DQ instructions
-  // (8 rows of 64 k, or 8 lines of an MN-major tile).  Instruction i of a
-  // wave fills lines L = (wave + i NW) 8 + lane/8, i.e. k-row k0 + i KSTEP and
-  // line lane/8 % NL of it: the column and the chunk swizzle (k & 3) are the
-  // same for every i.
+  // Per-tile state, set by setup().  Load sources: P in DP instructions of 8
+  // lines, Q in DQ instructions (8 rows of 64 k, or 8 lines of an MN-major
+  // tile).  Instruction i of a wave fills lines L = (wave + i NW) 8 + lane/8,
+  // i.e. k-row k0 + i KSTEP and line lane/8 % NL of it: the column and the
+  // chunk swizzle (k & 3) are the same for every i.  Each lane's sources are
+  // a base pointer (its k-row k0 and column folded in) plus a wave-uniform
+  // offset per slab and instruction.
   static_assert(8 % NLP == 0 && 8 % NLQ == 0, "lines per k-row");
   constexpr int KSP = NW * 8 / NLP, KSQ = NW * 8 / NLQ;
   static_assert(KSP % 4 == 0 && KSQ % 4 == 0, "swizzle must repeat across instructions");
-  const int pk0 = wave * (8 / NLP) + (lane >> 3) / NLP;
-  int pcol = n0 + ((lane >> 3) % NLP) * 64;
-  if (pcol > N - 64) pcol = N - 64;            // past the last column: any valid line
-  pcol += mn_chunk(lane, pk0) * 8;
+  int lane = 0;
+  int g = 0, m0 = 0, m1 = 0, n0 = 0, nk = 0, ks = 0, kb0 = 0, klen32 = 0, pk0 = 0, qk0 = 0;
   int64_t p_off[PKM ? DP : 1];   // K-major P: element offset of this lane's row and chunk
-  if constexpr (PKM) {
-#pragma unroll
-    for (int i = 0; i < DP; ++i) {
-      int r = n0 + (wave + i * NW) * 8 + dma_row(lane);
-      if (r > N - 1) r = N - 1;
-      p_off[i] = r * a.ldp + dma_chunk(lane) * 8 + prow0;
-    }
-  } else {
-    p_off[0] = 0;
-  }
-  int qk0 = 0, qcol = 0;
   int64_t q_off[QMN ? 1 : DQ];   // K-major Q: element offset of this lane's row and chunk
-  if constexpr (QMN) {
-    qk0 = wave * (8 / NLQ) + (lane >> 3) / NLQ;
-    qcol = m0 + ((lane >> 3) % NLQ) * 64;
-    if (qcol > a.M - 64) qcol = a.M - 64;
-    qcol += mn_chunk(lane, qk0) * 8;
-    q_off[0] = 0;
-  } else {
-#pragma unroll
-    for (int i = 0; i < DQ; ++i) {
-      int r = m0 + (wave + i * NW) * 8 + dma_row(lane);
-      if (r > m1 - 1) r = m1 - 1;
-      q_off[i] = PKM ? r * a.ldq + dma_chunk(lane) * 8 + qrow0
-                     : (qrow0 + r) * a.ldq + dma_chunk(lane) * 8;
-    }
-  }
-  // Each lane's sources are a base pointer (its k-row k0 and column folded
-  // in) plus a wave-uniform offset per slab and instruction.
-  const int64_t ldp = a.ldp, ldq = a.ldq;
-  const uint16_t* const zp = a.zero;   // every lane may read the same zeros
-  const uint16_t* pb;    // P at k-row pk0 of slab 0
+  const uint16_t* pb = nullptr;  // P at k-row pk0 of slab 0
   const uint16_t* pb2 = nullptr;
-  if constexpr (PKM) {
-    pb = a.P;
-  } else if constexpr (KIND == BG_DW) {
-    pb = a.P + (prow0 + pk0) * ldp + pcol;
-  } else {
-    pb = a.P + (int64_t)g * a.p_seg + pk0 * ldp + pcol;
-    if constexpr (KIND == BG_DX) pb2 = (a.P2 ? a.P2 : a.P) + (int64_t)g * a.p_seg + pk0 * ldp + pcol;
-  }
-  const uint16_t* qb = QMN ? a.Q + (qrow0 + qk0) * ldq + qcol : a.Q;
-  const int klen32 = (int)klen;
+  const uint16_t* qb = nullptr;
+  auto setup = [&](int e) -> bool {
+    // lane id, opaque to the optimiser so that nothing derived from it is
+    // hoisted out of the tile loop (it would stay live across every slab)
+    lane = tid & 63;
+    asm volatile("" : "+v"(lane));
+    int64_t prow0 = 0, qrow0 = 0, klen = 0;
+    ks = 0;
+    kb0 = 0;
+    if constexpr (WGRAD) {
+      // Longest segments first, so the costliest tiles start first and the
+      // short ones fill in at the end; within a segment, row blocks vary
+      // fastest, so an XCD's queue holds every eighth row block (its own
+      // slice of the Q operand) while the column blocks stream past.
+      const int V = a.G * a.MT * a.NT;
+      if (e >= V) return false;
+      const int rank = e / (a.MT * a.NT);
+      const int rem = e - rank * a.MT * a.NT;
+      const int nt = rem / a.MT, mt = rem - nt * a.MT;
+      m0 = mt * BM;
+      m1 = m0 + BM < a.M ? m0 + BM : a.M;
+      n0 = nt * BN;
+      if (persist) {
+        g = __builtin_amdgcn_readfirstlane(tab_order[rank]);
+        const int o0 = __builtin_amdgcn_readfirstlane(tab_off[g]);
+        klen = __builtin_amdgcn_readfirstlane(tab_off[g + 1]) - o0;
+        if constexpr (PKM) {
+          // transposed operands: the segment's columns start at a multiple
+          // of 64 and its padding columns hold zeros
+          prow0 = qrow0 = o0;
+        } else {
+          prow0 = (int64_t)g * a.p_row_seg + o0;
+          qrow0 = (int64_t)g * a.q_row_seg + o0;
+        }
+      } else if constexpr (!PKM) {
+        g = rank;
+        const int64_t r0 = a.seg ? a.seg[g] : 0;
+        klen = a.seg ? a.seg[g + 1] - r0 : a.dense_rows;
+        prow0 = (int64_t)g * a.p_row_seg + r0;
+        qrow0 = (int64_t)g * a.q_row_seg + r0;
+      }
+      nk = (int)((klen + BK - 1) / BK);
+    } else {
+      const int V = a.count[0];
+      if (e >= V) return false;
+      // plan order, dealt round-robin over the XCDs: each XCD takes every
+      // eighth row tile of a column tile, so a skewed segment's tiles spread
+      // over the whole chip and each L2 keeps its own slice of the rows
+      const PlanEntry pe = a.plan[e];
+      g = pe.g;
+      m0 = pe.m0;
+      m1 = pe.m1;
+      n0 = (pe.nt & ((1 << 24) - 1)) * BN;
+      ks = pe.nt >> 24;
+      qrow0 = (int64_t)g * a.q_row_seg;
+      // the slabs of this entry: all of them, or part ks of a split pass
+      const int nk_all = KIND == BG_DX && EPI == 1 ? 2 * a.nk1 : a.K / BK;
+      kb0 = (int)((int64_t)nk_all * ks / a.split);
+      nk = (int)((int64_t)nk_all * (ks + 1) / a.split) - kb0;
+    }
+    klen32 = (int)klen;
+    pk0 = wave * (8 / NLP) + (lane >> 3) / NLP;
+    int pcol = n0 + ((lane >> 3) % NLP) * 64;
+    if (pcol > N - 64) pcol = N - 64;            // past the last column: any valid line
+    pcol += mn_chunk(lane, pk0) * 8;
+    if constexpr (PKM) {
+#pragma unroll
+      for (int i = 0; i < DP; ++i) {
+        int r = n0 + (wave + i * NW) * 8 + dma_row(lane);
+        if (r > N - 1) r = N - 1;
+        p_off[i] = r * ldp + dma_chunk(lane) * 8 + prow0;
+      }
+    } else {
+      p_off[0] = 0;
+    }
+    int qcol = 0;
+    if constexpr (QMN) {
+      qk0 = wave * (8 / NLQ) + (lane >> 3) / NLQ;
+      qcol = m0 + ((lane >> 3) % NLQ) * 64;
+      if (qcol > a.M - 64) qcol = a.M - 64;
+      qcol += mn_chunk(lane, qk0) * 8;
+      q_off[0] = 0;
+    } else {
+#pragma unroll
+      for (int i = 0; i < DQ; ++i) {
+        int r = m0 + (wave + i * NW) * 8 + dma_row(lane);
+        if (r > m1 - 1) r = m1 - 1;
+        q_off[i] = PKM ? r * ldq + dma_chunk(lane) * 8 + qrow0
+                       : (qrow0 + r) * ldq + dma_chunk(lane) * 8;
+      }
+    }
+    if constexpr (PKM) {
+      pb = a.P;
+    } else if constexpr (KIND == BG_DW) {
+      pb = a.P + (prow0 + pk0) * ldp + pcol;
+    } else {
+      pb = a.P + (int64_t)g * a.p_seg + pk0 * ldp + pcol;
+      if constexpr (KIND == BG_DX) pb2 = (a.P2 ? a.P2 : a.P) + (int64_t)g * a.p_seg + pk0 * ldp + pcol;
+    }
+    qb = QMN ? a.Q + (qrow0 + qk0) * ldq + qcol : a.Q;
+    return true;
+  };
 
   auto issue = [&](int ktr, int stage) {
     uint16_t* sp = ring + stage * (SP + SQ);
@@ -281,7 +354,8 @@ __global__ __launch_bounds__(64 * GB_NW) void bwd_gemm_kernel(GemmArgs a) {
       const int kr = kb + i * KSP;                         // uniform
       const uint16_t* src = PKM ? pb + p_off[i] + kb : (second ? pb2 : pb) + (int64_t)kr * ldp;
       if constexpr (KIND == BG_DW) src = pk0 + kr < klen32 ? src : zp;
-      dma_rows(src, sp + (wave + i * NW) * 512);
+      if constexpr (PKM) dma_rows(src, sp + (wave + i * NW) * 512);
+      else dma_rows_untracked(src, sp + (wave + i * NW) * 512);
     }
 #pragma unroll
     for (int i = 0; i < DQ; ++i) {
@@ -292,15 +366,10 @@ __global__ __launch_bounds__(64 * GB_NW) void bwd_gemm_kernel(GemmArgs a) {
       } else {
         src = (second ? a.Q2 : a.Q) + q_off[i] + kb;
       }
-      dma_rows(src, sq + (wave + i * NW) * 512);
+      if constexpr (PKM) dma_rows(src, sq + (wave + i * NW) * 512);
+      else dma_rows_untracked(src, sq + (wave + i * NW) * 512);
     }
   };
-
-  f32x4_t acc[TM][TN];
-#pragma unroll
-  for (int i = 0; i < TM; ++i)
-#pragma unroll
-    for (int j = 0; j < TN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   // Software pipeline over 64-k slabs in a 2-stage LDS ring, each slab used
   // in two halves of 32 k.  Step kt: (A) MFMAs of half 0 of slab kt with the
@@ -332,126 +401,203 @@ __global__ __launch_bounds__(64 * GB_NW) void bwd_gemm_kernel(GemmArgs a) {
       }
     }
   };
-  auto mfma_half = [&](const bf16x8_t* fp, const bf16x8_t* fq) {
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-      for (int j = 0; j < TN; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fp[j], fq[i], acc[i][j], 0, 0, 0);
-  };
+
+  if (!setup(e0)) return;
   if (nk > 0) {
     issue(0, 0);
     issue(1 < nk ? 1 : 0, 1);
-    wait_vm_lgkm0<DPW>();      // slab 0 has landed (slab 1 may be in flight)
-    ring_barrier();
-    bf16x8_t p0[TN], q0[TM], p1[TN], q1[TM];
-    read_half(ring, 0, p0, q0);
-    for (int kt = 0; kt < nk; ++kt) {
-      const uint16_t* cur = ring + (kt & 1) * (SP + SQ);
-      const uint16_t* nxt = ring + ((kt + 1) & 1) * (SP + SQ);
-      // (A)
-      read_half(cur, 1, p1, q1);
-      mfma_half(p0, q0);
-#pragma unroll
-      for (int r = 0; r < NRD; ++r) {
-        __builtin_amdgcn_sched_group_barrier(0x008, PER, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      }
-      if (NM > NRD * PER) __builtin_amdgcn_sched_group_barrier(0x008, NM - NRD * PER, 0);
-      // (B)
-      wait_vm_lgkm0<0>();
-      ring_barrier();
-      issue(kt + 2 < nk ? kt + 2 : nk - 1, kt & 1);
-      // (C)
-      read_half(nxt, 0, p0, q0);
-      mfma_half(p1, q1);
-#pragma unroll
-      for (int r = 0; r < NRD; ++r) {
-        if (r < DPW) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, PER, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      }
-      if (NM > NRD * PER) __builtin_amdgcn_sched_group_barrier(0x008, NM - NRD * PER, 0);
-    }
   }
-  wait_vm_lgkm0<0>();
-
-  // epilogue: lane holds output columns 4*(lane/16)+q of tile j, row lane%16
-  // of tile i.  dH: the saved pre-activations of row block i+1 are requested
-  // before block i is finished, so their latency overlaps the stores.
-  const int64_t crow0 = WGRAD ? 0 : (int64_t)g * a.c_row_seg;
-  uint16_t* const cbase = a.C + (WGRAD ? (int64_t)g * a.c_seg : 0);
-  constexpr bool LOADS = KIND == BG_DH && EPI != 0;
-  uint2 s1v[2][TN], s2v[2][TN];
-  auto load_saved = [&](int i, int buf) {
-    const int m = m0 + wm * BMW + i * 16 + (lane & 15);
-    const int64_t row = (crow0 + m) * a.ldc;
+  int claim = 0;   // thread 0: the tile after the current one
+  if (persist && tid == 0) claim = atomicAdd(a.counter + cq + zl, 1);
+  // The previous tile's epilogue issued exactly NSTORE stores per wave after
+  // this tile's first two slabs (it was a whole tile), so the wait for slab 0
+  // may leave them in flight: vector memory operations complete in order.
+  constexpr int NSTORE = WGRAD ? 2 * TM : TM * TN;   // stores per wave of a whole tile
+  bool exact = false;
+  for (int it = 0;; ++it) {
+    f32x4_t acc[TM][TN];
 #pragma unroll
-    for (int j = 0; j < TN; ++j) {
-      const int col = n0 + wn * BNW + j * 16 + 4 * (lane >> 4);
-      const bool ok = m < m1 && col < N;
-      s1v[buf][j] = ok ? *reinterpret_cast<const uint2*>(a.S1 + row + col) : uint2{0u, 0u};
-      if constexpr (EPI == 3)
-        s2v[buf][j] = ok ? *reinterpret_cast<const uint2*>(a.S2 + row + col) : uint2{0u, 0u};
-    }
-  };
-  if constexpr (LOADS) load_saved(0, 0);
+    for (int i = 0; i < TM; ++i)
 #pragma unroll
-  for (int i = 0; i < TM; ++i) {
-    if constexpr (LOADS) {
-      if (i + 1 < TM) load_saved(i + 1, (i + 1) & 1);
-    }
-    const int m = m0 + wm * BMW + i * 16 + (lane & 15);
-    if (m >= m1) continue;
-    const int64_t row = (crow0 + m) * a.ldc;
+      for (int j = 0; j < TN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    auto mfma_half = [&](const bf16x8_t* fp, const bf16x8_t* fq) {
 #pragma unroll
-    for (int j = 0; j < TN; ++j) {
-      const int col = n0 + wn * BNW + j * 16 + 4 * (lane >> 4);
-      if (col >= N) continue;
-      float v[4] = {acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]};
-      if constexpr (KIND == BG_DX) {
-        if (a.part) {   // split pass: fp32 partial of part ks, added by the dx kernel
-          *reinterpret_cast<f32x4_t*>(a.part + ks * a.part_stride + row + col) =
-              f32x4_t{v[0], v[1], v[2], v[3]};
-          continue;
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fp[j], fq[i], acc[i][j], 0, 0, 0);
+    };
+    if (nk > 0) {
+      // slab 0 has landed (slab 1, the claim and the stores may be in flight)
+      if (exact) wait_vm_lgkm0<DPW + NSTORE>();
+      else wait_vm_lgkm0<DPW>();
+      ring_barrier();
+      bf16x8_t p0[TN], q0[TM], p1[TN], q1[TM];
+      read_half(ring, 0, p0, q0);
+      for (int kt = 0; kt < nk; ++kt) {
+        const uint16_t* cur = ring + (kt & 1) * (SP + SQ);
+        const uint16_t* nxt = ring + ((kt + 1) & 1) * (SP + SQ);
+        // (A)
+        read_half(cur, 1, p1, q1);
+        mfma_half(p0, q0);
+#pragma unroll
+        for (int r = 0; r < NRD; ++r) {
+          __builtin_amdgcn_sched_group_barrier(0x008, PER, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         }
+        if (NM > NRD * PER) __builtin_amdgcn_sched_group_barrier(0x008, NM - NRD * PER, 0);
+        // (B)
+        wait_vm_lgkm0<0>();
+        ring_barrier();
+        issue(kt + 2 < nk ? kt + 2 : nk - 1, kt & 1);
+        // (C)
+        read_half(nxt, 0, p0, q0);
+        mfma_half(p1, q1);
+#pragma unroll
+        for (int r = 0; r < NRD; ++r) {
+          if (r < DPW) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, PER, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        if (NM > NRD * PER) __builtin_amdgcn_sched_group_barrier(0x008, NM - NRD * PER, 0);
       }
+    }
+    wait_vm_lgkm0<0>();
+
+    // this tile's output block; then (persistent) the next tile's slabs are
+    // requested before the stores
+    const int cg = g, cm0 = m0, cm1 = m1, cn0 = n0, cks = ks;
+    bool more = false;
+    // Weight gradients: the block leaves through LDS.  In registers lane
+    // (r, c) = (lane % 16, lane / 16) holds columns 16 j + 4 c .. +3 of row r;
+    // each wave parks its 128 x 64 block in the idle ring (rows of 128 bytes,
+    // 16-byte chunks XOR-swizzled by the row) and reads it back as 16-byte
+    // pieces, 8 lanes to a row, so that each store writes whole 128-byte row
+    // segments with consecutive lanes on consecutive bytes.
+    u32x4_t stv[WGRAD ? 2 * TM : 1];
+    if constexpr (WGRAD) {
+      if (persist && tid == 0) tile_slot[(it + 1) & 1] = claim;
+      wait_lgkm0();
+      ring_barrier();    // every wave is done with the ring; the claim is visible
+      uint16_t* const st = ring + wave * (BMW * BNW);
+      static_assert(BNW == 64 && NW * BMW * BNW <= 2 * (SP + SQ), "staging fits the ring");
+      const int r = lane & 15, c = lane >> 4;
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+          uint2 pk;
+          pk.x = pack_bf16x2(acc[i][j][0], acc[i][j][1]);
+          pk.y = pack_bf16x2(acc[i][j][2], acc[i][j][3]);
+          const int row = i * 16 + r;
+          *reinterpret_cast<uint2*>(st + row * 64 + (((2 * j + (c >> 1)) ^ (row & 7)) << 3) + (c & 1) * 4) = pk;
+        }
+#pragma unroll
+      for (int t = 0; t < 2 * TM; ++t) {
+        const int row = t * 8 + (lane >> 3);
+        stv[t] = *reinterpret_cast<const u32x4_t*>(st + row * 64 + (((lane & 7) ^ (row & 7)) << 3));
+      }
+      wait_lgkm0();
+      ring_barrier();    // every wave has its rows back
+    }
+    if (persist) {
+      more = setup(claimed_tile((it + 1) & 1));
+      if (more) {
+        if (nk > 0) {
+          issue(0, 0);
+          issue(1 < nk ? 1 : 0, 1);
+        }
+        if (tid == 0) claim = atomicAdd(a.counter + cq + zl, 1);
+      }
+    }
+
+    // epilogue: lane holds output columns 4*(lane/16)+q of tile j, row lane%16
+    // of tile i.  dH: the saved pre-activations of row block i+1 are requested
+    // before block i is finished, so their latency overlaps the stores.
+    const int64_t crow0 = WGRAD ? 0 : (int64_t)cg * a.c_row_seg;
+    uint16_t* const cbase = a.C + (WGRAD ? (int64_t)cg * a.c_seg : 0);
+    constexpr bool LOADS = KIND == BG_DH && EPI != 0;
+    uint2 s1v[2][TN], s2v[2][TN];
+    auto load_saved = [&](int i, int buf) {
+      const int m = cm0 + wm * BMW + i * 16 + (lane & 15);
+      const int64_t row = (crow0 + m) * a.ldc;
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const int col = cn0 + wn * BNW + j * 16 + 4 * (lane >> 4);
+        const bool ok = m < cm1 && col < N;
+        s1v[buf][j] = ok ? *reinterpret_cast<const uint2*>(a.S1 + row + col) : uint2{0u, 0u};
+        if constexpr (EPI == 3)
+          s2v[buf][j] = ok ? *reinterpret_cast<const uint2*>(a.S2 + row + col) : uint2{0u, 0u};
+      }
+    };
+    if constexpr (WGRAD) {
+#pragma unroll
+      for (int t = 0; t < 2 * TM; ++t) {
+        const int m = cm0 + wm * BMW + t * 8 + (lane >> 3);
+        const int col = cn0 + wn * BNW + 8 * (lane & 7);
+        if (m < cm1 && col < N) *reinterpret_cast<u32x4_t*>(cbase + (int64_t)m * a.ldc + col) = stv[t];
+      }
+    } else {
+    if constexpr (LOADS) load_saved(0, 0);
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
       if constexpr (LOADS) {
-        // activation backward with the saved pre-activations
-        const uint2 s1 = s1v[i & 1][j];
-        const uint32_t z32[4] = {s1.x & 0xffffu, s1.x >> 16, s1.y & 0xffffu, s1.y >> 16};
-        if constexpr (EPI == 3) {
-          const uint2 s2 = s2v[i & 1][j];
-          const uint32_t u32[4] = {s2.x & 0xffffu, s2.x >> 16, s2.y & 0xffffu, s2.y >> 16};
-          float dg[4], du[4];
+        if (i + 1 < TM) load_saved(i + 1, (i + 1) & 1);
+      }
+      const int m = cm0 + wm * BMW + i * 16 + (lane & 15);
+      if (m >= cm1) continue;
+      const int64_t row = (crow0 + m) * a.ldc;
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const int col = cn0 + wn * BNW + j * 16 + 4 * (lane >> 4);
+        if (col >= N) continue;
+        float v[4] = {acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]};
+        if constexpr (KIND == BG_DX) {
+          if (a.part) {   // split pass: fp32 partial of part ks, added by the dx kernel
+            *reinterpret_cast<f32x4_t*>(a.part + cks * a.part_stride + row + col) =
+                f32x4_t{v[0], v[1], v[2], v[3]};
+            continue;
+          }
+        }
+        if constexpr (LOADS) {
+          // activation backward with the saved pre-activations
+          const uint2 s1 = s1v[i & 1][j];
+          const uint32_t z32[4] = {s1.x & 0xffffu, s1.x >> 16, s1.y & 0xffffu, s1.y >> 16};
+          if constexpr (EPI == 3) {
+            const uint2 s2 = s2v[i & 1][j];
+            const uint32_t u32[4] = {s2.x & 0xffffu, s2.x >> 16, s2.y & 0xffffu, s2.y >> 16};
+            float dg[4], du[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const float z = bf16_to_f32(z32[q]), u = bf16_to_f32(u32[q]);
+              const float sg = sigm(z);
+              du[q] = v[q] * z * sg;
+              dg[q] = v[q] * u * sg * (1.0f + z * (1.0f - sg));
+            }
+            uint2 pg, pu;
+            pg.x = pack_bf16x2(dg[0], dg[1]);
+            pg.y = pack_bf16x2(dg[2], dg[3]);
+            pu.x = pack_bf16x2(du[0], du[1]);
+            pu.y = pack_bf16x2(du[2], du[3]);
+            *reinterpret_cast<uint2*>(cbase + row + col) = pg;
+            *reinterpret_cast<uint2*>(a.C2 + row + col) = pu;
+            continue;
+          }
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
-            const float z = bf16_to_f32(z32[q]), u = bf16_to_f32(u32[q]);
-            const float sg = sigm(z);
-            du[q] = v[q] * z * sg;
-            dg[q] = v[q] * u * sg * (1.0f + z * (1.0f - sg));
+            const float z = bf16_to_f32(z32[q]);
+            v[q] = EPI == 1 ? (z > 0.f ? v[q] : 0.f) : v[q] * gelu_grad(z);
           }
-          uint2 pg, pu;
-          pg.x = pack_bf16x2(dg[0], dg[1]);
-          pg.y = pack_bf16x2(dg[2], dg[3]);
-          pu.x = pack_bf16x2(du[0], du[1]);
-          pu.y = pack_bf16x2(du[2], du[3]);
-          *reinterpret_cast<uint2*>(cbase + row + col) = pg;
-          *reinterpret_cast<uint2*>(a.C2 + row + col) = pu;
-          continue;
         }
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const float z = bf16_to_f32(z32[q]);
-          v[q] = EPI == 1 ? (z > 0.f ? v[q] : 0.f) : v[q] * gelu_grad(z);
-        }
+        uint2 pk;
+        pk.x = pack_bf16x2(v[0], v[1]);
+        pk.y = pack_bf16x2(v[2], v[3]);
+        *reinterpret_cast<uint2*>(cbase + row + col) = pk;
       }
-      uint2 pk;
-      pk.x = pack_bf16x2(v[0], v[1]);
-      pk.y = pack_bf16x2(v[2], v[3]);
-      *reinterpret_cast<uint2*>(cbase + row + col) = pk;
     }
-  }
+    }
+    exact = cm1 - cm0 == BM && cn0 + BN <= N;
+    if (!more) break;
   }  // tiles
 }
 
@@ -801,11 +947,12 @@ __global__ __launch_bounds__(256) void transpose_pad_kernel(const uint16_t* __re
   }
 }
 
-// order[r] = the segment with the r-th largest row count (ties: lower index).
+// order[r] = the segment with the r-th largest row count (ties: lower index);
+// also clears the tile counters of the launch that follows.
 __global__ __launch_bounds__(256) void seg_order_kernel(const int32_t* seg, int G, int32_t* order,
                                                         int* counter) {
   __shared__ int len[1024];
-  if (threadIdx.x == 0) *counter = 0;
+  if (threadIdx.x < GB_QUEUES) counter[threadIdx.x] = 0;
   for (int g = threadIdx.x; g < G; g += 256) len[g] = seg[g + 1] - seg[g];
   __syncthreads();
   for (int g = threadIdx.x; g < G; g += 256) {
@@ -909,9 +1056,9 @@ hipError_t launch_bwd_gemm(const BwdGemm& b, hipStream_t s) {
   a.seg = b.seg;
   a.poff = b.poff;
   a.order = b.seg ? b.order : nullptr;
-  a.counter = b.seg && b.order ? b.order + b.G : nullptr;   // the int after the order
+  a.counter = b.seg && b.order ? b.order + b.G : nullptr;   // the ints after the order
   if (a.order) {
-    if (b.G > 1024) return hipErrorInvalidValue;
+    if (b.G > GB_MAX_SEGS) return hipErrorInvalidValue;
     seg_order_kernel<<<1, 256, 0, s>>>(b.seg, b.G, b.order, a.counter);
   }
   a.dense_rows = b.dense_rows;

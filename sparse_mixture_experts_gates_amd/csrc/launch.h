@@ -170,8 +170,8 @@ struct BwdGemm {
   int64_t max_entries;     // grid of a plan-driven launch
   const int32_t* seg;      // BG_DW: [G+1] row offsets or null (dense_rows each)
   const int32_t* poff;     // BG_DWT: [G+1] padded column offsets (launch_pad_offsets)
-  int32_t* order;          // BG_DW with seg: [G + 1] scratch: the longest-first segment
-                           // order, then the tile counter of the persistent launch
+  int32_t* order;          // BG_DW with seg: [G + 8] scratch: the longest-first segment
+                           // order, then the 8 tile counters of the persistent launch
   int64_t dense_rows;
   const void* zero;        // BG_DW: >= 64 zero bf16 elements (16-byte aligned)
   int K, N, M, G;

@@ -240,7 +240,7 @@ BwdWs bwd_ws(const moe_config_t* c, int64_t T) {
     o += bwd_plan_bytes(ST, S, c->d);
   }
   w.wr = o; o += up(wr_ws_bytes(T, c->num_experts, c->d));
-  w.order = o; o += up((size_t)(c->num_experts + 1) * 4);
+  w.order = o; o += up((size_t)(c->num_experts + 8) * 4);
   // transposed operands of the routed weight gradients: each expert's rows
   // padded to a multiple of 64 columns
   w.ldt = (R + 63 * (int64_t)c->num_experts + 63) / 64 * 64;
