@@ -482,6 +482,10 @@ __global__ __launch_bounds__(64 * GB_NW) void bwd_gemm_kernel(GemmArgs a) {
       uint16_t* const st = ring + wave * (BMW * BNW);
       static_assert(BNW == 64 && NW * BMW * BNW <= 2 * (SP + SQ), "staging fits the ring");
       const int r = lane & 15, c = lane >> 4;
+      if (nk == 0) {   // a segment without rows: its block is zero
+#pragma unroll
+        for (int t = 0; t < 2 * TM; ++t) stv[t] = u32x4_t{0u, 0u, 0u, 0u};
+      } else {
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -499,6 +503,7 @@ __global__ __launch_bounds__(64 * GB_NW) void bwd_gemm_kernel(GemmArgs a) {
       }
       wait_lgkm0();
       ring_barrier();    // every wave has its rows back
+      }
     }
     if (persist) {
       more = setup(claimed_tile((it + 1) & 1));
