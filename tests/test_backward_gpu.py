@@ -69,6 +69,12 @@ CASES = {
     # few row tiles and a long K: the dX GEMM runs in 4 K parts (fp32 partials)
     "split_k_dx": small(T=300, d=256, d_ff=2048),
     "split_k_dx_gelu": small(T=300, d=320, d_ff=4096, act="gelu", E=4),
+    # more weight-gradient tiles than CUs, so each persistent block runs
+    # several in a row: ragged tiles in both dimensions (640 = 2.5 x 256,
+    # 1600 = 6.25 x 256) between whole ones, and (second case) mostly
+    # experts without rows, whose blocks are zero tiles
+    "multi_tile_ragged": small(T=512, d=640, E=32, k=2, d_ff=1600),
+    "multi_tile_idle": small(T=96, d=640, E=64, k=1, d_ff=1600, act="gelu"),
 }
 AUX = {"deepseek_like_shared_bias": 0.05, "gelu_sigmoid_capacity": 0.02,
        "all_dropped_shared": 0.1, "max_E256_k16": 0.03}
