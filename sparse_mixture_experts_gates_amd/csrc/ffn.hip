@@ -160,9 +160,12 @@ void ffn_bf16_kernel(KArgs a) {
   constexpr int LDS_ELEMS = NSTAGE == 2 ? 2 * BM * BK + NSB * BN * BK : NSTAGE * SEL;
   // One LDS object only (a second one makes the compiler assume the operand
   // reads may alias the in-flight direct-to-LDS writes and wait for them);
-  // the two int slots after the ring pass the next tile id to every wave.
-  __shared__ __attribute__((aligned(1024))) uint16_t ring[LDS_ELEMS + 4];
-  int* const tile_slot = reinterpret_cast<int*>(ring + LDS_ELEMS);
+  // two int slots pass the next tile id to every wave: after the ring, or,
+  // when the ring fills the 160 KB, at its start (the ring is idle between
+  // tiles; every wave reads the slot before the next slabs are requested).
+  constexpr bool SLOT_IN_RING = (LDS_ELEMS + 4) * 2 > 160 * 1024;
+  __shared__ __attribute__((aligned(1024))) uint16_t ring[LDS_ELEMS + (SLOT_IN_RING ? 0 : 4)];
+  int* const tile_slot = reinterpret_cast<int*>(ring + (SLOT_IN_RING ? 0 : LDS_ELEMS));
 
   const int V = a.count[0];
   const int P = blockIdx.x;
@@ -193,6 +196,7 @@ void ffn_bf16_kernel(KArgs a) {
     wait_lgkm0();
     ring_barrier();
     e = __builtin_amdgcn_readfirstlane(tile_slot[it & 1]);
+    if constexpr (SLOT_IN_RING) ring_barrier();   // read before the ring is refilled
     if (e < 0) break;
   } else {
     if (it > 0 || P >= V) break;
@@ -758,8 +762,8 @@ hipError_t launch_ffn_pass(const FfnPassArgs& p, hipStream_t s) {
     if (grid >= 2 * (int64_t)cus) {
       if (sh.id == 3) launch_bf16<256, 128, 4, 2, 3, 3, true>(p.mode, (unsigned)cus, k, s);
       else if (split > 1)
-        ffn_bf16_kernel<256, 256, 2, 4, 2, 2, MODE_PLAIN, true, true><<<(unsigned)cus, 512, 0, s>>>(k);
-      else launch_bf16<256, 256, 2, 4, 2, 2, true>(p.mode, (unsigned)cus, k, s);
+        ffn_bf16_kernel<256, 256, 2, 4, 2, 3, MODE_PLAIN, true, true><<<(unsigned)cus, 512, 0, s>>>(k);
+      else launch_bf16<256, 256, 2, 4, 2, 3, true>(p.mode, (unsigned)cus, k, s);
     } else {
       if (sh.id == 3) launch_bf16<256, 128, 4, 2, 3, 3, false>(p.mode, (unsigned)grid, k, s);
       else if (split > 1)
