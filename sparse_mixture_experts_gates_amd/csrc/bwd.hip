@@ -165,8 +165,20 @@ __global__ __launch_bounds__(64 * GB_NW) void bwd_gemm_kernel(GemmArgs a) {
   // second one makes the compiler wait for in-flight direct-to-LDS writes
   // before every operand read.
   constexpr int TAB = WGRAD ? 2 * GB_MAX_SEGS + 1 : 0;   // ints
-  __shared__ __attribute__((aligned(1024))) uint16_t ring[2 * (SP + SQ) + 4 + 2 * TAB];
-  int* const tile_slot = reinterpret_cast<int*>(ring + 2 * (SP + SQ));
+  // P stages: three for dH, whose P is a weight streamed from HBM (its slabs
+  // are requested two ahead; the rings then fill the 160 KB), two otherwise
+  // (a third made dX slower)
+  constexpr int NSP = KIND == BG_DH ? 3 : 2;
+  constexpr int RING = NSP * SP + 2 * SQ;
+  __shared__ __attribute__((aligned(1024))) uint16_t ring[RING + (WGRAD ? 4 + 2 * TAB : 0)];
+  // stages: the P stages, then the Q stages; dX keeps each stage's P and Q
+  // side by side, which measured faster for it (and slower for the others)
+  constexpr bool ILV = KIND == BG_DX;
+  static_assert(!ILV || NSP == 2, "interleaved stages hold one P and one Q slab each");
+  constexpr int P_STRIDE = ILV ? SP + SQ : SP, Q_STRIDE = ILV ? SP + SQ : SQ;
+  uint16_t* const ring_p = ring;
+  uint16_t* const ring_q = ring + (ILV ? SP : NSP * SP);
+  int* const tile_slot = reinterpret_cast<int*>(ring + RING);   // weight gradients only
   int* const tab_order = tile_slot + 2;
   int* const tab_off = tab_order + GB_MAX_SEGS;
 
@@ -343,9 +355,9 @@ __global__ __launch_bounds__(64 * GB_NW) void bwd_gemm_kernel(GemmArgs a) {
     return true;
   };
 
-  auto issue = [&](int ktr, int stage) {
-    uint16_t* sp = ring + stage * (SP + SQ);
-    uint16_t* sq = sp + SP;
+  // requests for slab ktr (relative to the tile's first slab) of P, of Q
+  auto issue_p = [&](int ktr, int stage) {
+    uint16_t* sp = ring_p + stage * P_STRIDE;
     const int kt = ktr + kb0;                              // slab index within K
     const bool second = KIND == BG_DX && kt >= a.nk1;
     const int kb = (second ? kt - a.nk1 : kt) * BK;      // first k-row of the slab
@@ -357,6 +369,12 @@ __global__ __launch_bounds__(64 * GB_NW) void bwd_gemm_kernel(GemmArgs a) {
       if constexpr (PKM) dma_rows(src, sp + (wave + i * NW) * 512);
       else dma_rows_untracked(src, sp + (wave + i * NW) * 512);
     }
+  };
+  auto issue_q = [&](int ktr, int stage) {
+    uint16_t* sq = ring_q + stage * Q_STRIDE;
+    const int kt = ktr + kb0;
+    const bool second = KIND == BG_DX && kt >= a.nk1;
+    const int kb = (second ? kt - a.nk1 : kt) * BK;
 #pragma unroll
     for (int i = 0; i < DQ; ++i) {
       const uint16_t* src;
@@ -370,18 +388,27 @@ __global__ __launch_bounds__(64 * GB_NW) void bwd_gemm_kernel(GemmArgs a) {
       else dma_rows_untracked(src, sq + (wave + i * NW) * 512);
     }
   };
+  // the tile's first slabs: P and Q of slabs 0 and 1, then (three P stages)
+  // P of slab 2; past the last slab the requests reload it (harmless)
+  auto prologue = [&]() {
+    issue_p(0, 0);
+    issue_q(0, 0);
+    issue_p(1 < nk ? 1 : 0, 1);
+    issue_q(1 < nk ? 1 : 0, 1);
+    if constexpr (NSP == 3) issue_p(2 < nk ? 2 : nk - 1, 2);
+  };
 
-  // Software pipeline over 64-k slabs in a 2-stage LDS ring, each slab used
-  // in two halves of 32 k.  Step kt: (A) MFMAs of half 0 of slab kt with the
-  // reads of half 1 spread between them; (B) wait for slab kt+1, barrier,
-  // request slab kt+2 into the stage slab kt held; (C) MFMAs of half 1 with
-  // the reads of half 0 of slab kt+1 (and the new requests) spread between
-  // them.  Past the last slab the requests reload it (harmless).
+  // Software pipeline over 64-k slabs in LDS rings (Q: 2 stages, P: NSP),
+  // each slab used in two halves of 32 k.  Step kt: (A) MFMAs of half 0 of
+  // slab kt with the reads of half 1 spread between them; (B) wait for slab
+  // kt+1, barrier, request Q of slab kt+2 and P of slab kt+NSP into the
+  // stages slab kt held; (C) MFMAs of half 1 with the reads of half 0 of
+  // slab kt+1 (and the new requests) spread between them.  Past the last
+  // slab the requests reload it (harmless).
   constexpr int NRD = (PKM ? 1 : 2) * TN + (QMN ? 2 : 1) * TM;   // LDS read instructions per half
   constexpr int NM = TM * TN, PER = NM / NRD > 0 ? NM / NRD : 1;
   constexpr int DPW = DP + DQ;
-  auto read_half = [&](const uint16_t* sp, int kk, bf16x8_t* fp, bf16x8_t* fq) {
-    const uint16_t* sq = sp + SP;
+  auto read_half = [&](const uint16_t* sp, const uint16_t* sq, int kk, bf16x8_t* fp, bf16x8_t* fq) {
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
       if constexpr (PKM) {
@@ -403,10 +430,7 @@ __global__ __launch_bounds__(64 * GB_NW) void bwd_gemm_kernel(GemmArgs a) {
   };
 
   if (!setup(e0)) return;
-  if (nk > 0) {
-    issue(0, 0);
-    issue(1 < nk ? 1 : 0, 1);
-  }
+  if (nk > 0) prologue();
   int claim = 0;   // thread 0: the tile after the current one
   if (persist && tid == 0) claim = atomicAdd(a.counter + cq + zl, 1);
   // The previous tile's epilogue issued exactly NSTORE stores per wave after
@@ -428,17 +452,17 @@ __global__ __launch_bounds__(64 * GB_NW) void bwd_gemm_kernel(GemmArgs a) {
           acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fp[j], fq[i], acc[i][j], 0, 0, 0);
     };
     if (nk > 0) {
-      // slab 0 has landed (slab 1, the claim and the stores may be in flight)
-      if (exact) wait_vm_lgkm0<DPW + NSTORE>();
-      else wait_vm_lgkm0<DPW>();
+      // slab 0 has landed (slab 1, P of slab 2, the claim and the stores may
+      // be in flight)
+      if (exact) wait_vm_lgkm0<DPW + (NSP - 2) * DP + NSTORE>();
+      else wait_vm_lgkm0<DPW + (NSP - 2) * DP>();
       ring_barrier();
       bf16x8_t p0[TN], q0[TM], p1[TN], q1[TM];
-      read_half(ring, 0, p0, q0);
+      read_half(ring_p, ring_q, 0, p0, q0);
+      int sp_cur = 0, sp_nxt = 1;   // P stages of slabs kt and kt+1
       for (int kt = 0; kt < nk; ++kt) {
-        const uint16_t* cur = ring + (kt & 1) * (SP + SQ);
-        const uint16_t* nxt = ring + ((kt + 1) & 1) * (SP + SQ);
         // (A)
-        read_half(cur, 1, p1, q1);
+        read_half(ring_p + sp_cur * P_STRIDE, ring_q + (kt & 1) * Q_STRIDE, 1, p1, q1);
         mfma_half(p0, q0);
 #pragma unroll
         for (int r = 0; r < NRD; ++r) {
@@ -446,12 +470,13 @@ __global__ __launch_bounds__(64 * GB_NW) void bwd_gemm_kernel(GemmArgs a) {
           __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         }
         if (NM > NRD * PER) __builtin_amdgcn_sched_group_barrier(0x008, NM - NRD * PER, 0);
-        // (B)
-        wait_vm_lgkm0<0>();
+        // (B) slab kt+1 has landed once only P of slab kt+2 may remain
+        wait_vm_lgkm0<(NSP - 2) * DP>();
         ring_barrier();
-        issue(kt + 2 < nk ? kt + 2 : nk - 1, kt & 1);
+        issue_q(kt + 2 < nk ? kt + 2 : nk - 1, kt & 1);
+        issue_p(kt + NSP < nk ? kt + NSP : nk - 1, sp_cur);
         // (C)
-        read_half(nxt, 0, p0, q0);
+        read_half(ring_p + sp_nxt * P_STRIDE, ring_q + ((kt + 1) & 1) * Q_STRIDE, 0, p0, q0);
         mfma_half(p1, q1);
 #pragma unroll
         for (int r = 0; r < NRD; ++r) {
@@ -460,6 +485,8 @@ __global__ __launch_bounds__(64 * GB_NW) void bwd_gemm_kernel(GemmArgs a) {
           __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         }
         if (NM > NRD * PER) __builtin_amdgcn_sched_group_barrier(0x008, NM - NRD * PER, 0);
+        sp_cur = sp_nxt;
+        sp_nxt = sp_nxt + 1 == NSP ? 0 : sp_nxt + 1;
       }
     }
     wait_vm_lgkm0<0>();
@@ -508,10 +535,7 @@ __global__ __launch_bounds__(64 * GB_NW) void bwd_gemm_kernel(GemmArgs a) {
     if (persist) {
       more = setup(claimed_tile((it + 1) & 1));
       if (more) {
-        if (nk > 0) {
-          issue(0, 0);
-          issue(1 < nk ? 1 : 0, 1);
-        }
+        if (nk > 0) prologue();
         if (tid == 0) claim = atomicAdd(a.counter + cq + zl, 1);
       }
     }
