@@ -28,15 +28,14 @@
 // ds_read_b64_tr_b16, which hands each lane 4 consecutive k of one column
 // (two reads make one 8-k MFMA operand); Q holds activation rows
 // (K-contiguous), read like the forward's operands.  The weight gradients
-// contract over rows, so both operands are k-strided: for the routed experts
-// they are first transposed (each expert's rows padded to 64 columns, zeros
-// between) and then read K-contiguously on both sides; the shared experts'
-// read both sides transposed from LDS.
+// contract over rows, so both operands are k-strided and both are read
+// transposed from LDS (rows past a segment's end read as zeros).  (Copying
+// the routed operands into K-contiguous transposes first made the GEMMs
+// faster per slab, but the five transposes cost more than that.)
 //
 // Loads.  Slabs go straight from global memory to LDS (global_load_lds) in
-// a two-stage ring; the kernels that read transposed issue them from asm, so
-// that the compiler does not wait for the newest slab before every
-// ds_read_b64_tr_b16 (it cannot tell the two apart).
+// rings, issued from asm so that the compiler does not wait for the newest
+// slab before every ds_read_b64_tr_b16 (it cannot tell the two apart).
 //
 // Scheduling.  Row tiles of dH / dX follow the device-built plans, dealt
 // round-robin over the XCDs.  Weight-gradient tiles run persistent: one
@@ -127,7 +126,6 @@ struct GemmArgs {
   const int32_t* seg;         // dW: [G+1] row offsets, or null (dense)
   const int32_t* order;       // dW: segments by descending row count (or null: natural)
   int* counter;               // dW: GB_QUEUES tile counters of a persistent launch (or null)
-  const int32_t* poff;        // dW from transposed operands: [G+1] padded column offsets
   int64_t dense_rows;
   const uint16_t* zero;       // >= 256 zero elements
   int K, N, M;                // dH/dX: K per operand pair; N output cols; dW: M output rows
@@ -154,12 +152,10 @@ __global__ __launch_bounds__(64 * GB_NW) void bwd_gemm_kernel(GemmArgs a) {
   constexpr int NLP = BN / 64, NLQ = BM / 64;
   constexpr int SP = BK * BN, SQ = BK * BM;
   constexpr bool QMN = KIND == BG_DW;       // Q stored k-strided (read transposed)
-  constexpr bool PKM = KIND == BG_DWT;      // P stored K-contiguous (read like Q)
-  constexpr bool WGRAD = KIND == BG_DW || KIND == BG_DWT;
-  constexpr int DP = (PKM ? BN : BK * NLP) / 8 / NW;   // P load instructions per wave per slab
+  constexpr bool WGRAD = KIND == BG_DW;
+  constexpr int DP = BK * NLP / 8 / NW;     // P load instructions per wave per slab
   constexpr int DQ = (QMN ? BK * NLQ : BM) / 8 / NW;
-  static_assert(DP * NW * 8 == (PKM ? BN : BK * NLP) && DQ * NW * 8 == (QMN ? BK * NLQ : BM),
-                "load split");
+  static_assert(DP * NW * 8 == BK * NLP && DQ * NW * 8 == (QMN ? BK * NLQ : BM), "load split");
   // the ring, then two int slots that pass a claimed tile to every wave, then
   // (weight gradients) the segment order and row offsets.  One LDS object: a
   // second one makes the compiler wait for in-flight direct-to-LDS writes
@@ -222,9 +218,8 @@ __global__ __launch_bounds__(64 * GB_NW) void bwd_gemm_kernel(GemmArgs a) {
   };
   int e0;
   if (persist) {
-    const int32_t* off = PKM ? a.poff : a.seg;
     for (int i = tid; i < a.G; i += 64 * NW) tab_order[i] = a.order[i];
-    for (int i = tid; i <= a.G; i += 64 * NW) tab_off[i] = off[i];
+    for (int i = tid; i <= a.G; i += 64 * NW) tab_off[i] = a.seg[i];
     if (tid == 0) tile_slot[0] = atomicAdd(a.counter + cq + zl, 1);
     wait_lgkm0();
     ring_barrier();
@@ -248,7 +243,6 @@ __global__ __launch_bounds__(64 * GB_NW) void bwd_gemm_kernel(GemmArgs a) {
   static_assert(KSP % 4 == 0 && KSQ % 4 == 0, "swizzle must repeat across instructions");
   int lane = 0;
   int g = 0, m0 = 0, m1 = 0, n0 = 0, nk = 0, ks = 0, kb0 = 0, klen32 = 0, pk0 = 0, qk0 = 0;
-  int64_t p_off[PKM ? DP : 1];   // K-major P: element offset of this lane's row and chunk
   int64_t q_off[QMN ? 1 : DQ];   // K-major Q: element offset of this lane's row and chunk
   const uint16_t* pb = nullptr;  // P at k-row pk0 of slab 0
   const uint16_t* pb2 = nullptr;
@@ -278,15 +272,9 @@ __global__ __launch_bounds__(64 * GB_NW) void bwd_gemm_kernel(GemmArgs a) {
         g = __builtin_amdgcn_readfirstlane(tab_order[rank]);
         const int o0 = __builtin_amdgcn_readfirstlane(tab_off[g]);
         klen = __builtin_amdgcn_readfirstlane(tab_off[g + 1]) - o0;
-        if constexpr (PKM) {
-          // transposed operands: the segment's columns start at a multiple
-          // of 64 and its padding columns hold zeros
-          prow0 = qrow0 = o0;
-        } else {
-          prow0 = (int64_t)g * a.p_row_seg + o0;
-          qrow0 = (int64_t)g * a.q_row_seg + o0;
-        }
-      } else if constexpr (!PKM) {
+        prow0 = (int64_t)g * a.p_row_seg + o0;
+        qrow0 = (int64_t)g * a.q_row_seg + o0;
+      } else {
         g = rank;
         const int64_t r0 = a.seg ? a.seg[g] : 0;
         klen = a.seg ? a.seg[g + 1] - r0 : a.dense_rows;
@@ -317,16 +305,6 @@ __global__ __launch_bounds__(64 * GB_NW) void bwd_gemm_kernel(GemmArgs a) {
     int pcol = n0 + ((lane >> 3) % NLP) * 64;
     if (pcol > N - 64) pcol = N - 64;            // past the last column: any valid line
     pcol += mn_chunk(lane, pk0) * 8;
-    if constexpr (PKM) {
-#pragma unroll
-      for (int i = 0; i < DP; ++i) {
-        int r = n0 + (wave + i * NW) * 8 + dma_row(lane);
-        if (r > N - 1) r = N - 1;
-        p_off[i] = r * ldp + dma_chunk(lane) * 8 + prow0;
-      }
-    } else {
-      p_off[0] = 0;
-    }
     int qcol = 0;
     if constexpr (QMN) {
       qk0 = wave * (8 / NLQ) + (lane >> 3) / NLQ;
@@ -339,13 +317,10 @@ __global__ __launch_bounds__(64 * GB_NW) void bwd_gemm_kernel(GemmArgs a) {
       for (int i = 0; i < DQ; ++i) {
         int r = m0 + (wave + i * NW) * 8 + dma_row(lane);
         if (r > m1 - 1) r = m1 - 1;
-        q_off[i] = PKM ? r * ldq + dma_chunk(lane) * 8 + qrow0
-                       : (qrow0 + r) * ldq + dma_chunk(lane) * 8;
+        q_off[i] = (qrow0 + r) * ldq + dma_chunk(lane) * 8;
       }
     }
-    if constexpr (PKM) {
-      pb = a.P;
-    } else if constexpr (KIND == BG_DW) {
+    if constexpr (KIND == BG_DW) {
       pb = a.P + (prow0 + pk0) * ldp + pcol;
     } else {
       pb = a.P + (int64_t)g * a.p_seg + pk0 * ldp + pcol;
@@ -364,10 +339,9 @@ __global__ __launch_bounds__(64 * GB_NW) void bwd_gemm_kernel(GemmArgs a) {
 #pragma unroll
     for (int i = 0; i < DP; ++i) {
       const int kr = kb + i * KSP;                         // uniform
-      const uint16_t* src = PKM ? pb + p_off[i] + kb : (second ? pb2 : pb) + (int64_t)kr * ldp;
+      const uint16_t* src = (second ? pb2 : pb) + (int64_t)kr * ldp;
       if constexpr (KIND == BG_DW) src = pk0 + kr < klen32 ? src : zp;
-      if constexpr (PKM) dma_rows(src, sp + (wave + i * NW) * 512);
-      else dma_rows_untracked(src, sp + (wave + i * NW) * 512);
+      dma_rows_untracked(src, sp + (wave + i * NW) * 512);
     }
   };
   auto issue_q = [&](int ktr, int stage) {
@@ -384,8 +358,7 @@ __global__ __launch_bounds__(64 * GB_NW) void bwd_gemm_kernel(GemmArgs a) {
       } else {
         src = (second ? a.Q2 : a.Q) + q_off[i] + kb;
       }
-      if constexpr (PKM) dma_rows(src, sq + (wave + i * NW) * 512);
-      else dma_rows_untracked(src, sq + (wave + i * NW) * 512);
+      dma_rows_untracked(src, sq + (wave + i * NW) * 512);
     }
   };
   // the tile's first slabs: P and Q of slabs 0 and 1, then (three P stages)
@@ -405,19 +378,12 @@ __global__ __launch_bounds__(64 * GB_NW) void bwd_gemm_kernel(GemmArgs a) {
   // stages slab kt held; (C) MFMAs of half 1 with the reads of half 0 of
   // slab kt+1 (and the new requests) spread between them.  Past the last
   // slab the requests reload it (harmless).
-  constexpr int NRD = (PKM ? 1 : 2) * TN + (QMN ? 2 : 1) * TM;   // LDS read instructions per half
+  constexpr int NRD = 2 * TN + (QMN ? 2 : 1) * TM;   // LDS read instructions per half
   constexpr int NM = TM * TN, PER = NM / NRD > 0 ? NM / NRD : 1;
   constexpr int DPW = DP + DQ;
   auto read_half = [&](const uint16_t* sp, const uint16_t* sq, int kk, bf16x8_t* fp, bf16x8_t* fq) {
 #pragma unroll
-    for (int j = 0; j < TN; ++j) {
-      if constexpr (PKM) {
-        const int ch = kk * 4 + (lane >> 4);
-        fp[j] = *reinterpret_cast<const bf16x8_t*>(sp + swz(wn * BNW + j * 16 + (lane & 15), ch));
-      } else {
-        fp[j] = read_mn<NLP>(sp, wn * BNW + j * 16, kk * 32, lane);
-      }
-    }
+    for (int j = 0; j < TN; ++j) fp[j] = read_mn<NLP>(sp, wn * BNW + j * 16, kk * 32, lane);
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
       if constexpr (QMN) {
@@ -919,63 +885,6 @@ __global__ __launch_bounds__(256) void wr_reduce_kernel(WrArgs a, int nchunks) {
   a.dw_router[idx] = s;
 }
 
-// Padded column offsets of the transposed operands: segment g's rows become
-// columns [poff[g], poff[g] + rows_g) of a row of the transposed matrix, and
-// every segment starts at a multiple of 64.
-__global__ __launch_bounds__(64) void pad_offsets_kernel(const int32_t* seg, int G, int32_t* poff) {
-  if (threadIdx.x != 0) return;
-  int acc = 0;
-  for (int g = 0; g < G; ++g) {
-    poff[g] = acc;
-    acc += (seg[g + 1] - seg[g] + 63) & ~63;
-  }
-  poff[G] = acc;
-}
-
-// AT[m, poff[g] + (r - seg[g])] = A[r, m] for the rows r of every segment g,
-// zeros in the padding columns.  A wave transposes a 64 x 64 block in
-// registers: lane (pc, mc) loads the 8 x 8 sub-block of rows 8 pc.. and
-// columns 8 mc.. (eight 16-byte loads; the 8 lanes of one pc cover a whole
-// 128-byte row segment), repacks it, and stores its 8 columns as 16-byte
-// pieces of 8 consecutive AT columns (the 8 lanes of one mc cover a whole
-// 128-byte segment of an AT row).  A workgroup (4 waves) covers 64 columns of
-// AT inside one segment and 256 of its rows.
-__global__ __launch_bounds__(256) void transpose_pad_kernel(const uint16_t* __restrict__ A,
-                                                            int64_t lda, int M,
-                                                            const int32_t* seg,
-                                                            const int32_t* poff, int G,
-                                                            uint16_t* __restrict__ AT,
-                                                            int64_t ldt) {
-  const int p0 = blockIdx.x * 64;
-  const int m0 = (blockIdx.y * 4 + (threadIdx.x >> 6)) * 64;
-  if (p0 >= poff[G] || m0 >= M) return;
-  int lo = 0, hi = G - 1;          // the segment holding column p0: last g with poff[g] <= p0
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (poff[mid] <= p0) lo = mid; else hi = mid - 1;
-  }
-  const int64_t r0 = seg[lo] + (p0 - poff[lo]);
-  const int64_t r_end = seg[lo + 1];
-  const int lane = threadIdx.x & 63, mc = lane & 7, pc = lane >> 3;
-  u32x4_t v[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int64_t r = r0 + 8 * pc + i;
-    v[i] = r < r_end ? *reinterpret_cast<const u32x4_t*>(A + r * lda + m0 + 8 * mc)
-                     : u32x4_t{0u, 0u, 0u, 0u};
-  }
-#pragma unroll
-  for (int c = 0; c < 8; ++c) {
-    u32x4_t o;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const uint32_t lo16 = v[2 * q][c >> 1], hi16 = v[2 * q + 1][c >> 1];
-      o[q] = (c & 1) ? (lo16 >> 16) | (hi16 & 0xffff0000u) : (lo16 & 0xffffu) | (hi16 << 16);
-    }
-    *reinterpret_cast<u32x4_t*>(AT + (int64_t)(m0 + 8 * mc + c) * ldt + p0 + 8 * pc) = o;
-  }
-}
-
 // order[r] = the segment with the r-th largest row count (ties: lower index);
 // also clears the tile counters of the launch that follows.
 __global__ __launch_bounds__(256) void seg_order_kernel(const int32_t* seg, int G, int32_t* order,
@@ -1083,7 +992,6 @@ hipError_t launch_bwd_gemm(const BwdGemm& b, hipStream_t s) {
   a.plan = b.plan ? reinterpret_cast<const PlanEntry*>(static_cast<const char*>(b.plan) + kPlanHeader)
                   : nullptr;
   a.seg = b.seg;
-  a.poff = b.poff;
   a.order = b.seg ? b.order : nullptr;
   a.counter = b.seg && b.order ? b.order + b.G : nullptr;   // the ints after the order
   if (a.order) {
@@ -1105,14 +1013,12 @@ hipError_t launch_bwd_gemm(const BwdGemm& b, hipStream_t s) {
   a.NT = (b.N + GB_BN - 1) / GB_BN;
   constexpr int TH = 64 * GB_NW;
   unsigned grid;
-  if (b.kind == BG_DW || b.kind == BG_DWT) {
+  if (b.kind == BG_DW) {
     const int64_t V = (int64_t)a.G * a.MT * a.NT;
     if (V == 0) return hipSuccess;
-    if (b.kind == BG_DWT && (!b.poff || !a.counter)) return hipErrorInvalidValue;
     grid = (unsigned)(a.counter && V > cu_count() ? cu_count() : V);
     prof_before(b.name, s);
-    if (b.kind == BG_DWT) bwd_gemm_kernel<BG_DWT, 0><<<grid, TH, 0, s>>>(a);
-    else bwd_gemm_kernel<BG_DW, 0><<<grid, TH, 0, s>>>(a);
+    bwd_gemm_kernel<BG_DW, 0><<<grid, TH, 0, s>>>(a);
   } else {
     if (b.max_entries == 0) return hipSuccess;
     grid = (unsigned)b.max_entries;
@@ -1159,24 +1065,6 @@ hipError_t launch_router_bwd(const WrArgs& in, hipStream_t s) {
   wr_partial_kernel<<<grid, 256, 0, s>>>(a);
   const int64_t n = (int64_t)a.E * a.d;
   wr_reduce_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(a, nch);
-  prof_after(s);
-  return hipGetLastError();
-}
-
-hipError_t launch_pad_offsets(const int32_t* seg, int G, int32_t* poff, hipStream_t s) {
-  pad_offsets_kernel<<<1, 64, 0, s>>>(seg, G, poff);
-  return hipGetLastError();
-}
-
-hipError_t launch_transpose_pad(const void* A, int64_t lda, int M, const int32_t* seg,
-                                const int32_t* poff, int G, int64_t max_cols, void* AT,
-                                int64_t ldt, hipStream_t s) {
-  if (M % 64 || ldt % 64 || lda % 8 || max_cols > ldt) return hipErrorInvalidValue;
-  const int64_t nx = (max_cols + 63) / 64;
-  if (nx == 0) return hipSuccess;
-  prof_before("bwd_transpose", s);
-  transpose_pad_kernel<<<dim3((unsigned)nx, (unsigned)((M + 255) / 256)), 256, 0, s>>>(
-      static_cast<const uint16_t*>(A), lda, M, seg, poff, G, static_cast<uint16_t*>(AT), ldt);
   prof_after(s);
   return hipGetLastError();
 }

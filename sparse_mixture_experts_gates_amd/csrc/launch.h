@@ -148,10 +148,7 @@ hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
 //         d_ff row), Q = dG (+ dU as Q2); epi 1 = two operand pairs
 //  BG_DW  per segment g a full M x N output, k over the segment's rows:
 //         P(n, k) = P[(g p_row_seg + r0 + k) ldp + n], Q(m, k) likewise
-//  BG_DWT like BG_DW from transposed operands: P(n, k) = P[n ldp + poff[g] + k],
-//         Q(m, k) = Q[m ldq + poff[g] + k], k < poff[g+1] - poff[g] (the padding
-//         columns hold zeros)
-enum { BG_DH = 0, BG_DX = 1, BG_DW = 2, BG_DWT = 3 };
+enum { BG_DH = 0, BG_DX = 1, BG_DW = 2 };
 struct BwdGemm {
   int kind, epi;
   const char* name;
@@ -169,7 +166,6 @@ struct BwdGemm {
   const void* plan;        // BG_DH / BG_DX: plan buffer (header + entries)
   int64_t max_entries;     // grid of a plan-driven launch
   const int32_t* seg;      // BG_DW: [G+1] row offsets or null (dense_rows each)
-  const int32_t* poff;     // BG_DWT: [G+1] padded column offsets (launch_pad_offsets)
   int32_t* order;          // BG_DW with seg: [G + 8] scratch: the longest-first segment
                            // order, then the 8 tile counters of the persistent launch
   int64_t dense_rows;
@@ -185,13 +181,6 @@ int bwd_tile_rows();
 int bwd_tile_cols();
 int64_t bwd_dw_blocks(int G, int M, int N);
 hipError_t launch_bwd_gemm(const BwdGemm& b, hipStream_t s);
-// poff[g] = sum over h < g of rows_h rounded up to 64 (poff[G] = the total).
-hipError_t launch_pad_offsets(const int32_t* seg, int G, int32_t* poff, hipStream_t s);
-// AT[m, poff[g] + (r - seg[g])] = A[r, m] (bf16), zeros in the padding columns;
-// max_cols >= poff[G] bounds the grid (M, ldt multiples of 64).
-hipError_t launch_transpose_pad(const void* A, int64_t lda, int M, const int32_t* seg,
-                                const int32_t* poff, int G, int64_t max_cols, void* AT,
-                                int64_t ldt, hipStream_t s);
 
 struct GateBwdArgs {
   const uint16_t* dy;       // [T, d]

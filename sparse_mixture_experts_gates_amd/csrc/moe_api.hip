@@ -209,9 +209,8 @@ int dx_split(const moe_config_t* c, int64_t T) {
 
 struct BwdWs {
   size_t zero, dO, dG, dU, dXp, dXpart, dlogits, dGs, dUs, dXs, plan_h, plan_x, splan_h, splan_x,
-      wr, order, poff, xT, dOT, hT, dGT, dUT, total;
+      wr, order, total;
   int split;       // K parts of the routed dX GEMM
-  int64_t ldt;     // row pitch of the transposed operands (padded rows of all experts)
 };
 BwdWs bwd_ws(const moe_config_t* c, int64_t T) {
   BwdWs w;
@@ -241,16 +240,6 @@ BwdWs bwd_ws(const moe_config_t* c, int64_t T) {
   }
   w.wr = o; o += up(wr_ws_bytes(T, c->num_experts, c->d));
   w.order = o; o += up((size_t)(c->num_experts + 8) * 4);
-  // transposed operands of the routed weight gradients: each expert's rows
-  // padded to a multiple of 64 columns
-  w.ldt = (R + 63 * (int64_t)c->num_experts + 63) / 64 * 64;
-  const size_t dT = up((size_t)c->d * w.ldt * 2), fT = up((size_t)c->d_ff * w.ldt * 2);
-  w.poff = o; o += up((size_t)(c->num_experts + 1) * 4);
-  w.xT = o; o += dT;
-  w.dOT = o; o += dT;
-  w.hT = o; o += fT;
-  w.dGT = o; o += fT;
-  w.dUT = o; o += glu ? fT : 0;
   w.total = o;
   return w;
 }
@@ -883,19 +872,6 @@ moe_status_t moe_backward(const moe_config_t* cfg, int64_t T, const void* x, con
     b.N = f;
     b.G = G;
     if (launch_bwd_gemm(b, s) != hipSuccess) return MOE_ERR_HIP;
-    // routed experts: the weight gradients read transposed operands (each
-    // expert's rows padded to 64 columns), so both sides are K-contiguous
-    int32_t* poff = reinterpret_cast<int32_t*>(at(workspace, bw.poff));
-    const int64_t ldt = bw.ldt;
-    auto transpose = [&](const void* A, int M, size_t dst) {
-      return launch_transpose_pad(A, M, M, offsets, poff, E, ldt, at(workspace, dst), ldt, s);
-    };
-    if (!shared) {
-      if (launch_pad_offsets(offsets, E, poff, s) != hipSuccess) return MOE_ERR_HIP;
-      if (transpose(dO, d, bw.dOT) != hipSuccess || transpose(Hin, f, bw.hT) != hipSuccess ||
-          transpose(Xin, d, bw.xT) != hipSuccess)
-        return MOE_ERR_HIP;
-    }
     // dW2 = dO^T H
     memset(&b, 0, sizeof(b));
     b.kind = BG_DW;
@@ -909,14 +885,6 @@ moe_status_t moe_backward(const moe_config_t* cfg, int64_t T, const void* x, con
     b.C = shared ? dws2 : dw2;
     b.ldc = f;
     b.c_seg = (int64_t)d * f;
-    if (!shared) {
-      b.kind = BG_DWT;
-      b.P = at(workspace, bw.hT);
-      b.ldp = ldt;
-      b.Q = at(workspace, bw.dOT);
-      b.ldq = ldt;
-      b.poff = poff;
-    }
     b.seg = seg;
     b.order = reinterpret_cast<int32_t*>(at(workspace, bw.order));
     b.dense_rows = T;
@@ -951,10 +919,6 @@ moe_status_t moe_backward(const moe_config_t* cfg, int64_t T, const void* x, con
     b.part_stride = rows * (int64_t)d;
     if (launch_bwd_gemm(b, s) != hipSuccess) return MOE_ERR_HIP;
     // dW1 = dG^T X, dW3 = dU^T X
-    if (!shared) {
-      if (transpose(gG, f, bw.dGT) != hipSuccess) return MOE_ERR_HIP;
-      if (g2 && transpose(gU, f, bw.dUT) != hipSuccess) return MOE_ERR_HIP;
-    }
     for (int u = 0; u < (g2 ? 2 : 1); ++u) {
       memset(&b, 0, sizeof(b));
       b.kind = BG_DW;
@@ -968,14 +932,6 @@ moe_status_t moe_backward(const moe_config_t* cfg, int64_t T, const void* x, con
       b.C = shared ? (u ? dws3 : dws1) : (u ? dw3 : dw1);
       b.ldc = d;
       b.c_seg = (int64_t)f * d;
-      if (!shared) {
-        b.kind = BG_DWT;
-        b.P = at(workspace, bw.xT);
-        b.ldp = ldt;
-        b.Q = at(workspace, u ? bw.dUT : bw.dGT);
-        b.ldq = ldt;
-        b.poff = poff;
-      }
       b.seg = seg;
       b.order = reinterpret_cast<int32_t*>(at(workspace, bw.order));
       b.dense_rows = T;
