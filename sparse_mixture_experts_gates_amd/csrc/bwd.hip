@@ -167,9 +167,9 @@ __global__ __launch_bounds__(64 * GB_NW) void bwd_gemm_kernel(GemmArgs a) {
   constexpr int NSP = KIND == BG_DH ? 3 : 2;
   constexpr int RING = NSP * SP + 2 * SQ;
   __shared__ __attribute__((aligned(1024))) uint16_t ring[RING + (WGRAD ? 4 + 2 * TAB : 0)];
-  // stages: the P stages, then the Q stages; dX keeps each stage's P and Q
-  // side by side, which measured faster for it (and slower for the others)
-  constexpr bool ILV = KIND == BG_DX;
+  // stages: dX and the weight gradients keep each stage's P and Q side by
+  // side; dH, with its third P stage, has the P stages, then the Q stages
+  constexpr bool ILV = KIND == BG_DX || KIND == BG_DW;
   static_assert(!ILV || NSP == 2, "interleaved stages hold one P and one Q slab each");
   constexpr int P_STRIDE = ILV ? SP + SQ : SP, Q_STRIDE = ILV ? SP + SQ : SQ;
   uint16_t* const ring_p = ring;
