@@ -256,8 +256,9 @@ __global__ __launch_bounds__(64 * GB_NW) void bwd_gemm_kernel(GemmArgs a) {
     ks = 0;
     kb0 = 0;
     if constexpr (WGRAD) {
-      // Longest segments first, so the costliest tiles start first and the
-      // short ones fill in at the end; within a segment, row blocks vary
+      // Segments with rows longest first, so the costliest tiles start first
+      // and the short ones fill in at the end, with the segments without rows
+      // (blocks of zeros: stores only) spread between them; within a segment, row blocks vary
       // fastest, so an XCD's queue holds every eighth row block (its own
       // slice of the Q operand) while the column blocks stream past.
       const int V = a.G * a.MT * a.NT;
@@ -885,18 +886,42 @@ __global__ __launch_bounds__(256) void wr_reduce_kernel(WrArgs a, int nchunks) {
   a.dw_router[idx] = s;
 }
 
-// order[r] = the segment with the r-th largest row count (ties: lower index);
-// also clears the tile counters of the launch that follows.
+// order[] lists the segments with rows by decreasing row count (ties: lower
+// index) and spreads the empty ones evenly between them: segment r of the nz
+// non-empty ones and empty segment j of the z others are merged by the keys
+// (2r + 1) z and (2j + 1) nz (a non-empty one first on equal keys), so the
+// blocks that are only zeros are written while other blocks compute instead
+// of all at the end.  Also clears the tile counters of the launch that follows.
 __global__ __launch_bounds__(256) void seg_order_kernel(const int32_t* seg, int G, int32_t* order,
                                                         int* counter) {
   __shared__ int len[1024];
+  __shared__ int nz_count;
   if (threadIdx.x < GB_QUEUES) counter[threadIdx.x] = 0;
+  if (threadIdx.x == 0) nz_count = 0;
   for (int g = threadIdx.x; g < G; g += 256) len[g] = seg[g + 1] - seg[g];
   __syncthreads();
+  for (int g = threadIdx.x; g < G; g += 256)
+    if (len[g] > 0) atomicAdd(&nz_count, 1);
+  __syncthreads();
+  const int64_t nz = nz_count, z = G - nz_count;
   for (int g = threadIdx.x; g < G; g += 256) {
-    int r = 0;
-    for (int h = 0; h < G; ++h) r += len[h] > len[g] || (len[h] == len[g] && h < g);
-    order[r] = g;
+    int r = 0, pos;
+    if (len[g] > 0) {
+      for (int h = 0; h < G; ++h) r += len[h] > len[g] || (len[h] == len[g] && h < g);
+      // empty segments j with (2j + 1) nz < (2r + 1) z go before it
+      const int64_t key = (2 * (int64_t)r + 1) * z;
+      int before = 0;
+      for (int j = 0; j < z; ++j) before += (2 * (int64_t)j + 1) * nz < key;
+      pos = r + before;
+    } else {
+      for (int h = 0; h < g; ++h) r += len[h] == 0;
+      // non-empty segments q with (2q + 1) z <= (2r + 1) nz go before it
+      const int64_t key = (2 * (int64_t)r + 1) * nz;
+      int before = 0;
+      for (int q = 0; q < nz; ++q) before += (2 * (int64_t)q + 1) * z <= key;
+      pos = r + before;
+    }
+    order[pos] = g;
   }
 }
 
