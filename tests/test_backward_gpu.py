@@ -190,43 +190,83 @@ def test_backward_rejects_fp32_and_bad_alpha():
                    saved[: saved.numel() // 2], dy)
 
 
-def test_backward_full_size_mixtral_sampled():
-    """The Mixtral shape at full size (T=4096, d=4096, d_ff=14336, E=8, k=2),
-    the configuration bench.py times, checked on samples the oracle can
-    compute one at a time: dx, d_gate and d_logits of 24 tokens; for three
-    experts, eight hidden units each, the matching rows of dW1 / dW3 and
-    columns of dW2 (hidden units are independent, so the oracle's expert
-    backward on the sliced weights gives exactly those slices); dW_r in full
-    from the GPU's own score gradients."""
+# full-size workloads bench.py times the backward on, and how many tokens of
+# each are checked
+FULL_BWD = {"mixtral_bf16": 24, "deepseek_v3_bf16": 8, "gptoss_prefill_bf16": 12}
+
+
+@pytest.mark.parametrize("name", list(FULL_BWD))
+def test_backward_full_size_sampled(name):
+    """A full-size workload in the configuration bench.py times (Mixtral:
+    T=4096, d=4096, d_ff=14336, E=8, k=2; DeepSeek-V3: T=8192, d=7168,
+    d_ff=2048, E=256, k=8, sigmoid gates with a selection bias, one shared
+    expert; gpt-oss prefill: T=16384, d=d_ff=2880, E=128, k=4, Zipf logit
+    offsets), checked on samples the oracle can compute one at a time: dx,
+    d_gate and d_logits of the sampled tokens (first, last and random ones);
+    for three routed experts (Mixtral: 0, 3, 7; otherwise the most loaded, a
+    median one and the least loaded with 16 rows or more) and each shared
+    expert, eight hidden units each, the matching rows of dW1 / dW3 and
+    columns of dW2
+    (hidden units are independent, so the oracle's expert backward on the
+    sliced weights gives exactly those slices); every expert without rows has
+    all-zero weight gradients; dW_r in full from the GPU's own score
+    gradients."""
     from oracle import moe_backward as BW
     from oracle import moe_oracle as O
-    w = W["mixtral_bf16"]
-    print(f"[bwd-full] {w.name} T={w.T}", flush=True)
+    w = W[name]
+    n_tok = FULL_BWD[name]
+    print(f"[bwd-full] {w.name} T={w.T} d={w.d} E={w.E} k={w.k} d_ff={w.d_ff} "
+          f"S={w.num_shared} tokens={n_tok}", flush=True)
     inp = make_inputs(w, "cuda")
     dy = make_output_grad(w, "cuda")
     cfg = B.config_for(w)
     y, saved = B.forward_train_inputs(cfg, inp)
     g = B.backward(cfg, inp["x"], inp["w_router"], inp["w1"], inp["w2"], inp["w3"], saved, dy,
-                   want_gate_grads=True)
+                   ws1=inp["ws1"], ws3=inp["ws3"], ws2=inp["ws2"], want_gate_grads=True)
     torch.cuda.synchronize()
     r = B.saved_routing(cfg, w.T, saved)
     idx = r["topk_idx"].cpu().numpy().astype(np.int64)
     kept = (r["slot_pos"].cpu().numpy() >= 0).reshape(w.T, w.k)
+    counts = np.bincount(idx[kept], minlength=w.E)
     s = f64(r["logits"])
     x, DY, wr = f64(inp["x"]), f64(dy), f64(inp["w_router"])
     gates = O.gate_values(s, idx, w.gating)
     rng = np.random.default_rng(7)
-    toks = np.unique(np.concatenate([[0, w.T - 1], rng.choice(w.T, 22, replace=False)]))
+    toks = np.unique(np.concatenate([[0, w.T - 1], rng.choice(w.T, n_tok - 2, replace=False)]))
     gx, gdg, gds = f64(g["dx"]), f64(g["d_gate"]), f64(g["d_logits"])
     dx_ref = {t: np.zeros(w.d) for t in toks}
     dg_ref = np.zeros((len(toks), w.k))
-    sample_experts = {0, 3, 7}
+    if name == "mixtral_bf16":
+        sample_experts = {0, 3, 7}
+    else:
+        # (the least loaded one with at least 16 rows: with one or two rows a
+        # slice of eight hidden units can be small through cancellation)
+        live = np.nonzero(counts >= 16)[0]
+        by_rows = live[np.argsort(counts[live], kind="stable")]
+        sample_experts = {int(by_rows[-1]), int(by_rows[len(by_rows) // 2]), int(by_rows[0])}
+    print(f"[bwd-full] experts with rows {int((counts > 0).sum())}, sampled "
+          f"{sorted((e, int(counts[e])) for e in sample_experts)}", flush=True)
+
+    def check_slices(tag, xr, dout, w1, w2, w3, act, got1, got2, got3):
+        F = np.sort(rng.choice(w1.shape[0], 8, replace=False))
+        _, a1, a2, a3 = BW.expert_backward(xr, w1[F], w2[:, F], None if w3 is None else w3[F],
+                                           act, dout)
+        pairs = [("dw1", a1, f64(got1[F])), ("dw2", a2, f64(got2[:, F]))]
+        if a3 is not None:
+            pairs.append(("dw3", a3, f64(got3[F])))
+        for nm, ref, got in pairs:
+            err = np.abs(got - ref).max() / np.abs(ref).max()
+            print(f"[bwd-full] {tag} {nm} rows {len(xr)} err {err:.2e}", flush=True)
+            assert err <= TOL, (tag, nm, err)
+
     for e in range(w.E):
         rows_t = [(i, t, j) for i, t in enumerate(toks) for j in range(w.k)
                   if idx[t, j] == e and kept[t, j]]
         if not rows_t and e not in sample_experts:
             continue
-        w1, w2, w3 = (f64(inp[n][e]) for n in ("w1", "w2", "w3"))
+        w1 = f64(inp["w1"][e])
+        w2 = f64(inp["w2"][e])
+        w3 = f64(inp["w3"][e]) if inp["w3"] is not None else None
         for i, t, j in rows_t:
             out = O.expert_ffn(x[t][None], w1, w2, w3, w.act)[0]
             dg_ref[i, j] = float(DY[t] @ out)
@@ -235,15 +275,21 @@ def test_backward_full_size_mixtral_sampled():
             dx_ref[t] += dxr[0]
         if e in sample_experts:
             sel_t, sel_j = np.nonzero((idx == e) & kept)
-            F = np.sort(rng.choice(w.d_ff, 8, replace=False))
-            _, a1, a2, a3 = BW.expert_backward(x[sel_t], w1[F], w2[:, F], w3[F], w.act,
-                                               gates[sel_t, sel_j][:, None] * DY[sel_t])
-            for name, ref, got in (("dw1", a1, f64(g["dw1"][e][F])),
-                                   ("dw3", a3, f64(g["dw3"][e][F])),
-                                   ("dw2", a2, f64(g["dw2"][e][:, F]))):
-                err = np.abs(got - ref).max() / np.abs(ref).max()
-                print(f"[bwd-full] expert {e} {name} rows {len(sel_t)} err {err:.2e}", flush=True)
-                assert err <= TOL, (e, name, err)
+            check_slices(f"expert {e}", x[sel_t], gates[sel_t, sel_j][:, None] * DY[sel_t],
+                         w1, w2, w3, w.act, g["dw1"][e], g["dw2"][e],
+                         g["dw3"][e] if w3 is not None else None)
+    idle = np.nonzero(counts == 0)[0]
+    for key in ("dw1", "dw2", "dw3"):
+        if g.get(key) is not None and len(idle):
+            nz = int(torch.count_nonzero(g[key][torch.as_tensor(idle, device=g[key].device)]))
+            assert nz == 0, f"{key}: {nz} nonzero values in the {len(idle)} experts without rows"
+    for sh in range(w.num_shared):
+        ws1, ws2, ws3 = (f64(inp[n][sh]) for n in ("ws1", "ws2", "ws3"))
+        for t in toks:
+            dxr, *_ = BW.expert_backward(x[t][None], ws1, ws2, ws3, "swiglu", DY[t][None])
+            dx_ref[t] += dxr[0]
+        check_slices(f"shared {sh}", x, DY, ws1, ws2, ws3, "swiglu",
+                     g["dws1"][sh], g["dws2"][sh], g["dws3"][sh])
     ds_ref = BW.gate_backward(s[toks], idx[toks], dg_ref, w.gating)
     for i, t in enumerate(toks):
         dx_ref[t] += ds_ref[i] @ wr
@@ -251,9 +297,12 @@ def test_backward_full_size_mixtral_sampled():
     dg_err = np.abs(gdg[toks] - dg_ref).max() / np.abs(gdg).max()
     ds_err = np.abs(gds[toks] - ds_ref).max() / np.abs(gds).max()
     dwr_own, _ = BW.router_backward(x, wr, gds)
+    sc = np.abs(dwr_own).max(axis=1)
     dwr_err = float((np.abs(f64(g["dw_router"]) - dwr_own).max(axis=1)
-                     / np.abs(dwr_own).max(axis=1)).max())
+                     / np.where(sc > 0, sc, 1.0)).max())
     print(f"[bwd-full] dx {dx_err:.2e} d_gate {dg_err:.2e} d_logits {ds_err:.2e} "
           f"dW_r(own ds) {dwr_err:.2e}", flush=True)
     assert dx_err <= TOL and dg_err <= TOL and ds_err <= TOL
     assert dwr_err <= 1e-5
+    del g, saved, inp, dy, y
+    torch.cuda.empty_cache()
