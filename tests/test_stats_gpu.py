@@ -38,6 +38,7 @@ CASES = {
     "E64": small(T=777, E=64, k=4),
     "gptoss_prefill_E128": W["gptoss_prefill_bf16"].scaled(d_ff=64),  # full T, Zipf skew
     "deepseek_E256_sigmoid": W["deepseek_v3_bf16"].scaled(T=3000, d=256, d_ff=64, d_ff_shared=64),
+    "deepseek_full_T_d": W["deepseek_v3_bf16"].scaled(d_ff=64, d_ff_shared=64),  # T 8192, d 7168
     "decode_T8": W["gptoss_decode_bf16"].scaled(d_ff=64),
     "one_token": small(T=1, E=16, k=3),
 }
