@@ -44,6 +44,7 @@
 // next tile's first two slabs are requested before the current tile's
 // output block is stored, and the block goes out through LDS as whole
 // 128-byte row segments.
+#include <atomic>
 #include <string.h>
 
 #include "common.h"
@@ -978,16 +979,17 @@ int bwd_dx_split(int64_t rows, int G, int N, int K_all) {
 
 // Compute units of the current device (one persistent workgroup each).
 int cu_count() {
-  static int cached[64] = {0};
+  // per device, filled on first use (threads racing here store the same value)
+  static std::atomic<int> cached[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cached[dev] == 0) {
-    int n = 0;
+  int n = cached[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
       n = 256;
-    cached[dev] = n;
+    cached[dev].store(n, std::memory_order_relaxed);
   }
-  return cached[dev];
+  return n;
 }
 
 int bwd_tile_rows() { return GB_BM; }

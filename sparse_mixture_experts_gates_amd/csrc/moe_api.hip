@@ -6,6 +6,7 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <atomic>
 #include <mutex>
 #include <string>
 #include <vector>
@@ -23,7 +24,7 @@ struct ProfRec {
   hipEvent_t e0, e1;
 };
 std::mutex g_prof_mu;
-bool g_prof_on = false;
+std::atomic<bool> g_prof_on{false};   // read by every launch, set under the mutex
 std::vector<ProfRec> g_prof_recs;
 std::vector<hipEvent_t> g_prof_pool;
 
@@ -40,7 +41,7 @@ hipEvent_t prof_event() {
 }  // namespace
 
 void prof_before(const char* name, hipStream_t s) {
-  if (!g_prof_on) return;
+  if (!g_prof_on.load(std::memory_order_relaxed)) return;
   std::lock_guard<std::mutex> lk(g_prof_mu);
   ProfRec r{name, prof_event(), prof_event()};
   if (!r.e0 || !r.e1) return;
@@ -49,7 +50,7 @@ void prof_before(const char* name, hipStream_t s) {
 }
 
 void prof_after(hipStream_t s) {
-  if (!g_prof_on) return;
+  if (!g_prof_on.load(std::memory_order_relaxed)) return;
   std::lock_guard<std::mutex> lk(g_prof_mu);
   if (!g_prof_recs.empty()) hipEventRecord(g_prof_recs.back().e1, s);
 }
@@ -578,7 +579,7 @@ moe_status_t moe_profile_enable(int32_t on) {
     g_prof_pool.push_back(r.e1);
   }
   g_prof_recs.clear();
-  g_prof_on = on != 0;
+  g_prof_on.store(on != 0, std::memory_order_relaxed);
   return MOE_OK;
 }
 
