@@ -119,9 +119,34 @@ def _ptr(t: Optional[torch.Tensor]):
         return None
     if not t.is_cuda:
         raise ValueError("tensor must be in device memory")
+    if t.device.index != torch.cuda.current_device():
+        raise ValueError(f"tensor on {t.device}, but the current device is "
+                         f"cuda:{torch.cuda.current_device()}")
     if not t.is_contiguous():
         raise ValueError("tensor must be contiguous")
     return ctypes.c_void_p(t.data_ptr())
+
+
+def _arg(t: Optional[torch.Tensor], name, numel, dtype):
+    """Device pointer of ``t`` once it holds exactly the ``numel`` elements of
+    ``dtype`` that the library reads or writes through it (None passes)."""
+    if t is None:
+        return None
+    if t.dtype != dtype:
+        raise ValueError(f"{name}: dtype {t.dtype}, expected {dtype}")
+    if t.numel() != numel:
+        raise ValueError(f"{name}: {t.numel()} elements, expected {numel}")
+    return _ptr(t)
+
+
+def _weights(cfg, w1, w3, w2, ws1, ws3, ws2):
+    """Checked pointers of the expert and shared-expert weights, in the
+    library's argument order (w1, w3, w2, ws1, ws3, ws2)."""
+    dt, E, d, f = _dt(cfg), cfg.num_experts, cfg.d, cfg.d_ff
+    S, fs = cfg.num_shared, cfg.d_ff_shared
+    return (_arg(w1, "w1", E * f * d, dt), _arg(w3, "w3", E * f * d, dt),
+            _arg(w2, "w2", E * d * f, dt), _arg(ws1, "ws1", S * fs * d, dt),
+            _arg(ws3, "ws3", S * fs * d, dt), _arg(ws2, "ws2", S * d * fs, dt))
 
 
 def _stream():
@@ -158,8 +183,12 @@ def route(cfg, x, w_router, logit_offset=None, select_bias=None, want_logits=Fal
     idx = torch.empty((T, k), dtype=torch.int32, device=x.device)
     gate = torch.empty((T, k), dtype=torch.float32, device=x.device)
     logits = torch.empty((T, E), dtype=torch.float32, device=x.device) if want_logits else None
-    _check(lib().moe_route(ctypes.byref(cfg), T, _ptr(x), _ptr(w_router), _ptr(logit_offset),
-                           _ptr(select_bias), _ptr(logits), _ptr(idx), _ptr(gate), _ptr(ws),
+    dt, d = _dt(cfg), cfg.d
+    _check(lib().moe_route(ctypes.byref(cfg), T, _arg(x, "x", T * d, dt),
+                           _arg(w_router, "w_router", E * d, dt),
+                           _arg(logit_offset, "logit_offset", E, torch.float32),
+                           _arg(select_bias, "select_bias", E, torch.float32),
+                           _ptr(logits), _ptr(idx), _ptr(gate), _ptr(ws),
                            0 if ws is None else ws.numel(), _stream()), "moe_route")
     return idx, gate, logits
 
@@ -176,7 +205,8 @@ def permute(cfg, topk_idx, x=None, gather=True, ws=None):
         x_perm=(torch.empty((T * k, cfg.d), dtype=_dt(cfg), device=dev) if gather else None))
     if ws is None:
         ws = workspace(cfg, T, dev)
-    _check(lib().moe_permute(ctypes.byref(cfg), T, _ptr(topk_idx), _ptr(x),
+    _check(lib().moe_permute(ctypes.byref(cfg), T, _arg(topk_idx, "topk_idx", T * k, torch.int32),
+                             _arg(x, "x", T * cfg.d, _dt(cfg)),
                              _ptr(out["expert_counts"]), _ptr(out["expert_offsets"]),
                              _ptr(out["perm_src"]), _ptr(out["slot_pos"]),
                              _ptr(out["num_dropped"]), _ptr(out["x_perm"]), _ptr(ws),
@@ -192,8 +222,12 @@ def expert_ffn(cfg, T, x_perm, expert_offsets, w1, w2, w3=None, x=None, ws1=None
             if cfg.num_shared > 0 else None)
     if ws is None:
         ws = workspace(cfg, T, dev)
-    _check(lib().moe_expert_ffn(ctypes.byref(cfg), T, _ptr(x), _ptr(x_perm), _ptr(expert_offsets),
-                                _ptr(w1), _ptr(w3), _ptr(w2), _ptr(ws1), _ptr(ws3), _ptr(ws2),
+    dt, d = _dt(cfg), cfg.d
+    _check(lib().moe_expert_ffn(ctypes.byref(cfg), T, _arg(x, "x", T * d, dt),
+                                _arg(x_perm, "x_perm", T * cfg.top_k * d, dt),
+                                _arg(expert_offsets, "expert_offsets", cfg.num_experts + 1,
+                                     torch.int32),
+                                *_weights(cfg, w1, w3, w2, ws1, ws3, ws2),
                                 _ptr(eout), _ptr(sout), _ptr(ws), ws.numel(), _stream()),
            "moe_expert_ffn")
     return eout, sout
@@ -201,8 +235,12 @@ def expert_ffn(cfg, T, x_perm, expert_offsets, w1, w2, w3=None, x=None, ws1=None
 
 def combine(cfg, T, expert_out, slot_pos, topk_gate, shared_out=None):
     y = torch.empty((T, cfg.d), dtype=_dt(cfg), device=expert_out.device)
-    _check(lib().moe_combine(ctypes.byref(cfg), T, _ptr(expert_out), _ptr(slot_pos),
-                             _ptr(topk_gate), _ptr(shared_out), _ptr(y), _stream()),
+    dt, d, k = _dt(cfg), cfg.d, cfg.top_k
+    _check(lib().moe_combine(ctypes.byref(cfg), T, _arg(expert_out, "expert_out", T * k * d, dt),
+                             _arg(slot_pos, "slot_pos", T * k, torch.int32),
+                             _arg(topk_gate, "topk_gate", T * k, torch.float32),
+                             _arg(shared_out, "shared_out", cfg.num_shared * T * d, dt),
+                             _ptr(y), _stream()),
            "moe_combine")
     return y
 
@@ -223,9 +261,13 @@ def forward(cfg, x, w_router, w1, w2, w3=None, *, logit_offset=None, select_bias
         dropped = torch.empty(1, dtype=torch.int32, device=dev)
     if ws is None:
         ws = workspace(cfg, T, dev)
-    _check(lib().moe_forward(ctypes.byref(cfg), T, _ptr(x), _ptr(w_router), _ptr(logit_offset),
-                             _ptr(select_bias), _ptr(w1), _ptr(w3), _ptr(w2), _ptr(ws1),
-                             _ptr(ws3), _ptr(ws2), _ptr(y), _ptr(idx), _ptr(gate),
+    dt, d, E = _dt(cfg), cfg.d, cfg.num_experts
+    _check(lib().moe_forward(ctypes.byref(cfg), T, _arg(x, "x", T * d, dt),
+                             _arg(w_router, "w_router", E * d, dt),
+                             _arg(logit_offset, "logit_offset", E, torch.float32),
+                             _arg(select_bias, "select_bias", E, torch.float32),
+                             *_weights(cfg, w1, w3, w2, ws1, ws3, ws2),
+                             _arg(y, "y", T * d, dt), _ptr(idx), _ptr(gate),
                              _ptr(counts), _ptr(dropped), _ptr(ws), ws.numel(), _stream()),
            "moe_forward")
     return y, idx, gate, counts, dropped
@@ -258,10 +300,15 @@ def routing_stats(cfg, logits, expert_counts, num_dropped=None, select_bias=None
         bias_out = torch.empty(E, dtype=torch.float32, device=dev)
     if ws is None:
         ws = workspace(cfg, T, dev)
-    _check(lib().moe_routing_stats(ctypes.byref(cfg), T, _ptr(logits), _ptr(expert_counts),
-                                   _ptr(num_dropped), _ptr(select_bias), float(gamma),
-                                   float(alpha), _ptr(f), _ptr(P), _ptr(loss), _ptr(rate),
-                                   _ptr(bias_out), _ptr(ws), ws.numel(), _stream()),
+    f32, i32 = torch.float32, torch.int32
+    _check(lib().moe_routing_stats(ctypes.byref(cfg), T, _arg(logits, "logits", T * E, f32),
+                                   _arg(expert_counts, "expert_counts", E, i32),
+                                   _arg(num_dropped, "num_dropped", 1, i32),
+                                   _arg(select_bias, "select_bias", E, f32), float(gamma),
+                                   float(alpha), _arg(f, "f", E, f32), _arg(P, "P", E, f32),
+                                   _arg(loss, "loss", 1, f32), _arg(rate, "drop_rate", 1, f32),
+                                   _arg(bias_out, "bias_out", E, f32), _ptr(ws), ws.numel(),
+                                   _stream()),
            "moe_routing_stats")
     return dict(f=f, P=P, loss=loss, drop_rate=rate, bias=bias_out)
 
@@ -291,10 +338,16 @@ def forward_train(cfg, x, w_router, w1, w2, w3=None, *, logit_offset=None, selec
         y = torch.empty((T, cfg.d), dtype=_dt(cfg), device=dev)
     if saved is None:
         saved = torch.empty(max(train_workspace_size(cfg, T), 1), dtype=torch.uint8, device=dev)
-    _check(lib().moe_forward_train(ctypes.byref(cfg), T, _ptr(x), _ptr(w_router),
-                                   _ptr(logit_offset), _ptr(select_bias), _ptr(w1), _ptr(w3),
-                                   _ptr(w2), _ptr(ws1), _ptr(ws3), _ptr(ws2), _ptr(y),
-                                   _ptr(saved), saved.numel(), _stream()),
+    dt, d, E = _dt(cfg), cfg.d, cfg.num_experts
+    if saved.dtype != torch.uint8:
+        raise ValueError(f"saved: dtype {saved.dtype}, expected torch.uint8")
+    _check(lib().moe_forward_train(ctypes.byref(cfg), T, _arg(x, "x", T * d, dt),
+                                   _arg(w_router, "w_router", E * d, dt),
+                                   _arg(logit_offset, "logit_offset", E, torch.float32),
+                                   _arg(select_bias, "select_bias", E, torch.float32),
+                                   *_weights(cfg, w1, w3, w2, ws1, ws3, ws2),
+                                   _arg(y, "y", T * d, dt), _ptr(saved), saved.numel(),
+                                   _stream()),
            "moe_forward_train")
     return y, saved
 
@@ -355,12 +408,20 @@ def backward(cfg, x, w_router, w1, w2, w3, saved, dy, *, ws1=None, ws3=None, ws2
     if ws is None:
         ws = torch.empty(max(backward_workspace_size(cfg, T), 1), dtype=torch.uint8, device=dev)
     g = grads
-    _check(lib().moe_backward(ctypes.byref(cfg), T, _ptr(x), _ptr(w_router), _ptr(w1), _ptr(w3),
-                              _ptr(w2), _ptr(ws1), _ptr(ws3), _ptr(ws2), _ptr(saved),
-                              saved.numel(), _ptr(dy), float(aux_alpha), _ptr(g["dx"]),
-                              _ptr(g["dw_router"]), _ptr(g["dw1"]), _ptr(g["dw3"]),
-                              _ptr(g["dw2"]), _ptr(g["dws1"]), _ptr(g["dws3"]), _ptr(g["dws2"]),
-                              _ptr(g["d_gate"]), _ptr(g["d_logits"]), _ptr(ws), ws.numel(),
+    dt, d, E, k = _dt(cfg), cfg.d, cfg.num_experts, cfg.top_k
+    f32 = torch.float32
+    if saved.dtype != torch.uint8:
+        raise ValueError(f"saved: dtype {saved.dtype}, expected torch.uint8")
+    weights = _weights(cfg, w1, w3, w2, ws1, ws3, ws2)
+    dweights = _weights(cfg, g["dw1"], g["dw3"], g["dw2"], g["dws1"], g["dws3"], g["dws2"])
+    _check(lib().moe_backward(ctypes.byref(cfg), T, _arg(x, "x", T * d, dt),
+                              _arg(w_router, "w_router", E * d, dt), *weights, _ptr(saved),
+                              saved.numel(), _arg(dy, "dy", T * d, dt), float(aux_alpha),
+                              _arg(g["dx"], "dx", T * d, dt),
+                              _arg(g["dw_router"], "dw_router", E * d, f32),
+                              dweights[0], dweights[1], dweights[2], dweights[3], dweights[4],
+                              dweights[5], _arg(g["d_gate"], "d_gate", T * k, f32),
+                              _arg(g["d_logits"], "d_logits", T * E, f32), _ptr(ws), ws.numel(),
                               _stream()), "moe_backward")
     return g
 

@@ -143,6 +143,29 @@ def test_binding_refuses_host_tensors():
                 torch.zeros((8, 256), dtype=torch.bfloat16))
 
 
+def test_binding_checks_dtype_and_size_of_each_argument():
+    """The binding compares every tensor with what the library will read or
+    write through its pointer (dtype, then element count, then device memory
+    and layout), before the call."""
+    import torch
+    c = cfg()
+    w2 = torch.zeros((c.num_experts, c.d, c.d_ff), dtype=torch.bfloat16)
+    n = c.num_experts * c.d * c.d_ff
+    with pytest.raises(ValueError, match="w2: dtype"):
+        B._arg(w2.float(), "w2", n, torch.bfloat16)
+    with pytest.raises(ValueError, match="w2: .* elements"):
+        B._arg(w2[:, :-1], "w2", n, torch.bfloat16)
+    with pytest.raises(ValueError, match="device memory"):
+        B._arg(w2, "w2", n, torch.bfloat16)
+    assert B._arg(None, "w2", n, torch.bfloat16) is None
+    x = torch.zeros((4, c.d), dtype=torch.bfloat16)
+    wr = torch.zeros((c.num_experts, c.d), dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="x: dtype"):
+        B.route(c, x.float(), wr)
+    with pytest.raises(ValueError, match="x: .* elements"):
+        B.forward(c, x[:, :-16], wr, w2, w2, w2, ws=torch.zeros(1, dtype=torch.uint8))
+
+
 def test_training_entry_points_reject_bad_arguments_before_any_gpu_work():
     L = B.lib()
     c = cfg()
