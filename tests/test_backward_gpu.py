@@ -151,6 +151,41 @@ def test_backward_matches_oracle(name):
     run_case(CASES[name], AUX.get(name, 0.0))
 
 
+def random_cases(n=16, seed=4048):
+    """Seeded random bf16 layers inside the library's limits (d, d_ff
+    multiples of 64; E up to 256; k up to min(E, 16)): each activation and
+    gating, with or without capacity (token- or slot-major), logit offsets, a
+    selection bias, shared experts and the balance loss, T from one token to
+    about a thousand.  Returns {name: (workload, aux_alpha)}."""
+    rng = np.random.default_rng(seed)
+    out = {}
+    for i in range(n):
+        E = int(rng.choice([1, 2, 5, 8, 16, 33, 64, 256]))
+        k = int(rng.integers(1, min(E, 16) + 1))
+        gating = str(rng.choice(["softmax_topk", "sigmoid_topk", "softmax_full"]))
+        S = int(rng.choice([0, 0, 1, 2]))
+        w = Workload(
+            name=f"random{i}", T=int(rng.choice([1, 9, 64, 200, 513, 1000])),
+            d=64 * int(rng.integers(1, 7)), E=E, k=k, d_ff=64 * int(rng.integers(1, 7)),
+            act=str(rng.choice(["relu", "gelu", "swiglu"])), gating=gating,
+            capacity_factor=float(rng.choice([0.0, 0.0, 0.6, 1.2])),
+            offset=("normal", 0.5) if rng.random() < 0.3 else None,
+            bias=("normal", 0.1) if gating == "sigmoid_topk" and rng.random() < 0.5 else None,
+            num_shared=S, d_ff_shared=64 * int(rng.integers(1, 4)) if S else 0,
+            capacity_priority=str(rng.choice(["token", "slot"])), seed=200 + i)
+        out[w.name] = (w, float(rng.choice([0.0, 0.0, 0.02])))
+    return out
+
+
+RANDOM = random_cases()
+
+
+@pytest.mark.parametrize("name", list(RANDOM))
+def test_backward_random_configuration(name):
+    w, aux = RANDOM[name]
+    run_case(w, aux)
+
+
 def test_backward_is_deterministic_and_reuses_buffers():
     w = small(T=257, E=8, k=2)
     inp = make_inputs(w, "cuda")

@@ -124,6 +124,46 @@ def test_sampled_edge_case(name):
     torch.cuda.empty_cache()
 
 
+def random_workloads(n=24, seed=2024):
+    """Seeded random layer configurations inside the library's limits: fp32 or
+    bf16 (dims multiples of 4 or 64), E up to 256, k up to min(E, 16), each
+    activation and gating, with or without capacity (token- or slot-major),
+    logit offsets, a selection bias (sigmoid gates), shared experts, and T
+    from one token (the small-batch path) to a few thousand."""
+    rng = np.random.default_rng(seed)
+    out = {}
+    for i in range(n):
+        dtype = "f32" if rng.random() < 0.2 else "bf16"
+        unit = 4 if dtype == "f32" else 64
+        E = int(rng.choice([1, 2, 3, 5, 8, 16, 33, 64, 128, 256]))
+        k = int(rng.integers(1, min(E, 16) + 1))
+        gating = str(rng.choice(["softmax_topk", "sigmoid_topk", "softmax_full"]))
+        S = int(rng.choice([0, 0, 0, 1, 2]))
+        w = Workload(
+            name=f"random{i}", T=int(rng.choice([1, 7, 33, 100, 257, 600, 1500])),
+            d=unit * int(rng.integers(1, 9)), E=E, k=k,
+            d_ff=unit * int(rng.integers(1, 9)), act=str(rng.choice(["relu", "gelu", "swiglu"])),
+            gating=gating, dtype=dtype,
+            capacity_factor=float(rng.choice([0.0, 0.0, 0.5, 1.0, 1.3])),
+            offset=("normal", 0.5) if rng.random() < 0.3 else None,
+            bias=("normal", 0.1) if gating == "sigmoid_topk" and rng.random() < 0.5 else None,
+            num_shared=S, d_ff_shared=unit * int(rng.integers(1, 4)) if S else 0,
+            capacity_priority=str(rng.choice(["token", "slot"])), seed=100 + i)
+        out[w.name] = w
+    return out
+
+
+RANDOM = random_workloads()
+
+
+@pytest.mark.parametrize("name", list(RANDOM))
+def test_random_configuration(name):
+    w = RANDOM[name]
+    say(f"[random] {w}")
+    rep = MC.check_layer(w)
+    say(f"[random] {name} ok {json.dumps(rep)}")
+
+
 @pytest.mark.parametrize("name", list(EDGES))
 def test_edge_case(name):
     w = EDGES[name]
