@@ -159,10 +159,14 @@ moe_status_t moe_capacity(const moe_config_t* cfg, int64_t T,
  *   workspace    optional device scratch (NULL allowed, 256-byte aligned).
  *                With T <= 16 (bf16) and ws_bytes >= moe_workspace_size(),
  *                the scores are computed split over K by many workgroups and
- *                reduced in a fixed order; otherwise it is not used.
+ *                reduced in a fixed order; with T > 16, E > 64 (bf16) and no
+ *                logits output it holds the scores between the two kernels
+ *                below; otherwise it is not used.
  * One fused kernel: MFMA score GEMM, then per-token top-k with wavefront
  * shuffles and the gates, from the scores held in LDS (small batches with a
- * workspace: a split-K score kernel plus one reduce-and-select kernel). */
+ * workspace: a split-K score kernel plus one reduce-and-select kernel; E > 64
+ * with logits or a workspace: the score GEMM in expert slices, then a
+ * select kernel).  The results do not depend on which path runs. */
 moe_status_t moe_route(const moe_config_t* cfg, int64_t T, const void* x,
                        const void* w_router, const float* logit_offset,
                        const float* select_bias, float* logits,
