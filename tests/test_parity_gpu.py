@@ -224,6 +224,33 @@ def test_capacity_drops_depend_on_the_batch():
         MC.check_outputs(ww, ii, g)
 
 
+@pytest.mark.parametrize("E,gating", [(65, "softmax_topk"), (128, "sigmoid_topk"),
+                                      (200, "softmax_full"), (256, "sigmoid_topk")])
+def test_expert_slice_router_agrees_with_fused(E, gating):
+    """For E > 64 and T > 16 the router computes the scores in expert slices
+    (into the logits output, or the workspace) and selects in a second
+    kernel; without either it runs the fused kernel.  Each score is the same
+    sequence of MFMAs on every path, so the three must agree bit for bit."""
+    w = small(T=333, E=E, d=192, k=min(6, E), act="swiglu", gating=gating,
+              offset=("normal", 0.5),
+              bias=("normal", 0.1) if gating == "sigmoid_topk" else None)
+    inp = make_inputs(w, "cuda")
+    cfg = B.config_for(w)
+    kw = dict(logit_offset=inp["logit_offset"], select_bias=inp["select_bias"])
+    fused = B.route(cfg, inp["x"], inp["w_router"], **kw)
+    via_ws = B.route(cfg, inp["x"], inp["w_router"], ws=B.workspace(cfg, w.T), **kw)
+    via_logits = B.route(cfg, inp["x"], inp["w_router"], want_logits=True, **kw)
+    torch.cuda.synchronize()
+    for other in (via_ws, via_logits):
+        assert torch.equal(fused[0], other[0]), "topk_idx differs between router paths"
+        assert torch.equal(fused[1].view(torch.int32), other[1].view(torch.int32)), \
+            "gates differ between router paths"
+    from oracle import moe_oracle as O
+    s_ref = O.router_logits(MC.np64(inp["x"]), MC.np64(inp["w_router"]),
+                            MC.np64(inp["logit_offset"]))
+    assert np.abs(via_logits[2].cpu().numpy() - s_ref).max() <= 1e-4
+
+
 @pytest.mark.parametrize("E,d", [(8, 256), (128, 192), (256, 128)])
 def test_small_batch_router_paths_agree(E, d):
     """T <= 16 has two router paths: split-K over many workgroups (with a
