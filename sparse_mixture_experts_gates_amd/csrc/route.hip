@@ -28,19 +28,21 @@ constexpr int RT_BT = 64;       // tokens per workgroup (fp32 path)
 // scores are computed in expert slices of 64 (E <= 128) or 128, two per token
 // block, and a second kernel runs the top-k: one workgroup per token block
 // with every expert streams the whole router matrix through each CU, with
-// half the CUs busy at E = 256 (DeepSeek-V3 shape: 0.195 -> 0.100 ms;
-// gpt-oss, E = 128: 0.082 -> 0.065 ms).
+// half the CUs busy at E = 256 (DeepSeek-V3 shape: 0.195 -> 0.086 ms;
+// gpt-oss, E = 128: 0.082 -> 0.050 ms, with the four-token selection below).
 constexpr int RT_SPLIT_MIN = 128;
 constexpr int RT_THREADS = 256;
 
 // Top-k and gates for the BT tokens whose scores sit in lg[BT][ld]; each of
-// the 4 waves handles BT/4 tokens.
-template <int EP, int BT>
+// the 4 waves handles BT/4 tokens, TPW_ of them at a time (0: as many as
+// keep one key per lane, at least one).
+template <int EP, int BT, int TPW_ = 0>
 __device__ void topk_from_lds(const float* lg, int ld, const RouteArgs& a,
                               int64_t t0) {
-  constexpr int TPW = EP <= 16 ? 4 : (EP <= 32 ? 2 : 1);  // tokens per wave pass
+  constexpr int TPW = TPW_ ? TPW_ : (EP <= 16 ? 4 : (EP <= 32 ? 2 : 1));  // tokens per pass
   constexpr int LPT = 64 / TPW;                            // lanes per token
-  constexpr int KPL = EP > 64 ? EP / 64 : 1;               // keys per lane
+  constexpr int KPL = EP > LPT ? EP / LPT : 1;             // keys per lane
+  static_assert(LPT >= 16, "a token's k <= 16 winners are written by its first k lanes");
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int sl = lane % LPT;
   const int E = a.E, k = a.k;
@@ -279,13 +281,31 @@ __global__ __launch_bounds__(RT_THREADS) void route_topk_kernel(RouteArgs a, con
   __shared__ float lg[BT * LD];
   const int64_t t0 = (int64_t)blockIdx.x * BT;
   const int E = a.E;
-  for (int idx = threadIdx.x; idx < BT * E; idx += RT_THREADS) {
-    const int tl = idx / E, e = idx - tl * E;
+  // every load of the tile in flight before the first LDS store
+  constexpr int PER = BT * EP / RT_THREADS;
+  static_assert(BT * EP % RT_THREADS == 0, "tile divides over the threads");
+  float v[PER];
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    const int idx = u * RT_THREADS + threadIdx.x;
+    const int tl = idx / EP, e = idx - tl * EP;
     const int64_t t = t0 + tl < a.T ? t0 + tl : a.T - 1;
-    lg[tl * LD + e] = sc[t * E + e];
+    v[u] = e < E ? sc[t * E + e] : 0.f;
+  }
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    const int idx = u * RT_THREADS + threadIdx.x;
+    lg[(idx / EP) * LD + idx % EP] = v[u];
   }
   __syncthreads();
-  topk_from_lds<EP, BT>(lg, LD, a, t0);
+  // four tokens per wave pass: 16 lanes per token, so each selection round is
+  // four shuffle steps and four tokens advance together.  Full-softmax gates
+  // sum exp over every expert across the lanes, so they keep the fused
+  // kernel's lane layout (and its summation order: the same bits).
+  if (a.gating == MOE_GATE_SOFTMAX_FULL)
+    topk_from_lds<EP, BT>(lg, LD, a, t0);
+  else
+    topk_from_lds<EP, BT, 4>(lg, LD, a, t0);
 }
 
 // Small batches (T <= 16, bf16): one workgroup of 8 waves splits the K
