@@ -584,7 +584,10 @@ hipError_t launch_route(const RouteArgs& a, hipStream_t s) {
   if (a.T == 0) return hipSuccess;
   // (padded E, tokens per workgroup, ring depth): fewer tokens per workgroup
   // for small E so that the grid covers the chip
-  if (a.E <= 16) return launch_ep<16, 16, 4>(a, s);
+  // E <= 16: 4 KB slabs, so a long K keeps 11 of them in flight (Mixtral
+  // shape, d = 4096: 19 -> 15 us); a short one (Switch, d = 768) is faster
+  // with 4 stages and more workgroups per CU
+  if (a.E <= 16) return a.d >= 2048 ? launch_ep<16, 16, 12>(a, s) : launch_ep<16, 16, 4>(a, s);
   if (a.E <= 32) return launch_ep<32, 32, 4>(a, s);
   if (a.E <= 64) return launch_ep<64, 32, 4>(a, s);
   if (a.E <= 128) return launch_ep<128, 64, 4>(a, s);
