@@ -157,8 +157,9 @@ __global__ __launch_bounds__(64) void permute_scatter_kernel(
 // (ballot groups, no atomics), the per-expert prefix over waves gives each
 // wave's starting ranks and the counts, capacity and offsets, and pass 2
 // re-walks the run to place every slot.  Same results as the three kernels.
-constexpr int FUSED_MAX = 2048;
+constexpr int FUSED_MAX = 8192;
 constexpr int FUSED_WAVES = 16;
+constexpr int FUSED_IT = FUSED_MAX / (FUSED_WAVES * 64);   // 64-slot groups per wave, at most
 
 __device__ __forceinline__ uint64_t expert_peers(int e, bool valid) {
   uint64_t peers = __ballot(valid);
@@ -188,16 +189,21 @@ __global__ __launch_bounds__(1024) void permute_fused_kernel(
   const int lo = w * per;
   const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   for (int e = lane; e < 256; e += 64) run[w][e] = 0;
+  // every expert id of this wave's run in flight at once, kept for both passes
+  int ev[FUSED_IT];
+#pragma unroll
+  for (int i = 0; i < FUSED_IT; ++i) {
+    const int a = lo + i * 64 + lane;
+    ev[i] = (i * 64 < per && a < n) ? idx[slot_of(a, tslot, k)] : -1;
+  }
   __syncthreads();
   // pass 1: per-wave counts
-  for (int st = 0; st < per; st += 64) {
-    const int a = lo + st + lane;
-    int e = -1;
-    bool valid = a < n;
-    if (valid) {
-      e = idx[slot_of(a, tslot, k)];
-      valid = e >= 0 && e < E;
-    }
+#pragma unroll
+  for (int i = 0; i < FUSED_IT; ++i) {
+    if (i * 64 >= per) break;
+    const int a = lo + i * 64 + lane;
+    const int e = ev[i];
+    const bool valid = a < n && e >= 0 && e < E;
     const uint64_t peers = expert_peers(e, valid);
     if (valid && (peers & lt) == 0) run[w][e] += __popcll(peers);
   }
@@ -246,15 +252,13 @@ __global__ __launch_bounds__(1024) void permute_fused_kernel(
   }
   const int total = sk[255];
   // pass 2: place every slot of this wave's run
-  for (int st = 0; st < per; st += 64) {
-    const int a = lo + st + lane;
+#pragma unroll
+  for (int i = 0; i < FUSED_IT; ++i) {
+    if (i * 64 >= per) break;
+    const int a = lo + i * 64 + lane;
     const int sa = a < n ? slot_of(a, tslot, k) : 0;   // physical slot
-    int e = -1;
-    bool valid = a < n;
-    if (valid) {
-      e = idx[sa];
-      valid = e >= 0 && e < E;
-    }
+    const int e = ev[i];
+    const bool valid = a < n && e >= 0 && e < E;
     const uint64_t peers = expert_peers(e, valid);
     int r = 0;
     if (valid) r = run[w][e] + __popcll(peers & lt);
