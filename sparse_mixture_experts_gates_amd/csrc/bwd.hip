@@ -977,20 +977,6 @@ int bwd_dx_split(int64_t rows, int G, int N, int K_all) {
   return best;
 }
 
-// Compute units of the current device (one persistent workgroup each).
-int cu_count() {
-  // per device, filled on first use (threads racing here store the same value)
-  static std::atomic<int> cached[64];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  int n = cached[dev].load(std::memory_order_relaxed);
-  if (n == 0) {
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
-      n = 256;
-    cached[dev].store(n, std::memory_order_relaxed);
-  }
-  return n;
-}
 
 int bwd_tile_rows() { return GB_BM; }
 int bwd_tile_cols() { return GB_BN; }
@@ -1040,16 +1026,17 @@ hipError_t launch_bwd_gemm(const BwdGemm& b, hipStream_t s) {
   a.NT = (b.N + GB_BN - 1) / GB_BN;
   constexpr int TH = 64 * GB_NW;
   unsigned grid;
+  int64_t prof_rec;
   if (b.kind == BG_DW) {
     const int64_t V = (int64_t)a.G * a.MT * a.NT;
     if (V == 0) return hipSuccess;
     grid = (unsigned)(a.counter && V > cu_count() ? cu_count() : V);
-    prof_before(b.name, s);
+    prof_rec = prof_before(b.name, s);
     bwd_gemm_kernel<BG_DW, 0><<<grid, TH, 0, s>>>(a);
   } else {
     if (b.max_entries == 0) return hipSuccess;
     grid = (unsigned)b.max_entries;
-    prof_before(b.name, s);
+    prof_rec = prof_before(b.name, s);
     if (b.kind == BG_DX) {
       if (b.epi == 1) bwd_gemm_kernel<BG_DX, 1><<<grid, TH, 0, s>>>(a);
       else bwd_gemm_kernel<BG_DX, 0><<<grid, TH, 0, s>>>(a);
@@ -1062,23 +1049,23 @@ hipError_t launch_bwd_gemm(const BwdGemm& b, hipStream_t s) {
       }
     }
   }
-  prof_after(s);
+  prof_after(prof_rec, s);
   return hipGetLastError();
 }
 
 hipError_t launch_gate_bwd(const GateBwdArgs& a, hipStream_t s) {
   if (a.T == 0) return hipSuccess;
-  prof_before("bwd_gate", s);
+  const int64_t prof_rec = prof_before("bwd_gate", s);
   gate_bwd_kernel<<<(unsigned)((a.T + 3) / 4), 256, 0, s>>>(a);
-  prof_after(s);
+  prof_after(prof_rec, s);
   return hipGetLastError();
 }
 
 hipError_t launch_dx(const DxArgs& a, hipStream_t s) {
   if (a.T == 0) return hipSuccess;
-  prof_before("bwd_dx_sum", s);
+  const int64_t prof_rec = prof_before("bwd_dx_sum", s);
   dx_kernel<<<dim3((unsigned)((a.T + 3) / 4), (unsigned)((a.d / 8 + 63) / 64)), 256, 0, s>>>(a);
-  prof_after(s);
+  prof_after(prof_rec, s);
   return hipGetLastError();
 }
 
@@ -1087,12 +1074,12 @@ hipError_t launch_router_bwd(const WrArgs& in, hipStream_t s) {
   WrArgs a = in;
   a.chunk = wr_chunk(a.T, a.E, a.d);
   const int nch = (int)((a.T + a.chunk - 1) / a.chunk);
-  prof_before("bwd_router", s);
+  const int64_t prof_rec = prof_before("bwd_router", s);
   dim3 grid((a.d + WR_COLS - 1) / WR_COLS, (a.E + WR_EB - 1) / WR_EB, nch);
   wr_partial_kernel<<<grid, 256, 0, s>>>(a);
   const int64_t n = (int64_t)a.E * a.d;
   wr_reduce_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(a, nch);
-  prof_after(s);
+  prof_after(prof_rec, s);
   return hipGetLastError();
 }
 

@@ -134,7 +134,7 @@ hipError_t launch_combine(const CombineArgs& a, hipStream_t s) {
   if (a.T == 0) return hipSuccess;
   const int64_t ncg = a.dtype == MOE_BF16 ? (a.d + CB_COLS - 1) / CB_COLS : (a.d + 255) / 256;
   const unsigned grid = (unsigned)((a.T * ncg + 3) / 4);
-  prof_before("combine", s);
+  const int64_t prof_rec = prof_before("combine", s);
   if (a.dtype == MOE_BF16) {
     if (a.part) {
       if (a.k <= 2) combine_bf16_kernel<2, true><<<grid, 256, 0, s>>>(a);
@@ -150,7 +150,7 @@ hipError_t launch_combine(const CombineArgs& a, hipStream_t s) {
   }
   else
     combine_f32_kernel<<<grid, 256, 0, s>>>(a);
-  prof_after(s);
+  prof_after(prof_rec, s);
   return hipGetLastError();
 }
 

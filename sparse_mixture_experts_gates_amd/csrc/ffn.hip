@@ -618,19 +618,6 @@ void launch_bf16(int mode, unsigned grid, const KArgs& k, hipStream_t s) {
   }
 }
 
-// Compute units of the current device (one persistent block each).
-int device_cus() {
-  static int cached[64] = {0};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return kCUs;
-  if (cached[dev] == 0) {
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
-      n = kCUs;
-    cached[dev] = n;
-  }
-  return cached[dev];
-}
 
 }  // namespace
 
@@ -679,9 +666,9 @@ bool ffn_plan_spec(const FfnPassArgs& p1, const FfnPassArgs& p2, PlanSpec* ps) {
 hipError_t launch_plan_kernel(const int32_t* seg, int G, int64_t dense_rows, const PlanSpec& ps,
                               hipStream_t s) {
   if (G > 1024) return hipErrorInvalidValue;
-  prof_before("plan", s);
+  const int64_t prof_rec = prof_before("plan", s);
   ffn_plan_kernel<<<1, 1024, 0, s>>>(seg, G, dense_rows, ps);
-  prof_after(s);
+  prof_after(prof_rec, s);
   return hipGetLastError();
 }
 
@@ -691,9 +678,9 @@ hipError_t launch_ffn_plans(const FfnPassArgs& p1, const FfnPassArgs& p2, hipStr
     const Shape sh1 = pick_shape(p1.dtype, p1.small, p1.mode, p1.max_rows, p1.N);
     return max_entries(p1.max_rows, p1.G, p1.N, sh1) == 0 ? hipSuccess : hipErrorInvalidValue;
   }
-  prof_before(p1.seg_offsets ? "ffn_plan" : "ffn_plan_shared", s);
+  const int64_t prof_rec = prof_before(p1.seg_offsets ? "ffn_plan" : "ffn_plan_shared", s);
   ffn_plan_kernel<<<1, 1024, 0, s>>>(p1.seg_offsets, p1.G, p1.dense_rows, ps);
-  prof_after(s);
+  prof_after(prof_rec, s);
   return hipGetLastError();
 }
 
@@ -729,7 +716,7 @@ hipError_t launch_ffn_pass(const FfnPassArgs& p, hipStream_t s) {
     return hipErrorInvalidValue;
   const char* nm = p.seg_offsets ? (p.mode == MODE_PLAIN ? "ffn2" : "ffn1")
                                  : (p.mode == MODE_PLAIN ? "ffn2_shared" : "ffn1_shared");
-  prof_before(nm, s);
+  const int64_t prof_rec = prof_before(nm, s);
   if (p.dtype == MOE_F32) {
     switch (p.mode) {
       case MODE_PLAIN: ffn_f32_kernel<MODE_PLAIN><<<(unsigned)grid, 256, 0, s>>>(k); break;
@@ -746,7 +733,7 @@ hipError_t launch_ffn_pass(const FfnPassArgs& p, hipStream_t s) {
       if (p.mode == MODE_RELU) ffn_bf16_kernel<32, 64, 1, 4, 4, 4, MODE_RELU, false, false, true><<<(unsigned)grid, T4, 0, s>>>(k);
       else if (p.mode == MODE_GELU) ffn_bf16_kernel<32, 64, 1, 4, 4, 4, MODE_GELU, false, false, true><<<(unsigned)grid, T4, 0, s>>>(k);
       else return hipErrorInvalidValue;
-      prof_after(s);
+      prof_after(prof_rec, s);
       return hipGetLastError();
     }
     switch (p.mode) {
@@ -758,7 +745,7 @@ hipError_t launch_ffn_pass(const FfnPassArgs& p, hipStream_t s) {
   } else {
     // With at least two rounds of tiles: one persistent block per CU (the
     // LDS ring fills a CU).  Fewer, short tiles do not repay the queue.
-    const int cus = device_cus();
+    const int cus = cu_count();
     if (grid >= 2 * (int64_t)cus) {
       if (sh.id == 3) launch_bf16<256, 128, 4, 2, 3, 3, true>(p.mode, (unsigned)cus, k, s);
       else if (split > 1)
@@ -771,7 +758,7 @@ hipError_t launch_ffn_pass(const FfnPassArgs& p, hipStream_t s) {
       else launch_bf16<256, 256, 2, 4, 2, 2, false>(p.mode, (unsigned)grid, k, s);
     }
   }
-  prof_after(s);
+  prof_after(prof_rec, s);
   return hipGetLastError();
 }
 
@@ -799,10 +786,10 @@ hipError_t launch_ffn_split_reduce(const FfnPassArgs& p, hipStream_t s) {
   if (p.split != 2) return hipErrorInvalidValue;
   const int64_t n8 = p.max_rows * (int64_t)p.N / 8;
   if (n8 == 0) return hipSuccess;
-  prof_before("ffn2_split_reduce", s);
+  const int64_t prof_rec = prof_before("ffn2_split_reduce", s);
   split_reduce_kernel<<<(unsigned)((n8 + 255) / 256), 256, 0, s>>>(
       p.part, p.max_rows * (int64_t)p.N, static_cast<uint16_t*>(p.C), n8);
-  prof_after(s);
+  prof_after(prof_rec, s);
   return hipGetLastError();
 }
 

@@ -8,9 +8,15 @@
 
 namespace moe {
 
-// Named-kernel launch bracket for the optional event profiler (moe_api.hip).
-void prof_before(const char* name, hipStream_t s);
-void prof_after(hipStream_t s);
+// Named-kernel launch bracket for the optional event profiler (moe_api.hip):
+// prof_before records the start event and returns a handle (-1 when the
+// profiler is off) that the matching prof_after takes, so launches from
+// several host threads pair their own events.
+int64_t prof_before(const char* name, hipStream_t s);
+void prof_after(int64_t rec, hipStream_t s);
+
+// Compute units of the current device (one persistent workgroup each).
+int cu_count();
 
 struct RouteArgs {
   const void* x;

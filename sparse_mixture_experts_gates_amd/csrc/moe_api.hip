@@ -27,6 +27,7 @@ std::mutex g_prof_mu;
 std::atomic<bool> g_prof_on{false};   // read by every launch, set under the mutex
 std::vector<ProfRec> g_prof_recs;
 std::vector<hipEvent_t> g_prof_pool;
+uint32_t g_prof_gen = 0;          // generation of g_prof_recs (under the mutex)
 
 hipEvent_t prof_event() {
   if (!g_prof_pool.empty()) {
@@ -40,19 +41,40 @@ hipEvent_t prof_event() {
 }
 }  // namespace
 
-void prof_before(const char* name, hipStream_t s) {
-  if (!g_prof_on.load(std::memory_order_relaxed)) return;
+// A handle is the record's index in the low 32 bits and the generation of
+// the record list (bumped whenever moe_profile_enable / moe_profile_read
+// clear it) above them, so an end event never lands on another launch's
+// record or on a list that was cleared in between.
+int64_t prof_before(const char* name, hipStream_t s) {
+  if (!g_prof_on.load(std::memory_order_relaxed)) return -1;
   std::lock_guard<std::mutex> lk(g_prof_mu);
   ProfRec r{name, prof_event(), prof_event()};
-  if (!r.e0 || !r.e1) return;
+  if (!r.e0 || !r.e1) return -1;
   hipEventRecord(r.e0, s);
   g_prof_recs.push_back(r);
+  return ((int64_t)g_prof_gen << 32) | (int64_t)(g_prof_recs.size() - 1);
 }
 
-void prof_after(hipStream_t s) {
-  if (!g_prof_on.load(std::memory_order_relaxed)) return;
+void prof_after(int64_t rec, hipStream_t s) {
+  if (rec < 0) return;
   std::lock_guard<std::mutex> lk(g_prof_mu);
-  if (!g_prof_recs.empty()) hipEventRecord(g_prof_recs.back().e1, s);
+  const uint32_t gen = (uint32_t)(rec >> 32);
+  const size_t i = (size_t)(rec & 0xffffffff);
+  if (gen == g_prof_gen && i < g_prof_recs.size()) hipEventRecord(g_prof_recs[i].e1, s);
+}
+
+int cu_count() {
+  // per device, filled on first use (threads racing here store the same value)
+  static std::atomic<int> cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int n = cached[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cached[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
 }
 
 }  // namespace moe
@@ -579,6 +601,7 @@ moe_status_t moe_profile_enable(int32_t on) {
     g_prof_pool.push_back(r.e1);
   }
   g_prof_recs.clear();
+  ++g_prof_gen;
   g_prof_on.store(on != 0, std::memory_order_relaxed);
   return MOE_OK;
 }
@@ -612,6 +635,7 @@ int32_t moe_profile_read(const char** names, double* total_ms, int32_t* launches
     g_prof_pool.push_back(r.e1);
   }
   g_prof_recs.clear();
+  ++g_prof_gen;
   if (rc < 0) return -1;
   int32_t n = 0;
   for (size_t i = 0; i < nm.size() && n < max_names; ++i, ++n) {

@@ -300,32 +300,32 @@ hipError_t launch_permute(const PermuteArgs& a, hipStream_t s, bool* plans_built
   const int tslot = a.slot_major && a.k > 1 ? (int)a.T : 0;
   if (n == 0) return hipSuccess;
   if (n <= FUSED_MAX) {
-    prof_before("permute", s);
+    const int64_t prof_rec = prof_before("permute", s);
     const PlanSpec none{0, 0, 0, 1, nullptr, nullptr};
     permute_fused_kernel<<<1, 1024, 0, s>>>(a.topk_idx, (int)n, a.E, a.capacity, a.counts,
                                             a.offsets, a.perm_src, a.slot_pos, a.num_dropped,
                                             a.kept_total, a.plans ? *a.plans : none,
                                             a.plans ? 1 : 0, tslot, a.k);
     if (plans_built && a.plans) *plans_built = true;
-    prof_after(s);
+    prof_after(prof_rec, s);
   } else {
   const int nb = permute_nblocks(n);
-  prof_before("permute_count", s);
+  int64_t prof_rec = prof_before("permute_count", s);
   permute_count_kernel<<<nb, 256, 0, s>>>(a.topk_idx, n, a.E, a.block_counts, tslot, a.k);
-  prof_after(s);
-  prof_before("permute_scan", s);
+  prof_after(prof_rec, s);
+  prof_rec = prof_before("permute_scan", s);
   permute_scan_kernel<<<1, 256, 0, s>>>(a.block_counts, nb, a.E, a.capacity, a.counts,
                                         a.offsets, a.num_dropped, a.kept_total);
-  prof_after(s);
-  prof_before("permute_scatter", s);
+  prof_after(prof_rec, s);
+  prof_rec = prof_before("permute_scatter", s);
   permute_scatter_kernel<<<nb, 64, 0, s>>>(a.topk_idx, n, a.E, a.capacity, a.block_counts,
                                            a.offsets, a.kept_total, a.perm_src, a.slot_pos,
                                            tslot, a.k);
-  prof_after(s);
+  prof_after(prof_rec, s);
   }
   if (a.x_perm) {
     const unsigned grid = (unsigned)((n + 3) / 4);
-    prof_before("gather", s);
+    const int64_t prof_rec = prof_before("gather", s);
     if (a.dtype == MOE_BF16)
       gather_rows_kernel<uint4, 8><<<grid, 256, 0, s>>>(
           static_cast<const uint4*>(a.x), static_cast<uint4*>(a.x_perm), a.perm_src,
@@ -334,7 +334,7 @@ hipError_t launch_permute(const PermuteArgs& a, hipStream_t s, bool* plans_built
       gather_rows_kernel<uint4, 4><<<grid, 256, 0, s>>>(
           static_cast<const uint4*>(a.x), static_cast<uint4*>(a.x_perm), a.perm_src,
           a.kept_total, n, a.k, a.d / 4);
-    prof_after(s);
+    prof_after(prof_rec, s);
   }
   return hipGetLastError();
 }

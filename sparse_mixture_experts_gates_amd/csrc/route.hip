@@ -547,7 +547,7 @@ __global__ __launch_bounds__(RT_THREADS) void route_f32_kernel(RouteArgs a) {
 
 template <int EP, int BT, int NS>
 hipError_t launch_ep(const RouteArgs& a, hipStream_t s) {
-  prof_before("route", s);
+  const int64_t prof_rec = prof_before("route", s);
   if (a.dtype == MOE_BF16 && a.T <= 16 && a.partial) {
     const int sp = route_split(a.d, a.E);
     route_partial_kernel<EP><<<dim3(EP / 16, sp), 256, 0, s>>>(a, sp);
@@ -567,7 +567,7 @@ hipError_t launch_ep(const RouteArgs& a, hipStream_t s) {
     route_bf16_kernel<EP, BT, NS><<<(unsigned)((a.T + BT - 1) / BT), RT_THREADS, 0, s>>>(a);
   else
     route_f32_kernel<EP><<<(unsigned)((a.T + RT_BT - 1) / RT_BT), RT_THREADS, 0, s>>>(a);
-  prof_after(s);
+  prof_after(prof_rec, s);
   return hipGetLastError();
 }
 

@@ -151,7 +151,7 @@ size_t stats_ws_bytes(int64_t T, int E) { return (size_t)stats_nblocks(T) * E * 
 hipError_t launch_stats(const StatsArgs& a, hipStream_t s) {
   if (a.T == 0) return hipSuccess;
   const int nblk = stats_nblocks(a.T);
-  prof_before("routing_stats", s);
+  const int64_t prof_rec = prof_before("routing_stats", s);
   if (a.E <= 8) stats_probs_kernel<8><<<nblk, 256, 0, s>>>(a);
   else if (a.E <= 16) stats_probs_kernel<16><<<nblk, 256, 0, s>>>(a);
   else if (a.E <= 32) stats_probs_kernel<32><<<nblk, 256, 0, s>>>(a);
@@ -159,7 +159,7 @@ hipError_t launch_stats(const StatsArgs& a, hipStream_t s) {
   else if (a.E <= 128) stats_probs_kernel<128><<<nblk, 256, 0, s>>>(a);
   else stats_probs_kernel<256><<<nblk, 256, 0, s>>>(a);
   stats_final_kernel<<<1, ST_FINAL, 0, s>>>(a, nblk);
-  prof_after(s);
+  prof_after(prof_rec, s);
   return hipGetLastError();
 }
 
