@@ -7,17 +7,22 @@ gate-weighted combine.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                     [--no-cpu-baseline] [--graph] [--cold-runs N] [--copy-calib MiB]
-                    [--no-backward]
+                    [--no-backward] [--no-per-config]
 
-Prints one JSON line.  `value` is tokens/s of the whole layer over K
-back-to-back steps; `roofline` reports the dominant kernel (the first grouped
-GEMM) against the bf16 MFMA peak (HBM peak for a decode batch), timed with HIP
-events recorded by the library around each of its launches inside a second
-timed region; `cold` times N single steps each after a 1 GiB write that
-evicts L2 and the Infinity Cache; `next_rows` times the routing statistics
-call and the training step (moe_forward_train + moe_backward, per kernel);
-`cpu_baseline` times the CPU oracle on a bounded token sample of the same
-workload.
+Prints one JSON line.  `value` is tokens/s of the headline workload (the
+Mixtral-shape prefill) over K back-to-back steps; `roofline` reports its
+dominant kernel (the first grouped GEMM) against the bf16 MFMA peak, timed
+with HIP events recorded by the library around each of its launches inside a
+second timed region; `subsystems` gives every kernel's time and its rate
+against its own bound (router, permutation, gather, combine in GB/s of
+algorithmic bytes; expert GEMMs in TFLOP/s, or GB/s for a decode batch);
+`cold` times N single steps each after a 1 GiB write that evicts L2 and the
+Infinity Cache; `next_rows` times the routing statistics call and the
+training step (moe_forward_train + moe_backward, per kernel);
+`per_config` repeats the step measurement for every other workload (the toy
+fp32 layer, the Switch layer with both gatings, DeepSeek-V3, gpt-oss prefill
+and decode; the small ones also as a replayed HIP graph); `cpu_baseline` times
+the CPU oracle on a bounded token sample of the headline workload.
 """
 
 from __future__ import annotations
@@ -209,6 +214,180 @@ def measure_backward(B, w, inp, cfg, counts, steps, warmup):
     return out
 
 
+def subsystem_work(w, kept_counts, active):
+    """Algorithmic work of each kernel of one step, by the profiler's kernel
+    name: (bound, amount, unit) with bytes for the HBM-bound kernels and
+    FLOPs for the expert GEMMs (bytes when the batch is a decode batch).
+
+    route: x and W_r read, the k indices and gates written; permute: the k
+    indices read, perm_src / slot_pos written; gather (stepwise path only):
+    each kept row read and written; combine: each kept expert-output row and
+    the shared outputs read, the gates and slot positions read, y written."""
+    b = 2 if w.dtype == "bf16" else 4
+    n_mat = 3 if w.act == "swiglu" else 2
+    kept = int(sum(kept_counts))
+    R = w.T * w.k
+    decode = R <= 64
+    out = {
+        "route": ("hbm", w.T * w.d * b + w.E * w.d * b + 8 * R, "B"),
+        "permute": ("hbm", 4 * R + 8 * R, "B"),
+        # small batches: router and permutation in one launch pair
+        "route_permute": ("hbm", w.T * w.d * b + w.E * w.d * b + 8 * R + 12 * R, "B"),
+        "gather": ("hbm", 2 * kept * w.d * b, "B"),
+        "combine": ("hbm", kept * w.d * b + w.num_shared * w.T * w.d * b + 8 * R
+                    + w.T * w.d * b, "B"),
+    }
+    if decode:
+        out["ffn1"] = ("hbm", active * (n_mat - 1) * w.d * w.d_ff * b + kept * (w.d + w.d_ff) * b, "B")
+        out["ffn2"] = ("hbm", active * w.d * w.d_ff * b + kept * (w.d + w.d_ff) * b, "B")
+    else:
+        out["ffn1"] = ("mfma", kept * (n_mat - 1) * 2 * w.d * w.d_ff, "FLOP")
+        out["ffn2"] = ("mfma", kept * 2 * w.d * w.d_ff, "FLOP")
+    if w.num_shared:
+        out["ffn1_shared"] = ("mfma", w.num_shared * 2 * 2 * w.T * w.d * w.d_ff_shared, "FLOP")
+        out["ffn2_shared"] = ("mfma", w.num_shared * 2 * w.T * w.d * w.d_ff_shared, "FLOP")
+    return out
+
+
+def rate_of(kind, amount, ms, peak_flops):
+    if ms is None or not ms > 0:
+        return None
+    if kind == "hbm":
+        gbs = amount / (ms * 1e-3) / 1e9
+        return {"ms": ms, "bound": "hbm", "GB_s": gbs, "frac": gbs / PEAK_HBM_GBS}
+    tf = amount / (ms * 1e-3) / 1e12
+    return {"ms": ms, "bound": "mfma", "TFLOP_s": tf, "frac": tf / peak_flops}
+
+
+def measure_workload(B, w, steps, warmup, graph=False, gather=True, dev="cuda:0"):
+    """Inputs, warm-up, K timed back-to-back steps (and, with graph=True, K
+    replays of one captured step), per-kernel times from the library's HIP
+    events, and the batch's routing.  Returns (result dict, inputs, cfg)."""
+    import torch
+    from sparse_mixture_experts_gates_amd.workloads import make_inputs
+    inp = make_inputs(w, dev)
+    cfg = B.config_for(w)
+    ws = B.workspace(cfg, w.T, dev)
+    y = torch.empty((w.T, w.d), dtype=w.torch_dtype, device=dev)
+
+    def step():
+        B.forward(cfg, inp["x"], inp["w_router"], inp["w1"], inp["w2"], inp["w3"],
+                  logit_offset=inp["logit_offset"], select_bias=inp["select_bias"],
+                  ws1=inp["ws1"], ws3=inp["ws3"], ws2=inp["ws2"], ws=ws, y=y, outputs=False)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    _, _, _, cnt_dev, drp_dev = B.forward_inputs(cfg, inp, ws=ws)
+    torch.cuda.synchronize()
+    cnt = cnt_dev.cpu().tolist()
+    dropped = int(drp_dev.item())
+    kept_counts = [min(c, B.capacity(cfg, w.T)) for c in cnt] if w.capacity_factor > 0 else cnt
+    work = algorithmic_work(w, kept_counts)
+
+    def timed(fn):
+        torch.cuda.synchronize()
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for _ in range(steps):
+            fn()
+        t1.record()
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1) / steps
+
+    ms = timed(step)
+    ms_graph = None
+    if graph:
+        # the library launches on torch's current stream, so a capture on a
+        # side stream records every kernel of the step
+        g = torch.cuda.CUDAGraph()
+        cs = torch.cuda.Stream()
+        cs.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(cs):
+            step()
+            torch.cuda.synchronize()
+            with torch.cuda.graph(g, stream=cs):
+                step()
+        torch.cuda.current_stream().wait_stream(cs)
+        torch.cuda.synchronize()
+        for _ in range(warmup):
+            g.replay()
+        ms_graph = timed(g.replay)
+
+    # per-kernel times: the same steps with the library's per-launch events
+    B.profile_enable(True)
+    torch.cuda.synchronize()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    prof = B.profile_read()
+    B.profile_enable(False)
+    kern = {k: v[0] / max(v[1], 1) for k, v in prof.items()}
+    # the row gather as a pass of its own (the stepwise moe_permute with
+    # x_perm; moe_forward folds it into the first GEMM's loads)
+    if gather and w.T * w.k > 0:
+        idx, _, _ = B.route(cfg, inp["x"], inp["w_router"], inp["logit_offset"],
+                            inp["select_bias"], ws=ws)
+        B.permute(cfg, idx, inp["x"], gather=True, ws=ws)
+        torch.cuda.synchronize()
+        B.profile_enable(True)
+        for _ in range(steps):
+            B.permute(cfg, idx, inp["x"], gather=True, ws=ws)
+        torch.cuda.synchronize()
+        gp = B.profile_read()
+        B.profile_enable(False)
+        if "gather" in gp:
+            kern["gather"] = gp["gather"][0] / max(gp["gather"][1], 1)
+
+    active = work["active"]
+    peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
+    decode = w.T * w.k <= B.DECODE_MAX_ROWS
+    subs = {}
+    if "permute" not in kern and "permute_scatter" in kern:   # chunked permutation
+        kern["permute"] = sum(kern.pop(n) for n in ("permute_count", "permute_scan",
+                                                     "permute_scatter") if n in kern)
+    for name, (kind, amount, unit) in subsystem_work(w, kept_counts, active).items():
+        r = rate_of(kind, amount, kern.get(name), peak)
+        if r is not None:
+            r["algorithmic_" + ("bytes" if unit == "B" else "flops")] = amount
+            subs[name] = r
+    for name, v in kern.items():          # plans, split reduce, chunked permutation
+        if name not in subs:
+            subs[name] = {"ms": v}
+    tflops = work["flops"] / (ms * 1e-3) / 1e12
+    gbs = work["bytes"] / (ms * 1e-3) / 1e9
+    res = {
+        "workload": w.name,
+        "config": {"T": w.T, "d": w.d, "E": w.E, "k": w.k, "d_ff": w.d_ff, "act": w.act,
+                   "gating": w.gating, "dtype": w.dtype, "capacity_factor": w.capacity_factor,
+                   "num_shared": w.num_shared, "d_ff_shared": w.d_ff_shared},
+        "bound": "hbm" if decode else ("mfma" if w.T * w.k >= 4096 else "latency"),
+        "ms_per_step": ms,
+        "tokens_per_s": w.T / (ms * 1e-3),
+        "active_tflops": tflops,
+        "frac_of_peak": tflops / peak,
+        "peak_tflops": peak,
+        "algorithmic_gbs": gbs,
+        "frac_of_hbm": gbs / PEAK_HBM_GBS,
+        "routing": {"kept_rows": work["kept"], "active_experts": active, "dropped": dropped},
+        "subsystems": subs,
+    }
+    if ms_graph is not None:
+        res["hip_graph"] = {"ms_per_step": ms_graph, "tokens_per_s": w.T / (ms_graph * 1e-3),
+                            "algorithmic_gbs": work["bytes"] / (ms_graph * 1e-3) / 1e9,
+                            "frac_of_hbm": work["bytes"] / (ms_graph * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                            "active_tflops": work["flops"] / (ms_graph * 1e-3) / 1e12}
+    ctx = dict(inp=inp, cfg=cfg, ws=ws, y=y, step=step, work=work, kern=kern,
+               kept_counts=kept_counts, cnt_dev=cnt_dev, drp_dev=drp_dev)
+    return res, ctx
+
+
+PER_CONFIG = ("toy_fp32", "switch_bf16", "switch_softmax_full_bf16", "deepseek_v3_bf16",
+              "gptoss_prefill_bf16", "gptoss_decode_bf16")
+GRAPHED = ("toy_fp32", "switch_bf16", "switch_softmax_full_bf16", "gptoss_decode_bf16")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -217,12 +396,14 @@ def main():
     ap.add_argument("--workload", default="mixtral_bf16")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--graph", action="store_true",
-                    help="capture one step in a HIP graph (torch.cuda.CUDAGraph) and time replays")
+                    help="also time replays of one step captured in a HIP graph")
     ap.add_argument("--cold-runs", type=int, default=20,
                     help="extra single-step runs, each after writing 1 GiB to flush L2 and "
                          "the Infinity Cache (median / min / p90 reported; 0 = skip)")
     ap.add_argument("--no-backward", action="store_true",
                     help="skip the training-step measurement (forward_train + backward)")
+    ap.add_argument("--no-per-config", action="store_true",
+                    help="measure the headline workload only")
     ap.add_argument("--copy-calib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -234,41 +415,15 @@ def main():
 
     import torch
     from sparse_mixture_experts_gates_amd import binding as B
-    from sparse_mixture_experts_gates_amd.workloads import WORKLOADS, make_inputs
+    from sparse_mixture_experts_gates_amd.workloads import WORKLOADS
 
     w = WORKLOADS[args.workload]
     dev = "cuda:0"
     torch.cuda.set_device(0)
-    inp = make_inputs(w, dev)
-    cfg = B.config_for(w)
-    ws = B.workspace(cfg, w.T, dev)
-    y = torch.empty((w.T, w.d), dtype=w.torch_dtype, device=dev)
-    idx = torch.empty((w.T, w.k), dtype=torch.int32, device=dev)
-    gate = torch.empty((w.T, w.k), dtype=torch.float32, device=dev)
-    counts = torch.empty(w.E, dtype=torch.int32, device=dev)
-    dropped = torch.empty(1, dtype=torch.int32, device=dev)
-
-    def step():
-        B.forward(cfg, inp["x"], inp["w_router"], inp["w1"], inp["w2"], inp["w3"],
-                  logit_offset=inp["logit_offset"], select_bias=inp["select_bias"],
-                  ws1=inp["ws1"], ws3=inp["ws3"], ws2=inp["ws2"], ws=ws, y=y, outputs=False)
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    # routing statistics of this batch (for the algorithmic work)
-    B.forward(cfg, inp["x"], inp["w_router"], inp["w1"], inp["w2"], inp["w3"],
-              logit_offset=inp["logit_offset"], select_bias=inp["select_bias"],
-              ws1=inp["ws1"], ws3=inp["ws3"], ws2=inp["ws2"], ws=ws, y=y)
-    _, _, _, cnt_dev, drp_dev = B.forward_inputs(cfg, inp, ws=ws)
-    torch.cuda.synchronize()
-    cnt, drp = cnt_dev.cpu().tolist(), drp_dev
-    if w.capacity_factor > 0:
-        C = B.capacity(cfg, w.T)
-        kept_counts = [min(c, C) for c in cnt]
-    else:
-        kept_counts = cnt
-    work = algorithmic_work(w, kept_counts)
+    head, ctx = measure_workload(B, w, args.steps, args.warmup, graph=args.graph)
+    inp, cfg, ws, step = ctx["inp"], ctx["cfg"], ctx["ws"], ctx["step"]
+    work, kern = ctx["work"], ctx["kern"]
+    ms = head["ms_per_step"]
 
     if args.copy_calib:
         n = args.copy_calib * (1 << 20) // 4
@@ -277,36 +432,6 @@ def main():
         b.copy_(a)
         torch.cuda.synchronize()
         del a, b
-
-    run = step
-    if args.graph:
-        # the library launches on torch's current stream, so a capture on a
-        # side stream records every kernel of the step; replays reuse the
-        # same buffers
-        g = torch.cuda.CUDAGraph()
-        cs = torch.cuda.Stream()
-        cs.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(cs):
-            step()
-            torch.cuda.synchronize()
-            with torch.cuda.graph(g, stream=cs):
-                step()
-        torch.cuda.current_stream().wait_stream(cs)
-        torch.cuda.synchronize()
-        run = g.replay
-        for _ in range(args.warmup):
-            run()
-
-    # timed region 1: whole steps (the throughput `value`)
-    torch.cuda.synchronize()
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
-    t0.record()
-    for _ in range(args.steps):
-        run()
-    t1.record()
-    torch.cuda.synchronize()
-    ms = t0.elapsed_time(t1) / args.steps
 
     # cold runs: each step after a 1 GiB write that evicts L2 and the 256 MB
     # Infinity Cache (the flush is not timed)
@@ -319,7 +444,7 @@ def main():
         for i in range(args.cold_runs):
             flush.fill_(float(i))
             c0.record()
-            run()
+            step()
             c1.record()
             torch.cuda.synchronize()
             times.append(c0.elapsed_time(c1))
@@ -336,36 +461,26 @@ def main():
     bias_in = (inp["select_bias"] if inp["select_bias"] is not None
                else torch.zeros(w.E, dtype=torch.float32, device=dev))
     stats_out = torch.empty(w.E, dtype=torch.float32, device=dev)
-
+    cnt_dev, drp_dev = ctx["cnt_dev"], ctx["drp_dev"]
     st_res = B.routing_stats(cfg, logits, cnt_dev, drp_dev, bias_in, gamma=1e-3, alpha=0.01,
                              bias_out=stats_out, ws=ws)
-
-    def stats():
+    torch.cuda.synchronize()
+    B.profile_enable(True)
+    for _ in range(args.steps):
         B.routing_stats(cfg, logits, cnt_dev, drp_dev, bias_in, gamma=1e-3, alpha=0.01,
                         bias_out=stats_out, ws=ws, out=st_res)
-
     torch.cuda.synchronize()
-
-    # timed region 2: the same steps with the library's per-launch HIP events
-    # (on the stream each kernel is launched on) for the per-kernel times
-    B.profile_enable(True)
-    torch.cuda.synchronize()
-    for _ in range(args.steps):
-        step()
-    for _ in range(args.steps):
-        stats()
-    torch.cuda.synchronize()
-    prof = B.profile_read()
+    sp = B.profile_read()
     B.profile_enable(False)
-
-    kern = {k: v[0] / max(v[1], 1) for k, v in prof.items()}
-    st_ms = kern.pop("routing_stats", float("nan"))
+    st_ms = sp["routing_stats"][0] / max(sp["routing_stats"][1], 1) if "routing_stats" in sp \
+        else float("nan")
     # bytes: the scores once, counts, bias in and out, f, P
     st_bytes = w.T * w.E * 4 + 5 * w.E * 4
     next_rows = {"routing_stats": {
         "ms": st_ms, "bound": "hbm", "algorithmic_bytes": st_bytes,
         "achieved_gbs": st_bytes / (st_ms * 1e-3) / 1e9,
         "frac": st_bytes / (st_ms * 1e-3) / 1e9 / PEAK_HBM_GBS}}
+
     dom = "ffn1"
     dom_ms = kern.get(dom, float("nan"))
     peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
@@ -381,8 +496,6 @@ def main():
     roof["frac"] = roof["achieved"] / roof["peak"]
     roof["traffic"] = measured_traffic(dom, w.name)
     roof["avg_ms"] = dom_ms
-    tflops = work["flops"] / (ms * 1e-3) / 1e12
-    gbs = work["bytes"] / (ms * 1e-3) / 1e9
     res = {
         "metric": METRIC,
         "value": w.T / (ms * 1e-3),
@@ -396,27 +509,45 @@ def main():
         "vs_baseline": None,
         "dtype": w.dtype,
         "data": "synthetic",
-        "hip_graph": bool(args.graph),
+        "hip_graph": False,
         "config": {"workload": w.name, "T": w.T, "d": w.d, "E": w.E, "k": w.k,
                    "d_ff": w.d_ff, "act": w.act, "gating": w.gating,
                    "capacity_factor": w.capacity_factor, "num_shared": w.num_shared,
                    "d_ff_shared": w.d_ff_shared, "parallelism": "none (1 GPU)"},
-        "active_tflops": tflops,
-        "active_tflops_frac_of_peak": tflops / peak,
-        "algorithmic_gbs": gbs,
-        "algorithmic_gbs_frac_of_hbm": gbs / PEAK_HBM_GBS,
-        "routing": {"kept_rows": work["kept"], "active_experts": work["active"],
-                    "dropped": int(drp.item())},
+        "active_tflops": head["active_tflops"],
+        "active_tflops_frac_of_peak": head["frac_of_peak"],
+        "algorithmic_gbs": head["algorithmic_gbs"],
+        "algorithmic_gbs_frac_of_hbm": head["frac_of_hbm"],
+        "routing": head["routing"],
         "kernels_ms": {k: round(v, 5) for k, v in sorted(kern.items())},
+        "subsystems": head["subsystems"],
         "roofline": roof,
         "next_rows": next_rows,
         "cold": cold,
     }
+    if "hip_graph" in head:
+        res["graph_replay"] = head["hip_graph"]
     if w.dtype == "bf16" and not args.no_backward:
-        next_rows["backward"] = measure_backward(B, w, inp, cfg, kept_counts, args.steps,
+        next_rows["backward"] = measure_backward(B, w, inp, cfg, ctx["kept_counts"], args.steps,
                                                  args.warmup)
+    cpu = None
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(w, inp, work["flops"] / w.T)
+        cpu = cpu_baseline(w, inp, work["flops"] / w.T)
+    del inp, ctx, ws, step, logits
+    torch.cuda.empty_cache()
+    if not args.no_per_config:
+        per = {}
+        for name in PER_CONFIG:
+            if name == w.name:
+                continue
+            r, c = measure_workload(B, WORKLOADS[name], args.steps, args.warmup,
+                                    graph=name in GRAPHED)
+            del c
+            torch.cuda.empty_cache()
+            per[name] = r
+        res["per_config"] = per
+    if cpu is not None:
+        res["cpu_baseline"] = cpu
     print(json.dumps(res), flush=True)
 
 

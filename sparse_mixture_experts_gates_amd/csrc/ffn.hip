@@ -660,6 +660,7 @@ bool ffn_plan_spec(const FfnPassArgs& p1, const FfnPassArgs& p2, PlanSpec* ps) {
   ps->S2 = p2.split > 1 ? p2.split : 1;
   ps->plan = static_cast<int32_t*>(p1.plan);
   ps->plan2 = static_cast<int32_t*>(p2.plan);
+  ps->balanced = 1;
   return true;
 }
 

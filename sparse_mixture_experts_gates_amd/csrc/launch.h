@@ -41,6 +41,9 @@ struct PlanSpec {
   int S2;                   // K parts of the second pass (1 = not split)
   int32_t* plan;
   int32_t* plan2;
+  int balanced;             // 1: a segment's rows split into equal row tiles
+                            // (multiples of 16 rows, at most BM); 0: tiles of
+                            // BM rows and one ragged last tile
 };
 
 struct PermuteArgs {
@@ -62,6 +65,12 @@ struct PermuteArgs {
                             // here when the one-workgroup path runs
 };
 int permute_nblocks(int64_t rows);
+// Small batches (bf16, 1 <= T <= 16, router workspace given, no x_perm): the
+// router's score parts, then one workgroup that adds them, selects the top-k
+// and runs the whole permutation (plans included when pa.plans is set).
+bool route_permute_small_ok(const RouteArgs& ra, const PermuteArgs& pa);
+hipError_t launch_route_permute_small(const RouteArgs& ra, const PermuteArgs& pa, hipStream_t s,
+                                      bool* plans_built);
 // *plans_built (if given) tells whether a.plans were written.
 hipError_t launch_permute(const PermuteArgs& a, hipStream_t s, bool* plans_built = nullptr);
 

@@ -272,19 +272,23 @@ const char* at(const void* base, size_t off) { return static_cast<const char*>(b
 
 moe_status_t hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
 
+RouteArgs route_args(const moe_config_t* c, int64_t T, const void* x, const void* wr,
+                     const float* off, const float* bias, float* logits, int32_t* idx,
+                     float* gate, void* ws) {
+  return RouteArgs{x, wr, off, bias, logits, idx, gate, static_cast<float*>(ws), T, c->d,
+                   c->num_experts, c->top_k, c->gating, c->dtype};
+}
+
 moe_status_t do_route(const moe_config_t* c, int64_t T, const void* x, const void* wr,
                       const float* off, const float* bias, float* logits, int32_t* idx,
                       float* gate, void* ws, hipStream_t s) {
-  RouteArgs a{x, wr, off, bias, logits, idx, gate, static_cast<float*>(ws), T, c->d,
-              c->num_experts, c->top_k, c->gating, c->dtype};
-  return hip_status(launch_route(a, s));
+  return hip_status(launch_route(route_args(c, T, x, wr, off, bias, logits, idx, gate, ws), s));
 }
 
-moe_status_t do_permute(const moe_config_t* c, int64_t T, const int32_t* idx, const void* x,
-                        int32_t* counts, int32_t* offsets, int32_t* perm_src,
-                        int32_t* slot_pos, int32_t* dropped, void* x_perm, void* ws,
-                        hipStream_t s, const PlanSpec* plans = nullptr,
-                        bool* plans_built = nullptr) {
+PermuteArgs permute_args(const moe_config_t* c, int64_t T, const int32_t* idx, const void* x,
+                         int32_t* counts, int32_t* offsets, int32_t* perm_src,
+                         int32_t* slot_pos, int32_t* dropped, void* x_perm, void* ws,
+                         const PlanSpec* plans) {
   const PermWs w = perm_ws(c, T);
   PermuteArgs a;
   a.topk_idx = idx;
@@ -305,6 +309,16 @@ moe_status_t do_permute(const moe_config_t* c, int64_t T, const int32_t* idx, co
   a.capacity = capacity_of(c, T);
   a.slot_major = c->capacity_priority == MOE_PRIORITY_SLOT ? 1 : 0;
   a.plans = plans;
+  return a;
+}
+
+moe_status_t do_permute(const moe_config_t* c, int64_t T, const int32_t* idx, const void* x,
+                        int32_t* counts, int32_t* offsets, int32_t* perm_src,
+                        int32_t* slot_pos, int32_t* dropped, void* x_perm, void* ws,
+                        hipStream_t s, const PlanSpec* plans = nullptr,
+                        bool* plans_built = nullptr) {
+  const PermuteArgs a = permute_args(c, T, idx, x, counts, offsets, perm_src, slot_pos, dropped,
+                                     x_perm, ws, plans);
   return hip_status(launch_permute(a, s, plans_built));
 }
 
@@ -573,9 +587,6 @@ moe_status_t moe_forward(const moe_config_t* cfg, int64_t T, const void* x, cons
   int32_t* slot_pos = reinterpret_cast<int32_t*>(at(workspace, w.slot_pos));
   void* eout = at(workspace, w.eout);
   void* sout = cfg->num_shared > 0 ? at(workspace, w.sout) : nullptr;
-  st = do_route(cfg, T, x, w_router, logit_offset, select_bias, nullptr, idx, gate,
-                route_ws_bytes(T, cfg->num_experts, cfg->dtype) ? at(workspace, w.route) : nullptr, s);
-  if (st != MOE_OK) return st;
   // the permutation also writes the GEMM tile plans when it runs as one
   // workgroup (small batches), which saves the plan kernel's launch
   const FfnPasses passes = ffn_passes(cfg, T, x, nullptr, perm_src, offsets, w1, w3, w2, ws1,
@@ -583,9 +594,22 @@ moe_status_t moe_forward(const moe_config_t* cfg, int64_t T, const void* x, cons
   PlanSpec spec;
   const bool have_spec = ffn_plan_spec(passes.p, passes.p2, &spec);
   bool built = false;
-  st = do_permute(cfg, T, idx, x, counts, offsets, perm_src, slot_pos, dropped, nullptr,
-                  at(workspace, w.perm), s, have_spec ? &spec : nullptr, &built);
-  if (st != MOE_OK) return st;
+  const RouteArgs ra = route_args(cfg, T, x, w_router, logit_offset, select_bias, nullptr, idx,
+                                  gate, route_ws_bytes(T, cfg->num_experts, cfg->dtype)
+                                            ? at(workspace, w.route) : nullptr);
+  const PermuteArgs pa = permute_args(cfg, T, idx, x, counts, offsets, perm_src, slot_pos,
+                                      dropped, nullptr, at(workspace, w.perm),
+                                      have_spec ? &spec : nullptr);
+  if (route_permute_small_ok(ra, pa)) {
+    // decode batches: router and permutation in two launches instead of three
+    st = hip_status(launch_route_permute_small(ra, pa, s, &built));
+    if (st != MOE_OK) return st;
+  } else {
+    st = hip_status(launch_route(ra, s));
+    if (st != MOE_OK) return st;
+    st = hip_status(launch_permute(pa, s, &built));
+    if (st != MOE_OK) return st;
+  }
   st = run_ffn(passes, built, s);
   if (st != MOE_OK) return st;
   if (passes.p2.split > 1)   // the combine adds the second GEMM's K parts
@@ -855,6 +879,7 @@ moe_status_t moe_backward(const moe_config_t* cfg, int64_t T, const void* x, con
     void* plan_h = at(workspace, shared ? bw.splan_h : bw.plan_h);
     void* plan_x = at(workspace, shared ? bw.splan_x : bw.plan_x);
     PlanSpec ps;
+    ps.balanced = 0;   // the backward GEMMs store full row tiles through LDS
     ps.BM = bwd_tile_rows();
     ps.NT = (f + bwd_tile_cols() - 1) / bwd_tile_cols();
     ps.NT2 = (d + bwd_tile_cols() - 1) / bwd_tile_cols();

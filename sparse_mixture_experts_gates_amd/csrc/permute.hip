@@ -18,6 +18,7 @@
 #include "common.h"
 #include "launch.h"
 #include "plan.h"
+#include "permute_fused.h"
 
 namespace moe {
 
@@ -25,14 +26,6 @@ namespace {
 
 constexpr int CH = 1024;  // slots per chunk
 
-// Slots are visited in priority order: the L-th visited slot is slot L
-// (token-major: every slot of token 0, then of token 1, ...), or with
-// slot-major priority (tslot = T) token L % T's choice L / T, so every
-// token's first choice comes before any second choice.  Ranks, capacity and
-// the row order inside each expert follow this order.
-__device__ __forceinline__ int slot_of(int L, int tslot, int k) {
-  return tslot ? (L % tslot) * k + L / tslot : L;
-}
 
 __global__ __launch_bounds__(256) void permute_count_kernel(
     const int32_t* __restrict__ idx, int64_t n, int E, int32_t* __restrict__ bc, int tslot,
@@ -152,129 +145,14 @@ __global__ __launch_bounds__(64) void permute_scatter_kernel(
   }
 }
 
-// All of the above in one workgroup of 16 waves, for up to FUSED_MAX slots:
-// wave w owns a contiguous run of the slots; pass 1 counts its run per expert
-// (ballot groups, no atomics), the per-expert prefix over waves gives each
-// wave's starting ranks and the counts, capacity and offsets, and pass 2
-// re-walks the run to place every slot.  Same results as the three kernels.
-constexpr int FUSED_MAX = 8192;
-constexpr int FUSED_WAVES = 16;
-constexpr int FUSED_IT = FUSED_MAX / (FUSED_WAVES * 64);   // 64-slot groups per wave, at most
-
-__device__ __forceinline__ uint64_t expert_peers(int e, bool valid) {
-  uint64_t peers = __ballot(valid);
-#pragma unroll
-  for (int b = 0; b < 8; ++b) {
-    const bool bit = (e >> b) & 1;
-    const uint64_t bb = __ballot(bit);
-    peers &= bit ? bb : ~bb;
-  }
-  return peers;
-}
-
+// The whole permutation in one workgroup (see permute_fused.h).
 __global__ __launch_bounds__(1024) void permute_fused_kernel(
     const int32_t* __restrict__ idx, int n, int E, int64_t cap, int32_t* __restrict__ counts,
     int32_t* __restrict__ offsets, int32_t* __restrict__ perm_src,
     int32_t* __restrict__ slot_pos, int32_t* __restrict__ num_dropped,
     int32_t* __restrict__ kept_total, PlanSpec ps, int want_plans, int tslot, int k) {
-  __shared__ int run[FUSED_WAVES][256];
-  __shared__ int sk[256];
-  __shared__ int sdrop[256];
-  __shared__ int soff[256];
-  __shared__ int prows[256];
-  __shared__ int pmt[256];
-  __shared__ int pbase[257];
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int per = ((n + FUSED_WAVES * 64 - 1) / (FUSED_WAVES * 64)) * 64;  // slots per wave
-  const int lo = w * per;
-  const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  for (int e = lane; e < 256; e += 64) run[w][e] = 0;
-  // every expert id of this wave's run in flight at once, kept for both passes
-  int ev[FUSED_IT];
-#pragma unroll
-  for (int i = 0; i < FUSED_IT; ++i) {
-    const int a = lo + i * 64 + lane;
-    ev[i] = (i * 64 < per && a < n) ? idx[slot_of(a, tslot, k)] : -1;
-  }
-  __syncthreads();
-  // pass 1: per-wave counts
-#pragma unroll
-  for (int i = 0; i < FUSED_IT; ++i) {
-    if (i * 64 >= per) break;
-    const int a = lo + i * 64 + lane;
-    const int e = ev[i];
-    const bool valid = a < n && e >= 0 && e < E;
-    const uint64_t peers = expert_peers(e, valid);
-    if (valid && (peers & lt) == 0) run[w][e] += __popcll(peers);
-  }
-  __syncthreads();
-  // per expert: exclusive prefix over waves, counts, capacity
-  if (tid < 256) {
-    const int e = tid;
-    int tot = 0;
-    for (int v = 0; v < FUSED_WAVES; ++v) {
-      const int c = run[v][e];
-      run[v][e] = tot;
-      tot += c;
-    }
-    const int kept = e < E ? (cap < 0 ? tot : (int)(tot < cap ? tot : cap)) : 0;
-    sk[e] = kept;
-    sdrop[e] = e < E ? tot - kept : 0;
-    if (e < E && counts) counts[e] = tot;
-  }
-  __syncthreads();
-  for (int off = 1; off < 256; off <<= 1) {
-    int v = 0, u = 0;
-    if (tid < 256 && tid >= off) {
-      v = sk[tid - off];
-      u = sdrop[tid - off];
-    }
-    __syncthreads();
-    if (tid < 256) {
-      sk[tid] += v;
-      sdrop[tid] += u;
-    }
-    __syncthreads();
-  }
-  if (tid < 256) soff[tid] = tid == 0 ? 0 : sk[tid - 1];
-  if (tid < E) offsets[tid + 1] = sk[tid];
-  if (tid == 0) {
-    offsets[0] = 0;
-    if (num_dropped) num_dropped[0] = sdrop[255];
-    kept_total[0] = sk[255];
-  }
-  __syncthreads();
-  if (want_plans) {
-    // the expert FFN's tile plans from the kept counts just formed
-    if (tid < E) prows[tid] = sk[tid] - soff[tid];
-    __syncthreads();
-    build_tile_plans(soff, prows, E, ps, pmt, pbase);
-  }
-  const int total = sk[255];
-  // pass 2: place every slot of this wave's run
-#pragma unroll
-  for (int i = 0; i < FUSED_IT; ++i) {
-    if (i * 64 >= per) break;
-    const int a = lo + i * 64 + lane;
-    const int sa = a < n ? slot_of(a, tslot, k) : 0;   // physical slot
-    const int e = ev[i];
-    const bool valid = a < n && e >= 0 && e < E;
-    const uint64_t peers = expert_peers(e, valid);
-    int r = 0;
-    if (valid) r = run[w][e] + __popcll(peers & lt);
-    __builtin_amdgcn_wave_barrier();
-    if (valid && (peers & lt) == 0) run[w][e] += __popcll(peers);
-    if (a < n) {
-      if (valid && (cap < 0 || r < cap)) {
-        const int p = soff[e] + r;
-        slot_pos[sa] = p;
-        perm_src[p] = sa;
-      } else {
-        slot_pos[sa] = -1;
-      }
-      if (a >= total) perm_src[a] = -1;   // rows past the kept ones
-    }
-  }
+  permute_one_workgroup(idx, n, E, cap, counts, offsets, perm_src, slot_pos, num_dropped,
+                        kept_total, ps, want_plans, tslot, k);
 }
 
 // x_perm[p] = x[perm_src[p] / k] for p < kept_total; one wave per row.
@@ -301,7 +179,7 @@ hipError_t launch_permute(const PermuteArgs& a, hipStream_t s, bool* plans_built
   if (n == 0) return hipSuccess;
   if (n <= FUSED_MAX) {
     const int64_t prof_rec = prof_before("permute", s);
-    const PlanSpec none{0, 0, 0, 1, nullptr, nullptr};
+    const PlanSpec none{0, 0, 0, 1, nullptr, nullptr, 0};
     permute_fused_kernel<<<1, 1024, 0, s>>>(a.topk_idx, (int)n, a.E, a.capacity, a.counts,
                                             a.offsets, a.perm_src, a.slot_pos, a.num_dropped,
                                             a.kept_total, a.plans ? *a.plans : none,

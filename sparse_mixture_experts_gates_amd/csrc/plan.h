@@ -21,25 +21,57 @@ struct PlanEntry {
 
 constexpr int kPlanHeader = 128, kPlanHeads = 4;
 
+// Row tile height of a segment of `rows` rows: BM, or with balanced tiles
+// the rows split evenly over ceil(rows / BM) tiles and rounded up to 16.
+// Equal tiles take equal time, so the workgroups that share a weight slab
+// stay in step and find it in L2 (a short ragged last tile would finish
+// early and desynchronise its XCD).
+__device__ __forceinline__ int row_tile_height(int rows, int BM, int balanced) {
+  if (!balanced || rows <= BM) return BM;
+  const int m = (rows + BM - 1) / BM;
+  const int h = ((rows + m - 1) / m + 15) & ~15;
+  return h < BM ? h : BM;
+}
+
 // Writes the plans of ps (one or two passes over the same row tiling) for G
 // segments whose rows are [start[g], start[g] + rows[g]).  Every thread of the
-// (1-D) workgroup must call it; mt[G] and base[G + 1] are LDS scratch.
+// (1-D) workgroup must call it (G <= 1024, G < 2 * blockDim.x); mt[G] and
+// base[G + 1] are LDS scratch.
 __device__ inline void build_tile_plans(const int* start, const int* rows, int G,
                                         const PlanSpec& ps, int* mt, int* base) {
+  constexpr int kTab = 2048;        // row tiles the lookup table holds
+  __shared__ int hs[1024];          // row tile height per segment
+  __shared__ int rt_tab[kTab];      // row tile -> segment | (index in it << 10)
   const int tid = threadIdx.x, nthr = blockDim.x;
   const int BM = ps.BM;
-  for (int g = tid; g < G; g += nthr) mt[g] = (rows[g] + BM - 1) / BM;
-  __syncthreads();
-  if (tid == 0) {
-    int acc = 0;
-    for (int g = 0; g < G; ++g) {
-      base[g] = acc;
-      acc += mt[g];
-    }
-    base[G] = acc;
+  for (int g = tid; g < G; g += nthr) {
+    const int h = row_tile_height(rows[g], BM, ps.balanced);
+    hs[g] = h;
+    mt[g] = (rows[g] + h - 1) / h;
   }
+  __syncthreads();   // base[g] below reads mt[g - 1], written by another thread
+  // base = exclusive scan of mt (base[G] = all row tiles): an inclusive
+  // Hillis-Steele scan of [0, mt[0], .., mt[G-1]], two entries per thread
+  // (G < 2 * blockDim.x; a serial loop here cost microseconds at G = 128+)
+  for (int g = tid; g <= G; g += nthr) base[g] = g == 0 ? 0 : mt[g - 1];
   __syncthreads();
+  for (int off = 1; off <= G; off <<= 1) {
+    const int g0 = tid, g1 = tid + nthr;
+    const int v0 = (g0 <= G && g0 >= off) ? base[g0 - off] : 0;
+    const int v1 = (g1 <= G && g1 >= off) ? base[g1 - off] : 0;
+    __syncthreads();
+    if (g0 <= G) base[g0] += v0;
+    if (g1 <= G) base[g1] += v1;
+    __syncthreads();
+  }
   const int MT = base[G];   // row tiles over all segments
+  // row tile -> (segment, index): each entry then costs two LDS reads
+  // instead of a binary search over the segments
+  const bool tab = MT <= kTab;
+  if (tab)
+    for (int g = tid; g < G; g += nthr)
+      for (int mi = 0; mi < mt[g]; ++mi) rt_tab[base[g] + mi] = g | (mi << 10);
+  __syncthreads();
   for (int pass = 0; pass < 2; ++pass) {
     // a split pass (K in S parts) lists every row tile once per part:
     // segment, column tile, part, row tile
@@ -49,6 +81,22 @@ __device__ inline void build_tile_plans(const int* start, const int* rows, int G
     if (nt_all <= 0) break;
     PlanEntry* out = reinterpret_cast<PlanEntry*>(reinterpret_cast<char*>(count) + kPlanHeader);
     const int V = MT * nt_all;
+    if (tab) {
+      // q enumerates (row tile, column entry); L is its place in the order
+      // segment, column tile, part, row tile
+      for (int q = tid; q < V; q += nthr) {
+        const int rt = q / nt_all, c = q - rt * nt_all;
+        const int v = rt_tab[rt];
+        const int g = v & 1023, mi = v >> 10;
+        const int L = base[g] * nt_all + c * mt[g] + mi;
+        const int nt = S == 1 ? c : c / S, part = c - nt * S;
+        const int h = hs[g];
+        const int m0 = start[g] + mi * h;
+        int m1 = m0 + h;
+        if (m1 > start[g] + rows[g]) m1 = start[g] + rows[g];
+        out[L] = PlanEntry{g, m0, m1, nt | (part << 24)};
+      }
+    } else
     for (int L = tid; L < V; L += nthr) {
       int lo = 0, hi = G - 1;  // last g with base[g] * nt_all <= L
       while (lo < hi) {
@@ -58,8 +106,9 @@ __device__ inline void build_tile_plans(const int* start, const int* rows, int G
       const int g = lo, rem = L - base[g] * nt_all, m = mt[g];
       const int c = rem / m, mi = rem - c * m;
       const int nt = c / S, part = c - nt * S;
-      const int m0 = start[g] + mi * BM;
-      int m1 = m0 + BM;
+      const int h = hs[g];
+      const int m0 = start[g] + mi * h;
+      int m1 = m0 + h;
       if (m1 > start[g] + rows[g]) m1 = start[g] + rows[g];
       out[L] = PlanEntry{g, m0, m1, nt | (part << 24)};
     }

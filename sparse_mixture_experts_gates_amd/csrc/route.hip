@@ -18,6 +18,7 @@
 // the scores, and a second kernel selects from them.
 #include "common.h"
 #include "launch.h"
+#include "permute_fused.h"
 
 namespace moe {
 
@@ -399,8 +400,10 @@ __global__ __launch_bounds__(RS_THREADS) void route_small_kernel(RouteArgs a) {
 constexpr int RP_MAX_SPLIT = 64;
 
 template <int EP>
-__global__ __launch_bounds__(256) void route_partial_kernel(RouteArgs a, int nsplit) {
+__global__ __launch_bounds__(256) void route_partial_kernel(RouteArgs a, int nsplit,
+                                                            int* done = nullptr) {
   __shared__ float red[16 * 17];
+  if (done && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) *done = 0;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int et = blockIdx.x, ks = blockIdx.y;
@@ -443,14 +446,15 @@ __global__ __launch_bounds__(256) void route_partial_kernel(RouteArgs a, int nsp
 // over T workgroups.  Block b adds the parts of token b in order and runs
 // the top-k for it alone (the other rows of the score tile are masked by
 // passing T = b + 1).
+// Every thread of the workgroup calls it (it holds a barrier); the first 256
+// do the work.
 template <int EP>
-__global__ __launch_bounds__(256) void route_reduce_topk_kernel(RouteArgs a, int nsplit) {
+__device__ void route_reduce_topk_body(const RouteArgs& a, int nsplit, int b) {
   constexpr int TPW = EP <= 16 ? 4 : (EP <= 32 ? 2 : 1);   // as in topk_from_lds
   constexpr int BT = 4 * TPW, LD = EP + 4;
   __shared__ float lg[BT * LD];
   const int tid = threadIdx.x, E = a.E;
-  const int b = blockIdx.x;
-  for (int e = tid; e < EP; e += 256) {
+  for (int e = tid; e < EP && tid < 256; e += 256) {
     float p[16];
     float v = 0.f;
     for (int ks0 = 0; ks0 < nsplit; ks0 += 16) {
@@ -463,11 +467,62 @@ __global__ __launch_bounds__(256) void route_reduce_topk_kernel(RouteArgs a, int
     lg[e] = v + ((a.offset && e < E) ? a.offset[e] : 0.f);
   }
   __syncthreads();
+  if (tid >= 256) return;
   if (a.logits)
     for (int e = tid; e < E; e += 256) a.logits[(int64_t)b * E + e] = lg[e];
   RouteArgs one = a;
   one.T = b + 1;
   topk_from_lds<EP, BT>(lg, LD, one, b);
+}
+
+template <int EP>
+__global__ __launch_bounds__(256) void route_reduce_topk_kernel(RouteArgs a, int nsplit) {
+  route_reduce_topk_body<EP>(a, nsplit, blockIdx.x);
+}
+
+// Small batches in moe_forward: route_reduce_topk_kernel's per-token
+// workgroups (1024 threads, the first 256 of them as there), and the last
+// of them to finish runs the whole permutation (with the GEMM plans), which
+// saves the permutation's own launch on a decode step.  A workgroup counts
+// itself done with an agent-scope acquire-release increment after its
+// indices are written; route_partial_kernel zeroes the counter before.
+// Scores, indices and gates are those of the two-kernel route.
+struct RoutePermuteArgs {
+  RouteArgs r;
+  int nsplit;
+  int* done;               // workspace counter, zeroed by the score kernel
+  int64_t capacity;
+  int32_t* counts;
+  int32_t* offsets;
+  int32_t* perm_src;
+  int32_t* slot_pos;
+  int32_t* num_dropped;
+  int32_t* kept_total;
+  PlanSpec ps;
+  int want_plans, tslot;
+};
+
+template <int EP>
+__global__ __launch_bounds__(1024) void route_reduce_permute_kernel(RoutePermuteArgs p) {
+  __shared__ int last;
+  const int tid = threadIdx.x;
+  route_reduce_topk_body<EP>(p.r, p.nsplit, blockIdx.x);   // all threads: it has a barrier
+  __syncthreads();   // this token's indices are written (and acknowledged)
+  if (tid == 0)
+    last = __hip_atomic_fetch_add(p.done, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT) ==
+           (int)p.r.T - 1;
+  __syncthreads();
+  if (!last) return;
+  const RouteArgs& a = p.r;
+  permute_one_workgroup(a.topk_idx, (int)a.T * a.k, a.E, p.capacity, p.counts, p.offsets,
+                        p.perm_src, p.slot_pos, p.num_dropped, p.kept_total, p.ps, p.want_plans,
+                        p.tslot, a.k);
+}
+
+template <int EP>
+void launch_rp(const RoutePermuteArgs& p, hipStream_t s) {
+  route_partial_kernel<EP><<<dim3(EP / 16, p.nsplit), 256, 0, s>>>(p.r, p.nsplit, p.done);
+  route_reduce_permute_kernel<EP><<<(unsigned)p.r.T, 1024, 0, s>>>(p);
 }
 
 int route_split(int d, int E) {
@@ -573,11 +628,15 @@ hipError_t launch_ep(const RouteArgs& a, hipStream_t s) {
 
 }  // namespace
 
+static int padded_experts(int E) {
+  return E <= 16 ? 16 : E <= 32 ? 32 : E <= 64 ? 64 : E <= 128 ? 128 : 256;
+}
+
 size_t route_ws_bytes(int64_t T, int E, int dtype) {
   if (dtype != MOE_BF16) return 0;
   if (T > 16) return E > RT_SPLIT_MIN / 2 ? (size_t)T * E * 4 : 0;   // scores of the split pass
-  const int ep = E <= 16 ? 16 : E <= 32 ? 32 : E <= 64 ? 64 : E <= 128 ? 128 : 256;
-  return (size_t)RP_MAX_SPLIT * 16 * ep * 4;
+  // the score parts, then the done-counter of the fused small-batch path
+  return (size_t)RP_MAX_SPLIT * 16 * padded_experts(E) * 4 + 256;
 }
 
 hipError_t launch_route(const RouteArgs& a, hipStream_t s) {
@@ -592,6 +651,40 @@ hipError_t launch_route(const RouteArgs& a, hipStream_t s) {
   if (a.E <= 64) return launch_ep<64, 32, 4>(a, s);
   if (a.E <= 128) return launch_ep<128, 64, 4>(a, s);
   return launch_ep<256, 64, 3>(a, s);
+}
+
+bool route_permute_small_ok(const RouteArgs& ra, const PermuteArgs& pa) {
+  return ra.dtype == MOE_BF16 && ra.T >= 1 && ra.T <= 16 && ra.partial && pa.x_perm == nullptr &&
+         ra.T * ra.k <= FUSED_MAX;
+}
+
+hipError_t launch_route_permute_small(const RouteArgs& ra, const PermuteArgs& pa, hipStream_t s,
+                                      bool* plans_built) {
+  if (plans_built) *plans_built = false;
+  if (!route_permute_small_ok(ra, pa)) return hipErrorInvalidValue;
+  RoutePermuteArgs p;
+  p.r = ra;
+  p.nsplit = route_split(ra.d, ra.E);
+  p.done = reinterpret_cast<int*>(ra.partial + (size_t)RP_MAX_SPLIT * 16 * padded_experts(ra.E));
+  p.capacity = pa.capacity;
+  p.counts = pa.counts;
+  p.offsets = pa.offsets;
+  p.perm_src = pa.perm_src;
+  p.slot_pos = pa.slot_pos;
+  p.num_dropped = pa.num_dropped;
+  p.kept_total = pa.kept_total;
+  p.ps = pa.plans ? *pa.plans : PlanSpec{0, 0, 0, 1, nullptr, nullptr, 0};
+  p.want_plans = pa.plans ? 1 : 0;
+  p.tslot = pa.slot_major && pa.k > 1 ? (int)pa.T : 0;
+  const int64_t prof_rec = prof_before("route_permute", s);
+  if (ra.E <= 16) launch_rp<16>(p, s);
+  else if (ra.E <= 32) launch_rp<32>(p, s);
+  else if (ra.E <= 64) launch_rp<64>(p, s);
+  else if (ra.E <= 128) launch_rp<128>(p, s);
+  else launch_rp<256>(p, s);
+  prof_after(prof_rec, s);
+  if (plans_built && pa.plans) *plans_built = true;
+  return hipGetLastError();
 }
 
 }  // namespace moe

@@ -74,6 +74,11 @@ WORKLOADS = {
     "switch_bf16": Workload("switch_bf16", T=8192, d=768, E=8, k=1, d_ff=3072,
                             act="relu", capacity_factor=1.25,
                             offset=("normal", 0.5)),
+    # the Switch layer with the variant gate p_i (the selected expert's
+    # probability under a softmax over all E scores) instead of 1.0
+    "switch_softmax_full_bf16": Workload("switch_softmax_full_bf16", T=8192, d=768, E=8, k=1,
+                                         d_ff=3072, act="relu", gating="softmax_full",
+                                         capacity_factor=1.25, offset=("normal", 0.5)),
     "mixtral_bf16": Workload("mixtral_bf16", T=4096, d=4096, E=8, k=2,
                              d_ff=14336, act="swiglu"),
     "deepseek_v3_bf16": Workload("deepseek_v3_bf16", T=8192, d=7168, E=256,

@@ -53,7 +53,8 @@ def test_small_workload_all_tokens(name):
     say(f"[parity] {name} ok {json.dumps(rep)}")
 
 
-FULL_SAMPLE = {"toy_fp32": None, "switch_bf16": 96, "mixtral_bf16": 48,
+FULL_SAMPLE = {"toy_fp32": None, "switch_bf16": 96, "switch_softmax_full_bf16": 96,
+               "mixtral_bf16": 48,
                "deepseek_v3_bf16": 12, "gptoss_prefill_bf16": 48, "gptoss_decode_bf16": None}
 
 
