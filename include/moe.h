@@ -236,10 +236,17 @@ moe_status_t moe_combine(const moe_config_t* cfg, int64_t T,
                          const float* topk_gate, const void* shared_out,
                          void* y, void* stream);
 
-/* The whole layer: moe_route, moe_permute, moe_expert_ffn, moe_combine.
+/* The whole layer, y = sum_{i in S} g_i Expert_i(x) (+ shared experts), as
+ * the equation block of "Mixture of experts" (Inside the Model guide ch. 14,
+ * "The computation") states it and the numpy forward pass of "Mixture of
+ * Experts" (LLM tutorial ch. 11, "The mathematics") computes it token by
+ * token: moe_route, moe_permute, moe_expert_ffn, moe_combine on one stream,
+ * with the row gather folded into the first expert GEMM's loads and, for
+ * T <= 16, the routing and the permutation in two launches.
  *   y [T, d] dtype out.  topk_idx [T,k], topk_gate [T,k], expert_counts [E]
  *   and num_dropped [1] are optional outputs (NULL = keep them in the
- *   workspace).  The other arguments are as above. */
+ *   workspace).  The other arguments are as above; y's bits are those of the
+ *   stepwise calls. */
 moe_status_t moe_forward(const moe_config_t* cfg, int64_t T, const void* x,
                          const void* w_router, const float* logit_offset,
                          const float* select_bias, const void* w1,
