@@ -256,6 +256,32 @@ moe_status_t moe_forward(const moe_config_t* cfg, int64_t T, const void* x,
                          int32_t* expert_counts, int32_t* num_dropped,
                          void* workspace, size_t ws_bytes, void* stream);
 
+/* moe_forward without a workspace argument, for callers that cannot
+ * allocate: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation.  The layer's scratch memory (tile plans and queue
+ * words, router parts, the first GEMM's hidden activations, the expert
+ * outputs) is a device array of MOE_NOALLOC_SCRATCH_BYTES that the library
+ * holds on each GPU it runs on until the process ends.  Arguments, results
+ * and bits are those of moe_forward (which this call shares every kernel
+ * with); nothing is allocated (keep moe_profile_enable off: the event
+ * profiler creates events).
+ *   Limit: T such that moe_workspace_size(cfg, T) <= MOE_NOALLOC_SCRATCH_BYTES
+ *   (256 MiB: a Mixtral-shape layer, d = 4096, d_ff = 14336, top-2, up to
+ *   3638 tokens; a DeepSeek-V3-shape layer up to 1604; any decode batch);
+ *   beyond it the call returns MOE_ERR_WORKSPACE before touching the GPU.
+ *   Every call on one GPU uses that GPU's one array: calls that overlap on a
+ *   GPU (two streams, two host threads) race and must be serialised by the
+ *   caller.  Nothing in the array needs to start at zero. */
+#define MOE_NOALLOC_SCRATCH_BYTES ((size_t)256 << 20)
+moe_status_t moe_forward_noalloc(const moe_config_t* cfg, int64_t T, const void* x,
+                                 const void* w_router, const float* logit_offset,
+                                 const float* select_bias, const void* w1,
+                                 const void* w3, const void* w2, const void* ws1,
+                                 const void* ws3, const void* ws2, void* y,
+                                 int32_t* topk_idx, float* topk_gate,
+                                 int32_t* expert_counts, int32_t* num_dropped,
+                                 void* stream);
+
 /* Routing statistics of one batch: the balance signals a routing pass yields
  * (sources: "Mixture of experts", Inside the Model guide ch. 14, sections
  * "Auxiliary loss" (balance-loss equation) and "Auxiliary-loss-free

@@ -30,7 +30,7 @@ EXPORTS = ("moe_status_str", "moe_check_config", "moe_workspace_size", "moe_capa
            "moe_route", "moe_permute", "moe_expert_ffn", "moe_combine", "moe_forward",
            "moe_routing_stats", "moe_profile_enable", "moe_profile_read",
            "moe_train_workspace_size", "moe_forward_train", "moe_saved_routing",
-           "moe_backward_workspace_size", "moe_backward")
+           "moe_backward_workspace_size", "moe_backward", "moe_forward_noalloc")
 
 
 class MoeError(RuntimeError):
@@ -72,6 +72,7 @@ def lib():
         L.moe_expert_ffn.argtypes = [_cfgp, _i64] + [_vp] * 12 + [_sz, _vp]
         L.moe_combine.argtypes = [_cfgp, _i64] + [_vp] * 5 + [_vp]
         L.moe_forward.argtypes = [_cfgp, _i64] + [_vp] * 16 + [_sz, _vp]
+        L.moe_forward_noalloc.argtypes = [_cfgp, _i64] + [_vp] * 15 + [_vp]
         L.moe_routing_stats.argtypes = ([_cfgp, _i64] + [_vp] * 4 + [ctypes.c_float] * 2
                                         + [_vp] * 6 + [_sz, _vp])
         L.moe_train_workspace_size.argtypes = [_cfgp, _i64, ctypes.POINTER(_sz)]
@@ -87,6 +88,7 @@ def lib():
                                        ctypes.POINTER(ctypes.c_int32), ctypes.c_int32]
         for fn in ("moe_check_config", "moe_workspace_size", "moe_capacity", "moe_route",
                    "moe_permute", "moe_expert_ffn", "moe_combine", "moe_forward",
+                   "moe_forward_noalloc",
                    "moe_routing_stats", "moe_profile_enable", "moe_train_workspace_size",
                    "moe_forward_train", "moe_saved_routing", "moe_backward_workspace_size",
                    "moe_backward"):
@@ -271,6 +273,39 @@ def forward(cfg, x, w_router, w1, w2, w3=None, *, logit_offset=None, select_bias
                              _ptr(counts), _ptr(dropped), _ptr(ws), ws.numel(), _stream()),
            "moe_forward")
     return y, idx, gate, counts, dropped
+
+
+NOALLOC_SCRATCH_BYTES = 256 << 20   # MOE_NOALLOC_SCRATCH_BYTES
+
+
+def forward_noalloc(cfg, x, w_router, w1, w2, w3=None, *, logit_offset=None, select_bias=None,
+                    ws1=None, ws3=None, ws2=None, y=None, outputs=None):
+    """moe_forward_noalloc: the whole layer with the library's own scratch
+    array as its workspace.  ``outputs`` may be a (y, topk_idx, topk_gate,
+    expert_counts, num_dropped) tuple of preallocated tensors; otherwise they
+    are allocated here (in torch, before the call).  Returns that tuple."""
+    T = x.shape[0]
+    dev = x.device
+    dt, d, E = _dt(cfg), cfg.d, cfg.num_experts
+    if outputs is None:
+        outputs = (torch.empty((T, d), dtype=dt, device=dev) if y is None else y,
+                   torch.empty((T, cfg.top_k), dtype=torch.int32, device=dev),
+                   torch.empty((T, cfg.top_k), dtype=torch.float32, device=dev),
+                   torch.empty(E, dtype=torch.int32, device=dev),
+                   torch.empty(1, dtype=torch.int32, device=dev))
+    y, idx, gate, counts, dropped = outputs
+    _check(lib().moe_forward_noalloc(ctypes.byref(cfg), T, _arg(x, "x", T * d, dt),
+                                     _arg(w_router, "w_router", E * d, dt),
+                                     _arg(logit_offset, "logit_offset", E, torch.float32),
+                                     _arg(select_bias, "select_bias", E, torch.float32),
+                                     *_weights(cfg, w1, w3, w2, ws1, ws3, ws2),
+                                     _arg(y, "y", T * d, dt),
+                                     _arg(idx, "topk_idx", T * cfg.top_k, torch.int32),
+                                     _arg(gate, "topk_gate", T * cfg.top_k, torch.float32),
+                                     _arg(counts, "expert_counts", E, torch.int32),
+                                     _arg(dropped, "num_dropped", 1, torch.int32), _stream()),
+           "moe_forward_noalloc")
+    return outputs
 
 
 def forward_inputs(cfg, inp, **kw):

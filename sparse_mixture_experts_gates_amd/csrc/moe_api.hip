@@ -450,6 +450,111 @@ moe_status_t do_combine(const moe_config_t* c, int64_t T, const void* eout,
   return hip_status(launch_combine(a, s));
 }
 
+// ------------------------------------------------- allocation-free forward
+// The workspace of moe_forward_noalloc: one file-scope device array per GPU
+// (the HIP runtime places a copy on each device the library runs on, held
+// until the process ends).  Host code never uses the array's name as an
+// address: it is a host-side stand-in.  The device address comes from
+// hipGetSymbolAddress, once per device with that device current, and is
+// kept per device.  Nothing in it needs to start at zero: every kernel of
+// the forward pass writes what it later reads within the same call (plan
+// queue words and the router's done-counter are reset by the kernels that
+// precede their readers).
+constexpr size_t kScratchBytes = MOE_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_addr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// This device's address of the scratch array, or null on a HIP error.
+void* scratch_ptr() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  void* p = g_scratch_addr[dev].load(std::memory_order_acquire);
+  if (p) return p;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  p = g_scratch_addr[dev].load(std::memory_order_relaxed);
+  if (!p) {
+    void* q = nullptr;
+    if (hipGetSymbolAddress(&q, HIP_SYMBOL(scratch)) != hipSuccess || !q) return nullptr;
+    g_scratch_addr[dev].store(q, std::memory_order_release);
+    p = q;
+  }
+  return p;
+}
+
+// moe_forward, and with use_scratch the allocation-free variant: the
+// workspace is then this device's file-scope scratch array.
+moe_status_t forward_impl(const moe_config_t* cfg, int64_t T, const void* x,
+                          const void* w_router, const float* logit_offset,
+                          const float* select_bias, const void* w1, const void* w3,
+                          const void* w2, const void* ws1, const void* ws3, const void* ws2,
+                          void* y, int32_t* topk_idx, float* topk_gate, int32_t* expert_counts,
+                          int32_t* num_dropped, void* workspace, size_t ws_bytes, void* stream,
+                          bool use_scratch) {
+  moe_status_t st = check_cfg(cfg, T);
+  if (st != MOE_OK) return st;
+  if (T == 0) return MOE_OK;  // nothing to do; token-sized pointers may be null
+  if (!x || !w_router || !w1 || !w2 || !y) return MOE_ERR_INVALID_ARG;
+  if (cfg->act == MOE_ACT_SWIGLU && !w3) return MOE_ERR_INVALID_ARG;
+  if (cfg->num_shared > 0 && (!ws1 || !ws3 || !ws2)) return MOE_ERR_INVALID_ARG;
+  const void* p16[] = {x, w_router, w1, w2, y, w3, ws1, ws3, ws2};
+  for (const void* p : p16)
+    if (p && !al(p, 16)) return MOE_ERR_INVALID_ARG;
+  const void* p4[] = {logit_offset, select_bias, topk_idx, topk_gate, expert_counts, num_dropped};
+  for (const void* p : p4)
+    if (p && !al(p, 4)) return MOE_ERR_INVALID_ARG;
+  const FwdWs w = fwd_ws(cfg, T);
+  if (use_scratch) {
+    // sized before any HIP call: a batch beyond the array is refused
+    if (w.total > kScratchBytes) return MOE_ERR_WORKSPACE;
+    workspace = scratch_ptr();
+    if (!workspace) return MOE_ERR_HIP;
+    ws_bytes = kScratchBytes;
+  }
+  if (!workspace || !al(workspace, ALIGN)) return MOE_ERR_INVALID_ARG;
+  if (ws_bytes < w.total) return MOE_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int32_t* idx = topk_idx ? topk_idx : reinterpret_cast<int32_t*>(at(workspace, w.idx));
+  float* gate = topk_gate ? topk_gate : reinterpret_cast<float*>(at(workspace, w.gate));
+  int32_t* counts = expert_counts ? expert_counts : reinterpret_cast<int32_t*>(at(workspace, w.counts));
+  int32_t* dropped = num_dropped ? num_dropped : reinterpret_cast<int32_t*>(at(workspace, w.dropped));
+  int32_t* offsets = reinterpret_cast<int32_t*>(at(workspace, w.offsets));
+  int32_t* perm_src = reinterpret_cast<int32_t*>(at(workspace, w.perm_src));
+  int32_t* slot_pos = reinterpret_cast<int32_t*>(at(workspace, w.slot_pos));
+  void* eout = at(workspace, w.eout);
+  void* sout = cfg->num_shared > 0 ? at(workspace, w.sout) : nullptr;
+  // the permutation also writes the GEMM tile plans when it runs as one
+  // workgroup (small batches), which saves the plan kernel's launch
+  const FfnPasses passes = ffn_passes(cfg, T, x, nullptr, perm_src, offsets, w1, w3, w2, ws1,
+                                      ws3, ws2, eout, sout, at(workspace, w.ffn));
+  PlanSpec spec;
+  const bool have_spec = ffn_plan_spec(passes.p, passes.p2, &spec);
+  bool built = false;
+  const RouteArgs ra = route_args(cfg, T, x, w_router, logit_offset, select_bias, nullptr, idx,
+                                  gate, route_ws_bytes(T, cfg->num_experts, cfg->dtype)
+                                            ? at(workspace, w.route) : nullptr);
+  const PermuteArgs pa = permute_args(cfg, T, idx, x, counts, offsets, perm_src, slot_pos,
+                                      dropped, nullptr, at(workspace, w.perm),
+                                      have_spec ? &spec : nullptr);
+  if (route_permute_small_ok(ra, pa)) {
+    // decode batches: router and permutation in two launches instead of three
+    st = hip_status(launch_route_permute_small(ra, pa, s, &built));
+    if (st != MOE_OK) return st;
+  } else {
+    st = hip_status(launch_route(ra, s));
+    if (st != MOE_OK) return st;
+    st = hip_status(launch_permute(pa, s, &built));
+    if (st != MOE_OK) return st;
+  }
+  st = run_ffn(passes, built, s);
+  if (st != MOE_OK) return st;
+  if (passes.p2.split > 1)   // the combine adds the second GEMM's K parts
+    return do_combine(cfg, T, eout, slot_pos, gate, sout, y, s, passes.p2.part,
+                      passes.p2.max_rows * (int64_t)passes.p2.N);
+  return do_combine(cfg, T, eout, slot_pos, gate, sout, y, s);
+}
+
 }  // namespace
 
 extern "C" {
@@ -459,7 +564,9 @@ const char* moe_status_str(moe_status_t st) {
     case MOE_OK: return "MOE_OK";
     case MOE_ERR_INVALID_ARG: return "MOE_ERR_INVALID_ARG: invalid argument";
     case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED: configuration not supported";
-    case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE: workspace too small";
+    case MOE_ERR_WORKSPACE:
+      return "MOE_ERR_WORKSPACE: workspace too small (or, for moe_forward_noalloc, the batch's "
+             "workspace exceeds MOE_NOALLOC_SCRATCH_BYTES)";
     case MOE_ERR_HIP: return "MOE_ERR_HIP: HIP runtime or launch error";
   }
   return "unknown moe_status_t";
@@ -562,60 +669,20 @@ moe_status_t moe_forward(const moe_config_t* cfg, int64_t T, const void* x, cons
                          const void* ws2, void* y, int32_t* topk_idx, float* topk_gate,
                          int32_t* expert_counts, int32_t* num_dropped, void* workspace,
                          size_t ws_bytes, void* stream) {
-  moe_status_t st = check_cfg(cfg, T);
-  if (st != MOE_OK) return st;
-  if (T == 0) return MOE_OK;  // nothing to do; token-sized pointers may be null
-  if (!x || !w_router || !w1 || !w2 || !y) return MOE_ERR_INVALID_ARG;
-  if (cfg->act == MOE_ACT_SWIGLU && !w3) return MOE_ERR_INVALID_ARG;
-  if (cfg->num_shared > 0 && (!ws1 || !ws3 || !ws2)) return MOE_ERR_INVALID_ARG;
-  const void* p16[] = {x, w_router, w1, w2, y, w3, ws1, ws3, ws2};
-  for (const void* p : p16)
-    if (p && !al(p, 16)) return MOE_ERR_INVALID_ARG;
-  const void* p4[] = {logit_offset, select_bias, topk_idx, topk_gate, expert_counts, num_dropped};
-  for (const void* p : p4)
-    if (p && !al(p, 4)) return MOE_ERR_INVALID_ARG;
-  if (!workspace || !al(workspace, ALIGN)) return MOE_ERR_INVALID_ARG;
-  const FwdWs w = fwd_ws(cfg, T);
-  if (ws_bytes < w.total) return MOE_ERR_WORKSPACE;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  int32_t* idx = topk_idx ? topk_idx : reinterpret_cast<int32_t*>(at(workspace, w.idx));
-  float* gate = topk_gate ? topk_gate : reinterpret_cast<float*>(at(workspace, w.gate));
-  int32_t* counts = expert_counts ? expert_counts : reinterpret_cast<int32_t*>(at(workspace, w.counts));
-  int32_t* dropped = num_dropped ? num_dropped : reinterpret_cast<int32_t*>(at(workspace, w.dropped));
-  int32_t* offsets = reinterpret_cast<int32_t*>(at(workspace, w.offsets));
-  int32_t* perm_src = reinterpret_cast<int32_t*>(at(workspace, w.perm_src));
-  int32_t* slot_pos = reinterpret_cast<int32_t*>(at(workspace, w.slot_pos));
-  void* eout = at(workspace, w.eout);
-  void* sout = cfg->num_shared > 0 ? at(workspace, w.sout) : nullptr;
-  // the permutation also writes the GEMM tile plans when it runs as one
-  // workgroup (small batches), which saves the plan kernel's launch
-  const FfnPasses passes = ffn_passes(cfg, T, x, nullptr, perm_src, offsets, w1, w3, w2, ws1,
-                                      ws3, ws2, eout, sout, at(workspace, w.ffn));
-  PlanSpec spec;
-  const bool have_spec = ffn_plan_spec(passes.p, passes.p2, &spec);
-  bool built = false;
-  const RouteArgs ra = route_args(cfg, T, x, w_router, logit_offset, select_bias, nullptr, idx,
-                                  gate, route_ws_bytes(T, cfg->num_experts, cfg->dtype)
-                                            ? at(workspace, w.route) : nullptr);
-  const PermuteArgs pa = permute_args(cfg, T, idx, x, counts, offsets, perm_src, slot_pos,
-                                      dropped, nullptr, at(workspace, w.perm),
-                                      have_spec ? &spec : nullptr);
-  if (route_permute_small_ok(ra, pa)) {
-    // decode batches: router and permutation in two launches instead of three
-    st = hip_status(launch_route_permute_small(ra, pa, s, &built));
-    if (st != MOE_OK) return st;
-  } else {
-    st = hip_status(launch_route(ra, s));
-    if (st != MOE_OK) return st;
-    st = hip_status(launch_permute(pa, s, &built));
-    if (st != MOE_OK) return st;
-  }
-  st = run_ffn(passes, built, s);
-  if (st != MOE_OK) return st;
-  if (passes.p2.split > 1)   // the combine adds the second GEMM's K parts
-    return do_combine(cfg, T, eout, slot_pos, gate, sout, y, s, passes.p2.part,
-                      passes.p2.max_rows * (int64_t)passes.p2.N);
-  return do_combine(cfg, T, eout, slot_pos, gate, sout, y, s);
+  return forward_impl(cfg, T, x, w_router, logit_offset, select_bias, w1, w3, w2, ws1, ws3, ws2,
+                      y, topk_idx, topk_gate, expert_counts, num_dropped, workspace, ws_bytes,
+                      stream, false);
+}
+
+moe_status_t moe_forward_noalloc(const moe_config_t* cfg, int64_t T, const void* x,
+                                 const void* w_router, const float* logit_offset,
+                                 const float* select_bias, const void* w1, const void* w3,
+                                 const void* w2, const void* ws1, const void* ws3,
+                                 const void* ws2, void* y, int32_t* topk_idx, float* topk_gate,
+                                 int32_t* expert_counts, int32_t* num_dropped, void* stream) {
+  return forward_impl(cfg, T, x, w_router, logit_offset, select_bias, w1, w3, w2, ws1, ws3, ws2,
+                      y, topk_idx, topk_gate, expert_counts, num_dropped, nullptr, 0, stream,
+                      true);
 }
 
 moe_status_t moe_profile_enable(int32_t on) {

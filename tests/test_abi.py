@@ -219,3 +219,17 @@ def test_training_sizes_and_saved_views_on_host():
     for (o, s_), (o2, _) in zip(spans, spans[1:]):
         assert 0 <= o and o + s_ <= o2          # disjoint, inside the buffer
     assert spans[-1][0] + spans[-1][1] <= tr
+
+
+def test_noalloc_refuses_a_batch_beyond_its_scratch_before_touching_the_gpu():
+    """moe_forward_noalloc sizes the batch's workspace on the host first: a
+    Mixtral-shape batch of 4096 tokens needs more than the 256 MiB scratch
+    array and is refused with MOE_ERR_WORKSPACE (no pointer is dereferenced
+    and no HIP call is made, so this runs without a GPU)."""
+    c = B.config(4096, 8, 2, 14336, "swiglu")
+    assert B.workspace_size(c, 4096) > B.NOALLOC_SCRATCH_BYTES
+    assert B.workspace_size(c, 3638) <= B.NOALLOC_SCRATCH_BYTES
+    p = ctypes.c_void_p(1 << 20)          # aligned stand-ins, never read
+    st = B.lib().moe_forward_noalloc(ctypes.byref(c), 4096, p, p, None, None, p, p, p,
+                                     None, None, None, p, None, None, None, None, None)
+    assert st == 3
