@@ -142,15 +142,65 @@ def check_outputs(w, inp, g, tokens=None):
     return float(rel.max())
 
 
-def check_layer(w, tokens=None, seed_tokens=None, device="cuda"):
-    """Full parity check of workload w; returns a report dict."""
+def stratified_tokens(g, k, stride=64):
+    """Tokens whose permuted rows cover every expert's segment at a stride of
+    ``stride`` rows, plus each segment's last row: every run of ``stride``
+    rows of every expert, and so every row tile of any tiling with tiles of
+    at least ``stride`` rows (ragged ends included), holds a checked row."""
+    off = g["expert_offsets"]
+    rows = []
+    for e in range(len(off) - 1):
+        a, b = int(off[e]), int(off[e + 1])
+        if b > a:
+            rows.extend(range(a, b, stride))
+            rows.append(b - 1)
+    rows = np.asarray(sorted(set(rows)), dtype=np.int64)
+    return np.unique(g["perm_src"][rows] // k)
+
+
+def check_end_to_end_routing(w, inp, g, report):
+    """The oracle routes from its own float64 scores; the GPU routed from its
+    fp32 scores.  Every token whose float64 selection keys leave a gap larger
+    than the larger of the near-tie threshold (1e-6) and twice the largest
+    score difference between the two paths (an affinity can move by at most
+    that much, and a selection can only flip across a gap the keys close)
+    must get the same ordered top-k; the others are listed, not failed."""
+    x64, wr64 = np64(inp["x"]), np64(inp["w_router"])
+    off = np64(inp["logit_offset"])
+    bias = inp["select_bias"].cpu().numpy().astype(np.float64) if inp["select_bias"] is not None else None
+    s_ref = O.router_logits(x64, wr64, off)
+    dmax = float(np.abs(g["logits"] - s_ref).max())
+    keys = O.selection_keys(s_ref, w.gating, bias)
+    ref_idx = O.ordered_topk(keys, w.k)
+    thr = max(O.NEAR_TIE_EPS, 2.0 * dmax)
+    near = O.near_tie_tokens(keys, w.k, eps=thr)
+    mism = (ref_idx != g["idx"]).any(axis=1)
+    bad = mism & ~near
+    assert not bad.any(), (f"float64 end-to-end routing differs on {int(bad.sum())} tokens "
+                           f"beyond the {thr:.2e} gap, e.g. {np.nonzero(bad)[0][:5]}")
+    report["e2e_gap_threshold"] = thr
+    report["e2e_listed_tokens"] = int(near.sum())
+    report["e2e_listed_mismatch"] = int((mism & near).sum())
+
+
+def check_layer(w, tokens=None, seed_tokens=None, device="cuda", stratified=None,
+                end_to_end=False):
+    """Full parity check of workload w; returns a report dict.  Track Y runs
+    on all tokens, on ``tokens``, on a seeded sample (seed_tokens = (seed,
+    n)), or with stratified = stride on the rows stratified_tokens picks."""
     inp = make_inputs(w, device)
     g = run_gpu(w, inp)
     report = {}
     check_routing(w, inp, g, report)
-    if tokens is None and seed_tokens is not None:
+    if end_to_end:
+        check_end_to_end_routing(w, inp, g, report)
+    if tokens is None and stratified is not None:
+        tokens = stratified_tokens(g, w.k, stratified)
+    elif tokens is None and seed_tokens is not None:
         rng = np.random.default_rng(seed_tokens[0])
         tokens = np.sort(rng.choice(w.T, size=min(seed_tokens[1], w.T), replace=False))
+    if tokens is not None:
+        report["checked_tokens"] = int(len(tokens))
     report["max_rel_err"] = check_outputs(w, inp, g, tokens)
     # bitwise determinism of a second run
     y2 = B.forward_inputs(B.config_for(w), inp)[0]

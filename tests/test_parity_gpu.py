@@ -53,9 +53,13 @@ def test_small_workload_all_tokens(name):
     say(f"[parity] {name} ok {json.dumps(rep)}")
 
 
+# Full-size workloads: the prefill shapes check Track Y on stratified rows
+# (every 64 permuted rows of every expert plus its last row, so every row
+# tile and ragged tail is compared) and also compare the oracle's own float64
+# routing end to end; the others a seeded token sample (None: every token).
 FULL_SAMPLE = {"toy_fp32": None, "switch_bf16": 96, "switch_softmax_full_bf16": 96,
-               "mixtral_bf16": 48,
-               "deepseek_v3_bf16": 12, "gptoss_prefill_bf16": 48, "gptoss_decode_bf16": None}
+               "gptoss_decode_bf16": None}
+FULL_STRATIFIED = ("mixtral_bf16", "deepseek_v3_bf16", "gptoss_prefill_bf16")
 
 
 @pytest.mark.parametrize("name", list(FULL_SAMPLE))
@@ -64,6 +68,15 @@ def test_full_workload_sampled(name):
     n = FULL_SAMPLE[name]
     say(f"[parity-full] {name} T={w.T} d={w.d} E={w.E} k={w.k} d_ff={w.d_ff} sample={n}")
     rep = MC.check_layer(w, seed_tokens=None if n is None else (7, n))
+    say(f"[parity-full] {name} ok {json.dumps(rep)}")
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("name", FULL_STRATIFIED)
+def test_full_prefill_every_row_tile_and_end_to_end_routing(name):
+    w = W[name]
+    say(f"[parity-full] {name} T={w.T} d={w.d} E={w.E} k={w.k} d_ff={w.d_ff} stratified 64")
+    rep = MC.check_layer(w, stratified=64, end_to_end=True)
     say(f"[parity-full] {name} ok {json.dumps(rep)}")
     torch.cuda.empty_cache()
 
