@@ -599,8 +599,8 @@ __global__ __launch_bounds__(64 * GB_NW) void bwd_gemm_kernel(GemmArgs a) {
 }
 
 // ---------------------------------------------------------------- gate step
-// One wave per token.  dg_j = <dy_t, O_j> over the kept slots (O in bf16, or
-// the two fp32 K parts of a split second GEMM), dO_j = bf16(g_j dy_t) on the
+// One wave per token.  dg_j = <dy_t, O_j> over the kept slots (O the bf16
+// expert outputs the forward combined), dO_j = bf16(g_j dy_t) on the
 // slot's permuted row, then the score gradient of the token (dense [E]).
 __global__ __launch_bounds__(256) void gate_bwd_kernel(GateBwdArgs a) {
   const int lane = threadIdx.x & 63;
@@ -634,25 +634,11 @@ __global__ __launch_bounds__(256) void gate_bwd_kernel(GateBwdArgs a) {
         yf[2 * q + 1] = bf16_to_f32(y8[q] >> 16);
       }
       float of[8];
-      if (a.part) {
-        const float* p0 = a.part + (int64_t)r * d + c * 8;
-        const float* p1 = p0 + a.part_stride;
-        const f32x4_t a0 = *reinterpret_cast<const f32x4_t*>(p0);
-        const f32x4_t a1 = *reinterpret_cast<const f32x4_t*>(p0 + 4);
-        const f32x4_t b0 = *reinterpret_cast<const f32x4_t*>(p1);
-        const f32x4_t b1 = *reinterpret_cast<const f32x4_t*>(p1 + 4);
+      const u32x4_t o8 = *reinterpret_cast<const u32x4_t*>(a.eout + (int64_t)r * d + c * 8);
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          of[q] = a0[q] + b0[q];
-          of[4 + q] = a1[q] + b1[q];
-        }
-      } else {
-        const u32x4_t o8 = *reinterpret_cast<const u32x4_t*>(a.eout + (int64_t)r * d + c * 8);
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          of[2 * q] = bf16_to_f32(o8[q] & 0xffffu);
-          of[2 * q + 1] = bf16_to_f32(o8[q] >> 16);
-        }
+      for (int q = 0; q < 4; ++q) {
+        of[2 * q] = bf16_to_f32(o8[q] & 0xffffu);
+        of[2 * q + 1] = bf16_to_f32(o8[q] >> 16);
       }
       u32x4_t w;
 #pragma unroll

@@ -19,7 +19,7 @@ namespace {
 // the sums so that each wave waits for memory once.
 constexpr int CB_COLS = 512;
 
-template <int KMAX, bool SPLIT>
+template <int KMAX>
 __global__ __launch_bounds__(256) void combine_bf16_kernel(CombineArgs a) {
   const int ncg = (a.d + CB_COLS - 1) / CB_COLS;
   const int64_t wid = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -34,39 +34,13 @@ __global__ __launch_bounds__(256) void combine_bf16_kernel(CombineArgs a) {
   u32x4_t v[KMAX];
   float g[KMAX];
   bool on[KMAX];
-  int spj[KMAX];
 #pragma unroll
   for (int j = 0; j < KMAX; ++j) {
     const int sp = j < k ? a.slot_pos[t * k + j] : -1;
-    spj[j] = sp;
     on[j] = sp >= 0;
     g[j] = on[j] ? a.gate[t * k + j] : 0.f;
-    if (!SPLIT)
-      v[j] = on[j] ? *reinterpret_cast<const u32x4_t*>(eo + (int64_t)sp * d + c)
-                   : u32x4_t{0u, 0u, 0u, 0u};
-  }
-  if (SPLIT) {
-    // expert output = bf16(part 0 + part 1), rounded where the unsplit GEMM
-    // rounds its accumulator
-    f32x4_t p[KMAX][4];
-#pragma unroll
-    for (int j = 0; j < KMAX; ++j) {
-      const float* p0 = a.part + (int64_t)(on[j] ? spj[j] : 0) * d + c;
-      const float* p1 = p0 + a.part_stride;
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        p[j][h] = on[j] ? reinterpret_cast<const f32x4_t*>(p0)[h] : f32x4_t{0.f, 0.f, 0.f, 0.f};
-        p[j][2 + h] = on[j] ? reinterpret_cast<const f32x4_t*>(p1)[h] : f32x4_t{0.f, 0.f, 0.f, 0.f};
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < KMAX; ++j) {
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int h = q >> 1, e0 = (q & 1) * 2;
-        v[j][q] = pack_bf16x2(p[j][h][e0] + p[j][2 + h][e0], p[j][h][e0 + 1] + p[j][2 + h][e0 + 1]);
-      }
-    }
+    v[j] = on[j] ? *reinterpret_cast<const u32x4_t*>(eo + (int64_t)sp * d + c)
+                 : u32x4_t{0u, 0u, 0u, 0u};
   }
   float acc[8];
 #pragma unroll
@@ -136,17 +110,10 @@ hipError_t launch_combine(const CombineArgs& a, hipStream_t s) {
   const unsigned grid = (unsigned)((a.T * ncg + 3) / 4);
   const int64_t prof_rec = prof_before("combine", s);
   if (a.dtype == MOE_BF16) {
-    if (a.part) {
-      if (a.k <= 2) combine_bf16_kernel<2, true><<<grid, 256, 0, s>>>(a);
-      else if (a.k <= 4) combine_bf16_kernel<4, true><<<grid, 256, 0, s>>>(a);
-      else if (a.k <= 8) combine_bf16_kernel<8, true><<<grid, 256, 0, s>>>(a);
-      else combine_bf16_kernel<16, true><<<grid, 256, 0, s>>>(a);
-    } else {
-      if (a.k <= 2) combine_bf16_kernel<2, false><<<grid, 256, 0, s>>>(a);
-      else if (a.k <= 4) combine_bf16_kernel<4, false><<<grid, 256, 0, s>>>(a);
-      else if (a.k <= 8) combine_bf16_kernel<8, false><<<grid, 256, 0, s>>>(a);
-      else combine_bf16_kernel<16, false><<<grid, 256, 0, s>>>(a);
-    }
+    if (a.k <= 2) combine_bf16_kernel<2><<<grid, 256, 0, s>>>(a);
+    else if (a.k <= 4) combine_bf16_kernel<4><<<grid, 256, 0, s>>>(a);
+    else if (a.k <= 8) combine_bf16_kernel<8><<<grid, 256, 0, s>>>(a);
+    else combine_bf16_kernel<16><<<grid, 256, 0, s>>>(a);
   }
   else
     combine_f32_kernel<<<grid, 256, 0, s>>>(a);

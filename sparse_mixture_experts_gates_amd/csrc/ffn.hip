@@ -49,20 +49,25 @@ struct KArgs {
   const PlanEntry* plan;
   const int32_t* count;
   unsigned long long* queues;   // 8 per-XCD queue words (persistent launches)
+  int32_t* tail;                // claims from the tail queue (header int 2)
   const int32_t* a_rows;  // optional row indirection for A (row gather folded in)
   int a_div;
   int K, N;
   int64_t a_seg_rows, c_seg_rows;  // extra row offset per segment (shared experts)
-  int split;                       // K halves (plan entries carry the half)
-  float* part;                     // split: fp32 partials [split][rows, N]
-  int64_t part_stride;             // rows * N
+  float* part;                     // split: fp32 partial tiles [kTailParts][256][256]
   uint16_t* save1;                 // SAVE: pre-activations (W1 x), laid out like C
   uint16_t* save2;                 // SAVE, SwiGLU: W3 x
 };
 
 // A plan entry's column field: the column tile in the low 24 bits, the K
-// part of a split pass above them.
+// part of a split entry in bits 24-27 and, for a tail entry, its number of K
+// parts in bits 28-31 (0: one).
 constexpr int kNtBits = 24;
+__device__ __forceinline__ int entry_part(int nt) { return (int)(((unsigned)nt >> 24) & 15u); }
+__device__ __forceinline__ int entry_parts(int nt) {
+  const int n = (int)((unsigned)nt >> 28);
+  return n ? n : 1;
+}
 
 // Plan: one workgroup; G <= 1024 segments (offsets seg[G+1], or G dense
 // segments of dense_rows rows).
@@ -96,14 +101,20 @@ __device__ __forceinline__ int xcd_start(int x, int V) {
 }
 
 // Persistent launches: a block on XCD x takes the next entry of XCD x's
-// queue, and once that is drained, steals from the other XCDs' queues.  A
+// queue, and once that is drained, the next entry of the tail queue (when
+// the plan has one), then steals from the other XCDs' queues.  A
 // queue word holds the entries taken from its front (low 32 bits, by its own
 // XCD) and from its back (high 32 bits, by thieves): one atomic add claims
 // an entry from either end, and the entry exists while front + back < len.
 // Thieves take the last entries, whose weight slabs the owner XCD has not
 // fetched yet, so a slab is not pulled into two L2s.  Returns -1 when every
 // queue is drained.  Called by one lane.
-__device__ int next_tile(unsigned long long* queues, int V, int x) {
+__device__ int next_tile(unsigned long long* queues, int V, int x, int32_t* tail, int ntail) {
+  // the tail queue (K parts of the partial last round) before stealing
+  if (ntail > 0 && __hip_atomic_load(tail, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < ntail) {
+    const int t = atomicAdd(tail, 1);
+    if (t < ntail) return V + t;
+  }
 #pragma unroll 1
   for (int s = 0; s < 8; ++s) {
     const int y = (x + s) & 7;
@@ -168,6 +179,9 @@ void ffn_bf16_kernel(KArgs a) {
   int* const tile_slot = reinterpret_cast<int*>(ring + (SLOT_IN_RING ? 0 : LDS_ELEMS));
 
   const int V = a.count[0];
+  // persistent launches: entries [0, Vq) in the per-XCD queues, the rest
+  // (K parts of tail tiles) in the tail queue
+  const int Vq = PERSIST ? a.count[1] : V;
   const int P = blockIdx.x;
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
@@ -177,7 +191,7 @@ void ffn_bf16_kernel(KArgs a) {
   // each epilogue, so the atomic's round trip hides behind the stores (a
   // claim made earlier would hold an entry that an idle block could take)
   const int xq = P & 7;
-  const int own0 = xcd_start(xq, V), own_len = xcd_start(xq + 1, V) - own0;
+  const int own0 = xcd_start(xq, Vq), own_len = xcd_start(xq + 1, Vq) - own0;
   unsigned long long claimed = ~0ull;
   for (int it = 0;; ++it) {
   int e;
@@ -188,7 +202,7 @@ void ffn_bf16_kernel(KArgs a) {
         const unsigned f = (unsigned)claimed, b = (unsigned)(claimed >> 32);
         if (f + b < (unsigned)own_len) nxt = own0 + (int)f;
       }
-      tile_slot[it & 1] = nxt >= 0 ? nxt : next_tile(a.queues, V, xq);
+      tile_slot[it & 1] = nxt >= 0 ? nxt : next_tile(a.queues, Vq, xq, a.tail, V - Vq);
     }
     // also: every wave is done with the previous tile's LDS (its loads have
     // landed before the epilogue; its stores need not wait: outstanding
@@ -207,15 +221,16 @@ void ffn_bf16_kernel(KArgs a) {
   int lane = tid & 63;
   asm volatile("" : "+v"(lane));
   const PlanEntry pe = a.plan[e];
-  const int ks = SPLIT ? pe.nt >> kNtBits : 0;
+  const int ks = SPLIT ? entry_part(pe.nt) : 0;
+  const int nks = SPLIT ? entry_parts(pe.nt) : 1;
   const int n0 = (pe.nt & ((1 << kNtBits) - 1)) * BNOUT;
   const int64_t arow0 = (int64_t)pe.g * a.a_seg_rows;
   const int64_t wbase = (int64_t)pe.g * N * K;
 
-  // K slabs of this entry: all of them, or part ks of a split pass
+  // K slabs of this entry: all of them, or part ks of nks (a tail entry)
   const int nk_all = K / BK;
-  const int kb0 = SPLIT ? (int)((int64_t)nk_all * ks / a.split) : 0;
-  const int nk = SPLIT ? (int)((int64_t)nk_all * (ks + 1) / a.split) - kb0 : nk_all;
+  const int kb0 = SPLIT ? (int)((int64_t)nk_all * ks / nks) : 0;
+  const int nk = SPLIT ? (int)((int64_t)nk_all * (ks + 1) / nks) - kb0 : nk_all;
   // this lane's source (row, logical chunk) for each 8-row group the wave
   // loads: token groups first (rows past the segment end clamped to its last
   // row), then weight groups
@@ -471,11 +486,16 @@ void ffn_bf16_kernel(KArgs a) {
         for (int q = 0; q < 4; ++q) v[q] = act1<MODE>(acc[i][j][q]);
       }
       if constexpr (SPLIT) {
-        // split pass: the fp32 partial of part ks (added, then rounded, by
-        // whoever consumes the pass's output)
-        float* prow = a.part + ks * a.part_stride + (crow0 + r) * (int64_t)N;
-        if (row_ok && col < N) *reinterpret_cast<f32x4_t*>(prow + col) = f32x4_t{v[0], v[1], v[2], v[3]};
-        continue;
+        if (nks > 1) {
+          // a tail entry: the fp32 partial of part ks in its tile's slot
+          // (added in order and rounded by the tail reduce)
+          // tail entries are listed tile by tile, part by part: e - Vq is
+          // the entry's partial-tile slot
+          float* prow = a.part + ((int64_t)(e - Vq) * 256 + (r - pe.m0)) * 256;
+          if (row_ok && col < N)
+            *reinterpret_cast<f32x4_t*>(prow + (col - n0)) = f32x4_t{v[0], v[1], v[2], v[3]};
+          continue;
+        }
       }
       uint2 pk;
       pk.x = pack_bf16x2(v[0], v[1]);
@@ -624,22 +644,25 @@ void launch_bf16(int mode, unsigned grid, const KArgs& k, hipStream_t s) {
 size_t ffn_plan_bytes(int64_t max_rows, int G, int N, bool small, int dtype, int split) {
   size_t best = 0;
   for (int mode = 0; mode < 4; ++mode) {
-    const size_t b = kPlanHeader + 16 * (size_t)split *
-                     (size_t)max_entries(max_rows, G, N, pick_shape(dtype, small, mode, max_rows, N));
+    // a tail split adds at most kTailParts entries (the tail tiles' parts)
+    const size_t b = kPlanHeader + 16 * ((size_t)max_entries(max_rows, G, N,
+                                                             pick_shape(dtype, small, mode,
+                                                                        max_rows, N)) +
+                                         (split > 1 ? (size_t)kTailParts : 0));
     if (b > best) best = b;
   }
   return (best + 255) / 256 * 256;
 }
 
-// Two K parts for a second expert GEMM (plain mode) that has fewer than
-// three rounds of 256 x 256 tiles and a long K: its few, long tiles would
-// otherwise leave most CUs idle in the last round.  The parts are added by
-// the consumer of the pass's output in a fixed order.
+// Tail split for a routed second expert GEMM (plain mode) on 256 x 256
+// tiles with a long K and only a few rounds of tiles: the tiles of its
+// partial last round run in K parts, so that round keeps every CU busy (the
+// plan kernel picks the parts from the real tile count).
 int ffn_split(int64_t max_rows, int G, int N, int K, bool small, int dtype) {
   if (dtype != MOE_BF16 || small) return 1;
   const Shape sh = pick_shape(dtype, false, MODE_PLAIN, max_rows, N);
   if (sh.id != 2 || K / BK < 64) return 1;
-  return max_entries(max_rows, G, N, sh) < 3 * kCUs ? 2 : 1;
+  return max_entries(max_rows, G, N, sh) < 8 * kCUs ? 2 : 1;
 }
 
 namespace {
@@ -657,7 +680,12 @@ bool ffn_plan_spec(const FfnPassArgs& p1, const FfnPassArgs& p2, PlanSpec* ps) {
   ps->BM = sh1.BM;
   ps->NT = pass_nt(p1);
   ps->NT2 = pass_nt(p2);
-  ps->S2 = p2.split > 1 ? p2.split : 1;
+  ps->S2 = 1;
+  ps->tail_cus = 0;
+  if (p2.split > 1) {
+    const int cus = cu_count();
+    ps->tail_cus = cus < kTailParts ? cus : kTailParts;
+  }
   ps->plan = static_cast<int32_t*>(p1.plan);
   ps->plan2 = static_cast<int32_t*>(p2.plan);
   ps->balanced = 1;
@@ -674,7 +702,7 @@ hipError_t launch_plan_kernel(const int32_t* seg, int G, int64_t dense_rows, con
 }
 
 hipError_t launch_ffn_plans(const FfnPassArgs& p1, const FfnPassArgs& p2, hipStream_t s) {
-  PlanSpec ps;
+  PlanSpec ps{};
   if (!ffn_plan_spec(p1, p2, &ps)) {
     const Shape sh1 = pick_shape(p1.dtype, p1.small, p1.mode, p1.max_rows, p1.N);
     return max_entries(p1.max_rows, p1.G, p1.N, sh1) == 0 ? hipSuccess : hipErrorInvalidValue;
@@ -689,7 +717,7 @@ hipError_t launch_ffn_pass(const FfnPassArgs& p, hipStream_t s) {
   const Shape sh = pick_shape(p.dtype, p.small, p.mode, p.max_rows, p.N);
   const int split = p.split > 1 ? p.split : 1;
   if (split > 1 && (sh.id != 2 || p.mode != MODE_PLAIN || !p.part)) return hipErrorInvalidValue;
-  const int64_t grid = max_entries(p.max_rows, p.G, p.N, sh) * split;
+  const int64_t grid = max_entries(p.max_rows, p.G, p.N, sh) + (split > 1 ? kTailParts : 0);
   if (grid == 0) return hipSuccess;
   int32_t* count = static_cast<int32_t*>(p.plan);
   PlanEntry* plan = reinterpret_cast<PlanEntry*>(static_cast<char*>(p.plan) + kPlanHeader);
@@ -707,9 +735,8 @@ hipError_t launch_ffn_pass(const FfnPassArgs& p, hipStream_t s) {
   k.N = p.N;
   k.a_seg_rows = p.a_seg_rows;
   k.c_seg_rows = p.c_seg_rows;
-  k.split = split;
+  k.tail = count + 2;
   k.part = p.part;
-  k.part_stride = p.max_rows * (int64_t)p.N;
   k.save1 = static_cast<uint16_t*>(p.save1);
   k.save2 = static_cast<uint16_t*>(p.save2);
   if (k.save1 && (p.dtype != MOE_BF16 || p.mode == MODE_PLAIN || split > 1 ||
@@ -747,15 +774,13 @@ hipError_t launch_ffn_pass(const FfnPassArgs& p, hipStream_t s) {
     // With at least two rounds of tiles: one persistent block per CU (the
     // LDS ring fills a CU).  Fewer, short tiles do not repay the queue.
     const int cus = cu_count();
-    if (grid >= 2 * (int64_t)cus) {
+    if (split > 1) {   // the tail queue needs the persistent launch
+      ffn_bf16_kernel<256, 256, 2, 4, 2, 3, MODE_PLAIN, true, true><<<(unsigned)cus, 512, 0, s>>>(k);
+    } else if (grid >= 2 * (int64_t)cus) {
       if (sh.id == 3) launch_bf16<256, 128, 4, 2, 3, 3, true>(p.mode, (unsigned)cus, k, s);
-      else if (split > 1)
-        ffn_bf16_kernel<256, 256, 2, 4, 2, 3, MODE_PLAIN, true, true><<<(unsigned)cus, 512, 0, s>>>(k);
       else launch_bf16<256, 256, 2, 4, 2, 3, true>(p.mode, (unsigned)cus, k, s);
     } else {
       if (sh.id == 3) launch_bf16<256, 128, 4, 2, 3, 3, false>(p.mode, (unsigned)grid, k, s);
-      else if (split > 1)
-        ffn_bf16_kernel<256, 256, 2, 4, 2, 2, MODE_PLAIN, false, true><<<(unsigned)grid, 512, 0, s>>>(k);
       else launch_bf16<256, 256, 2, 4, 2, 2, false>(p.mode, (unsigned)grid, k, s);
     }
   }
@@ -764,32 +789,66 @@ hipError_t launch_ffn_pass(const FfnPassArgs& p, hipStream_t s) {
 }
 
 namespace {
-// C = bf16(part 0 + part 1), eight columns per thread.
-__global__ __launch_bounds__(256) void split_reduce_kernel(const float* __restrict__ part,
-                                                           int64_t stride, uint16_t* __restrict__ C,
-                                                           int64_t n8) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= n8) return;
-  const f32x4_t* p0 = reinterpret_cast<const f32x4_t*>(part) + 2 * i;
-  const f32x4_t* p1 = reinterpret_cast<const f32x4_t*>(part + stride) + 2 * i;
-  const f32x4_t a0 = p0[0], a1 = p0[1], b0 = p1[0], b1 = p1[1];
-  u32x4_t o;
-  o[0] = pack_bf16x2(a0[0] + b0[0], a0[1] + b0[1]);
-  o[1] = pack_bf16x2(a0[2] + b0[2], a0[3] + b0[3]);
-  o[2] = pack_bf16x2(a1[0] + b1[0], a1[1] + b1[1]);
-  o[3] = pack_bf16x2(a1[2] + b1[2], a1[3] + b1[3]);
-  reinterpret_cast<u32x4_t*>(C)[i] = o;
+// The tail tiles of a split pass: C = bf16(part 0 + part 1 + ...) in part
+// order, from the fp32 partial tiles.  Workgroup (tile, 16-row strip): each
+// thread sums two 8-column chunks of its strip with all their parts' loads
+// in flight at once (the sums are latency-bound otherwise).
+constexpr int kReduceStrips = 16;   // 16-row strips of a 256-row tile
+
+__global__ __launch_bounds__(256) void tail_reduce_kernel(const int32_t* __restrict__ count,
+                                                          const PlanEntry* __restrict__ plan,
+                                                          const float* __restrict__ part,
+                                                          uint16_t* __restrict__ C, int N,
+                                                          int64_t c_seg_rows) {
+  const int V = count[0], Vq = count[1], St = count[3];
+  const int ntiles = St > 1 ? (V - Vq) / St : 0;
+  const int tt = blockIdx.x / kReduceStrips, strip = blockIdx.x % kReduceStrips;
+  if (tt >= ntiles) return;
+  const PlanEntry pe = plan[Vq + tt * St];
+  const int n0 = (pe.nt & ((1 << kNtBits) - 1)) * 256;
+  const int rows = pe.m1 - pe.m0;
+  const float* base = part + (int64_t)tt * St * 65536;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int i = threadIdx.x + h * 256;               // 16 rows x 32 chunks
+    const int r = strip * 16 + (i >> 5), c = (i & 31) * 8;
+    if (r >= rows || n0 + c >= N) continue;
+    f32x4_t q[kTailMaxSplit][2];
+#pragma unroll
+    for (int p = 0; p < kTailMaxSplit; ++p) {
+      if (p < St) {
+        const f32x4_t* src = reinterpret_cast<const f32x4_t*>(base + ((int64_t)p * 256 + r) * 256 + c);
+        q[p][0] = src[0];
+        q[p][1] = src[1];
+      }
+    }
+    f32x4_t s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int p = 0; p < kTailMaxSplit; ++p) {
+      if (p < St) {
+        s0 += q[p][0];
+        s1 += q[p][1];
+      }
+    }
+    u32x4_t o;
+    o[0] = pack_bf16x2(s0[0], s0[1]);
+    o[1] = pack_bf16x2(s0[2], s0[3]);
+    o[2] = pack_bf16x2(s1[0], s1[1]);
+    o[3] = pack_bf16x2(s1[2], s1[3]);
+    *reinterpret_cast<u32x4_t*>(C + ((int64_t)pe.g * c_seg_rows + pe.m0 + r) * N + n0 + c) = o;
+  }
 }
 }  // namespace
 
-hipError_t launch_ffn_split_reduce(const FfnPassArgs& p, hipStream_t s) {
+hipError_t launch_ffn_tail_reduce(const FfnPassArgs& p, hipStream_t s) {
   if (p.split <= 1) return hipSuccess;
-  if (p.split != 2) return hipErrorInvalidValue;
-  const int64_t n8 = p.max_rows * (int64_t)p.N / 8;
-  if (n8 == 0) return hipSuccess;
-  const int64_t prof_rec = prof_before("ffn2_split_reduce", s);
-  split_reduce_kernel<<<(unsigned)((n8 + 255) / 256), 256, 0, s>>>(
-      p.part, p.max_rows * (int64_t)p.N, static_cast<uint16_t*>(p.C), n8);
+  int32_t* count = static_cast<int32_t*>(p.plan);
+  const PlanEntry* plan = reinterpret_cast<const PlanEntry*>(static_cast<char*>(p.plan) + kPlanHeader);
+  const int64_t prof_rec = prof_before("ffn2_tail_reduce", s);
+  // at most kTailParts / 2 tail tiles (each has at least two parts)
+  tail_reduce_kernel<<<kTailParts / 2 * kReduceStrips, 256, 0, s>>>(count, plan, p.part,
+                                                    static_cast<uint16_t*>(p.C), p.N,
+                                                    p.c_seg_rows);
   prof_after(prof_rec, s);
   return hipGetLastError();
 }

@@ -44,7 +44,15 @@ struct PlanSpec {
   int balanced;             // 1: a segment's rows split into equal row tiles
                             // (multiples of 16 rows, at most BM); 0: tiles of
                             // BM rows and one ragged last tile
+  int tail_cus;             // > 0: the second pass (S2 = 1) lists its whole
+                            // tiles for the per-XCD queues, and the tiles of a
+                            // partial last round over tail_cus CUs in K parts
+                            // (a shared tail queue); 0: no tail split
 };
+// Tail split of a second expert GEMM: at most this many K-part entries (and
+// fp32 partial tiles of 256 x 256 in the workspace).
+constexpr int kTailParts = 256;
+constexpr int kTailMaxSplit = 8;
 
 struct PermuteArgs {
   const int32_t* topk_idx;  // [T*k]
@@ -94,8 +102,9 @@ struct FfnPassArgs {
   void* plan;             // workspace for the tile plan
   int64_t max_rows;       // upper bound of rows over all segments (host)
   bool small;             // small-batch (decode) tile shape
-  int split;              // K parts (second GEMM only; 1 = none)
-  float* part;            // split: fp32 partials [split][max_rows, N]
+  int split;              // second GEMM only: > 1 = the partial last round of
+                          // tiles runs in K parts (see PlanSpec::tail_cus)
+  float* part;            // split: fp32 partial tiles [kTailParts][256][256]
   // first GEMM, training forward: the pre-activations in dtype, laid out like
   // C -- SwiGLU: W1 x to save1 and W3 x to save2; ReLU / GeLU: W1 x to save1
   void* save1;
@@ -106,10 +115,12 @@ size_t ffn_plan_bytes(int64_t max_rows, int G, int N, bool small, int dtype, int
 // offsets seg[G+1], or G dense segments of dense_rows rows).
 hipError_t launch_plan_kernel(const int32_t* seg, int G, int64_t dense_rows, const PlanSpec& ps,
                               hipStream_t s);
-// K parts (1 or 2) of a routed second GEMM pass of this shape.
+// 2 when a routed second GEMM pass of this shape splits the tiles of its
+// partial last round over K (decided on the device from the real tile
+// count), else 1.
 int ffn_split(int64_t max_rows, int G, int N, int K, bool small, int dtype);
-// For a split pass: C = bf16(sum of the fp32 parts) for all max_rows rows.
-hipError_t launch_ffn_split_reduce(const FfnPassArgs& p, hipStream_t s);
+// For a split pass: C = bf16(sum of the K parts, in order) on the tail tiles.
+hipError_t launch_ffn_tail_reduce(const FfnPassArgs& p, hipStream_t s);
 // The plan layout of the two passes of one expert FFN; false if there is
 // nothing to plan (no rows).
 bool ffn_plan_spec(const FfnPassArgs& p1, const FfnPassArgs& p2, PlanSpec* ps);
@@ -146,10 +157,6 @@ struct CombineArgs {
   void* y;                  // [T, d]
   int64_t T;
   int k, d, S, dtype;
-  // bf16 only: the expert outputs as two fp32 K parts of a split GEMM
-  // ([2][T*k, d], stride part_stride); expert_out is then unused
-  const float* part;
-  int64_t part_stride;
 };
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
 
@@ -199,9 +206,7 @@ hipError_t launch_bwd_gemm(const BwdGemm& b, hipStream_t s);
 
 struct GateBwdArgs {
   const uint16_t* dy;       // [T, d]
-  const uint16_t* eout;     // [T*k, d] expert outputs (bf16), or
-  const float* part;        // two fp32 K parts [2][T*k, d] (stride part_stride)
-  int64_t part_stride;
+  const uint16_t* eout;     // [T*k, d] expert outputs (bf16)
   const int32_t* slot_pos;  // [T*k]
   const int32_t* topk_idx;  // [T*k]
   const float* gate;        // [T*k]

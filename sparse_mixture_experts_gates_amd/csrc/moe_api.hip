@@ -152,8 +152,8 @@ FfnWs ffn_ws(const moe_config_t* c, int64_t T) {
   o += ffn_plan_bytes(R, c->num_experts, c->d_ff, small_batch(R), c->dtype);
   w.plan2 = o;
   o += ffn_plan_bytes(R, c->num_experts, c->d, small_batch(R), c->dtype, w.split);
-  w.part = o;
-  if (w.split > 1) o += up((size_t)w.split * R * c->d * 4);
+  w.part = o;   // fp32 partial tiles of the second GEMM's tail split
+  if (w.split > 1) o += up((size_t)kTailParts * 256 * 256 * 4);
   w.plan3 = w.plan4 = o;
   if (S) {
     o += ffn_plan_bytes((int64_t)S * T, S, c->d_ff_shared, small_batch(T), c->dtype);
@@ -421,6 +421,7 @@ moe_status_t run_ffn(const FfnPasses& f, bool routed_plans_built, hipStream_t s)
   if (!routed_plans_built && launch_ffn_plans(f.p, f.p2, s) != hipSuccess) return MOE_ERR_HIP;
   if (launch_ffn_pass(f.p, s) != hipSuccess) return MOE_ERR_HIP;
   if (launch_ffn_pass(f.p2, s) != hipSuccess) return MOE_ERR_HIP;
+  if (launch_ffn_tail_reduce(f.p2, s) != hipSuccess) return MOE_ERR_HIP;
   if (f.shared) {
     if (launch_ffn_plans(f.q, f.q2, s) != hipSuccess) return MOE_ERR_HIP;
     if (launch_ffn_pass(f.q, s) != hipSuccess) return MOE_ERR_HIP;
@@ -429,24 +430,21 @@ moe_status_t run_ffn(const FfnPasses& f, bool routed_plans_built, hipStream_t s)
   return MOE_OK;
 }
 
-// The stepwise entry point: expert_out in bf16 (a split second GEMM's parts
-// are added and rounded here; moe_forward lets the combine do it).
+// The stepwise entry point: expert_out in bf16.
 moe_status_t do_ffn(const moe_config_t* c, int64_t T, const void* x, const void* x_perm,
                     const int32_t* perm_src, const int32_t* offsets, const void* w1,
                     const void* w3, const void* w2, const void* ws1, const void* ws3,
                     const void* ws2, void* eout, void* sout, void* ws, hipStream_t s) {
   const FfnPasses f =
       ffn_passes(c, T, x, x_perm, perm_src, offsets, w1, w3, w2, ws1, ws3, ws2, eout, sout, ws);
-  const moe_status_t st = run_ffn(f, false, s);
-  if (st != MOE_OK) return st;
-  return hip_status(launch_ffn_split_reduce(f.p2, s));
+  return run_ffn(f, false, s);
 }
 
 moe_status_t do_combine(const moe_config_t* c, int64_t T, const void* eout,
                         const int32_t* slot_pos, const float* gate, const void* sout, void* y,
-                        hipStream_t s, const float* part = nullptr, int64_t part_stride = 0) {
+                        hipStream_t s) {
   CombineArgs a{eout, slot_pos, gate, sout, y, T, c->top_k, c->d,
-                sout ? c->num_shared : 0, c->dtype, part, part_stride};
+                sout ? c->num_shared : 0, c->dtype};
   return hip_status(launch_combine(a, s));
 }
 
@@ -528,7 +526,7 @@ moe_status_t forward_impl(const moe_config_t* cfg, int64_t T, const void* x,
   // workgroup (small batches), which saves the plan kernel's launch
   const FfnPasses passes = ffn_passes(cfg, T, x, nullptr, perm_src, offsets, w1, w3, w2, ws1,
                                       ws3, ws2, eout, sout, at(workspace, w.ffn));
-  PlanSpec spec;
+  PlanSpec spec{};
   const bool have_spec = ffn_plan_spec(passes.p, passes.p2, &spec);
   bool built = false;
   const RouteArgs ra = route_args(cfg, T, x, w_router, logit_offset, select_bias, nullptr, idx,
@@ -549,9 +547,6 @@ moe_status_t forward_impl(const moe_config_t* cfg, int64_t T, const void* x,
   }
   st = run_ffn(passes, built, s);
   if (st != MOE_OK) return st;
-  if (passes.p2.split > 1)   // the combine adds the second GEMM's K parts
-    return do_combine(cfg, T, eout, slot_pos, gate, sout, y, s, passes.p2.part,
-                      passes.p2.max_rows * (int64_t)passes.p2.N);
   return do_combine(cfg, T, eout, slot_pos, gate, sout, y, s);
 }
 
@@ -824,7 +819,7 @@ moe_status_t moe_forward_train(const moe_config_t* cfg, int64_t T, const void* x
   // the rows are gathered once (the weight gradients read them again)
   const FfnPasses passes = ffn_passes(cfg, T, x, x_perm, perm_src, offsets, w1, w3, w2, ws1, ws3,
                                       ws2, eout, sout, at(saved, w.ffn), &tw, saved);
-  PlanSpec spec;
+  PlanSpec spec{};
   const bool have_spec = ffn_plan_spec(passes.p, passes.p2, &spec);
   bool built = false;
   st = do_permute(cfg, T, idx, x, counts, offsets, perm_src, slot_pos, dropped, x_perm,
@@ -832,9 +827,6 @@ moe_status_t moe_forward_train(const moe_config_t* cfg, int64_t T, const void* x
   if (st != MOE_OK) return st;
   st = run_ffn(passes, built, s);
   if (st != MOE_OK) return st;
-  if (passes.p2.split > 1)
-    return do_combine(cfg, T, eout, slot_pos, gate, sout, y, s, passes.p2.part,
-                      passes.p2.max_rows * (int64_t)passes.p2.N);
   return do_combine(cfg, T, eout, slot_pos, gate, sout, y, s);
 }
 
@@ -914,12 +906,7 @@ moe_status_t moe_backward(const moe_config_t* cfg, int64_t T, const void* x, con
   GateBwdArgs ga;
   memset(&ga, 0, sizeof(ga));
   ga.dy = static_cast<const uint16_t*>(dy);
-  if (ffw.split > 1) {
-    ga.part = reinterpret_cast<const float*>(fbase + ffw.part);
-    ga.part_stride = R * (int64_t)d;
-  } else {
-    ga.eout = reinterpret_cast<const uint16_t*>(at(saved, fw.eout));
-  }
+  ga.eout = reinterpret_cast<const uint16_t*>(at(saved, fw.eout));
   ga.slot_pos = slot_pos;
   ga.topk_idx = idx;
   ga.gate = reinterpret_cast<const float*>(at(saved, fw.gate));
@@ -945,7 +932,7 @@ moe_status_t moe_backward(const moe_config_t* cfg, int64_t T, const void* x, con
     const int32_t* seg = shared ? nullptr : offsets;
     void* plan_h = at(workspace, shared ? bw.splan_h : bw.plan_h);
     void* plan_x = at(workspace, shared ? bw.splan_x : bw.plan_x);
-    PlanSpec ps;
+    PlanSpec ps{};
     ps.balanced = 0;   // the backward GEMMs store full row tiles through LDS
     ps.BM = bwd_tile_rows();
     ps.NT = (f + bwd_tile_cols() - 1) / bwd_tile_cols();

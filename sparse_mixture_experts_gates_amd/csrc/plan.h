@@ -5,7 +5,10 @@
 // tiles that share a weight slab are adjacent.  A plan buffer is a 128-byte
 // header -- the int32 entry count, then at int32 index kPlanHeads eight
 // 64-bit per-XCD queue words that the persistent GEMM claims entries with --
-// followed by the 16-byte entries.
+// followed by the 16-byte entries.  Header int32s: [0] entries, [1] entries
+// in the per-XCD queues, [2] claims from the tail queue, [3] K parts of a
+// tail entry (1 = no tail).  An entry's column field holds the column tile
+// (bits 0-23), its K part (24-27) and, for a tail entry, its K parts (28-31).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -81,6 +84,19 @@ __device__ inline void build_tile_plans(const int* start, const int* rows, int G
     if (nt_all <= 0) break;
     PlanEntry* out = reinterpret_cast<PlanEntry*>(reinterpret_cast<char*>(count) + kPlanHeader);
     const int V = MT * nt_all;
+    // tail split (second pass): the first Vq entries are whole tiles, the
+    // last V - Vq tiles (a partial round over tail_cus CUs) become St K parts
+    // each, listed tile by tile after them
+    int Vq = V, St = 1;
+    if (pass == 1 && ps.tail_cus > 0 && S == 1 && tab) {
+      const int ntail = V % ps.tail_cus;
+      int st = ntail > 0 ? ps.tail_cus / ntail : 1;
+      if (st > kTailMaxSplit) st = kTailMaxSplit;
+      if (st >= 2 && ntail * st <= kTailParts) {
+        St = st;
+        Vq = V - ntail;
+      }
+    }
     if (tab) {
       // q enumerates (row tile, column entry); L is its place in the order
       // segment, column tile, part, row tile
@@ -94,7 +110,12 @@ __device__ inline void build_tile_plans(const int* start, const int* rows, int G
         const int m0 = start[g] + mi * h;
         int m1 = m0 + h;
         if (m1 > start[g] + rows[g]) m1 = start[g] + rows[g];
-        out[L] = PlanEntry{g, m0, m1, nt | (part << 24)};
+        if (L < Vq) {
+          out[L] = PlanEntry{g, m0, m1, nt | (part << 24)};
+        } else {
+          for (int p = 0; p < St; ++p)
+            out[Vq + (L - Vq) * St + p] = PlanEntry{g, m0, m1, nt | (p << 24) | (St << 28)};
+        }
       }
     } else
     for (int L = tid; L < V; L += nthr) {
@@ -112,7 +133,14 @@ __device__ inline void build_tile_plans(const int* start, const int* rows, int G
       if (m1 > start[g] + rows[g]) m1 = start[g] + rows[g];
       out[L] = PlanEntry{g, m0, m1, nt | (part << 24)};
     }
-    if (tid == 0) count[0] = V;
+    // header: all entries, the per-XCD queues' share, the tail queue's
+    // claim counter, the tail's K parts; then the queue words
+    if (tid == 0) {
+      count[0] = Vq + (V - Vq) * St;
+      count[1] = Vq;
+      count[2] = 0;
+      count[3] = St;
+    }
     if (tid < 16) count[kPlanHeads + tid] = 0;   // queue words
   }
 }

@@ -498,7 +498,7 @@ struct RoutePermuteArgs {
   int32_t* slot_pos;
   int32_t* num_dropped;
   int32_t* kept_total;
-  PlanSpec ps;
+  PlanSpec ps{};
   int want_plans, tslot;
 };
 
