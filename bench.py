@@ -68,11 +68,15 @@ def algorithmic_work(w, counts):
                 kept=kept, active=active)
 
 
+KERNEL_SOURCES = ("ffn.hip", "common.h", "plan.h", "launch.h")
+
+
 def kernel_source_digest():
-    """sha256 of the sources the expert GEMM kernels are built from."""
+    """sha256 of the sources the expert GEMM kernels and their plans are built
+    from."""
     import hashlib
     h = hashlib.sha256()
-    for f in ("ffn.hip", "common.h"):
+    for f in KERNEL_SOURCES:
         with open(os.path.join(ROOT, "sparse_mixture_experts_gates_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()
