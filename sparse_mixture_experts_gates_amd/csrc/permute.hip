@@ -24,7 +24,7 @@ namespace moe {
 
 namespace {
 
-constexpr int CH = 1024;  // slots per chunk
+constexpr int CH = 512;   // slots per chunk
 
 
 __global__ __launch_bounds__(256) void permute_count_kernel(
@@ -54,36 +54,44 @@ __global__ __launch_bounds__(256) void permute_scan_kernel(
   const int e = threadIdx.x;
   int run = 0;
   if (e < E) {
-    int b = 0;
-    for (; b + 4 <= nb; b += 4) {
-      const int v0 = bc[(int64_t)(b + 0) * E + e];
-      const int v1 = bc[(int64_t)(b + 1) * E + e];
-      const int v2 = bc[(int64_t)(b + 2) * E + e];
-      const int v3 = bc[(int64_t)(b + 3) * E + e];
-      bc[(int64_t)(b + 0) * E + e] = run; run += v0;
-      bc[(int64_t)(b + 1) * E + e] = run; run += v1;
-      bc[(int64_t)(b + 2) * E + e] = run; run += v2;
-      bc[(int64_t)(b + 3) * E + e] = run; run += v3;
-    }
-    for (; b < nb; ++b) {
-      const int v = bc[(int64_t)b * E + e];
-      bc[(int64_t)b * E + e] = run;
-      run += v;
+    // 32 chunk counts in flight per round trip (the scan is latency-bound)
+    for (int b0 = 0; b0 < nb; b0 += 32) {
+      int v[32];
+#pragma unroll
+      for (int u = 0; u < 32; ++u) v[u] = b0 + u < nb ? bc[(int64_t)(b0 + u) * E + e] : 0;
+#pragma unroll
+      for (int u = 0; u < 32; ++u) {
+        if (b0 + u < nb) bc[(int64_t)(b0 + u) * E + e] = run;
+        run += v[u];
+      }
     }
   }
-  const int kept = (e < E) ? (cap < 0 ? run : (int)(run < cap ? run : cap)) : 0;
-  sk[e] = kept;
-  sdrop[e] = (e < E) ? run - kept : 0;
+  int kept = (e < E) ? (cap < 0 ? run : (int)(run < cap ? run : cap)) : 0;
+  int drop = (e < E) ? run - kept : 0;
+  // inclusive scans of kept and dropped over the experts: shuffles within
+  // each wave of 64, then the earlier waves' totals
+  __shared__ int wtot[2][4];
+  const int lane = e & 63, w = e >> 6;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(kept, off, 64), z = __shfl_up(drop, off, 64);
+    if (lane >= off) {
+      kept += y;
+      drop += z;
+    }
+  }
+  if (lane == 63) {
+    wtot[0][w] = kept;
+    wtot[1][w] = drop;
+  }
   __syncthreads();
-  // inclusive scans (Hillis-Steele) of kept and a sum of drops
-  for (int off = 1; off < 256; off <<= 1) {
-    const int v = e >= off ? sk[e - off] : 0;
-    const int w = e >= off ? sdrop[e - off] : 0;
-    __syncthreads();
-    sk[e] += v;
-    sdrop[e] += w;
-    __syncthreads();
+  for (int v = 0; v < w; ++v) {
+    kept += wtot[0][v];
+    drop += wtot[1][v];
   }
+  sk[e] = kept;
+  sdrop[e] = drop;
+  __syncthreads();
   if (e < E) {
     if (counts) counts[e] = run;
     offsets[e + 1] = sk[e];
@@ -111,6 +119,7 @@ __global__ __launch_bounds__(64) void permute_scatter_kernel(
   const int64_t base = (int64_t)blockIdx.x * CH;
   const int64_t total = kept_total[0];
   const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  const int nbits = expert_id_bits(E);
   for (int st = 0; st < CH / 64; ++st) {
     const int64_t a = base + st * 64 + lane;
     const int sa = a < n ? slot_of((int)a, tslot, k) : 0;   // physical slot
@@ -120,13 +129,7 @@ __global__ __launch_bounds__(64) void permute_scatter_kernel(
       e = idx[sa];
       valid = (e >= 0 && e < E);
     }
-    uint64_t peers = __ballot(valid);
-#pragma unroll
-    for (int b = 0; b < 8; ++b) {
-      const bool bit = (e >> b) & 1;
-      const uint64_t bb = __ballot(bit);
-      peers &= bit ? bb : ~bb;
-    }
+    const uint64_t peers = expert_peers(e, valid, nbits);
     int r = 0;
     if (valid) r = run[e] + __popcll(peers & lt);
     __syncthreads();  // every lane has read run[] before the leaders advance it

@@ -32,10 +32,22 @@ constexpr int FUSED_MAX = 8192;
 constexpr int FUSED_WAVES = 16;
 constexpr int FUSED_IT = FUSED_MAX / (FUSED_WAVES * 64);   // 64-slot groups per wave, at most
 
-__device__ __forceinline__ uint64_t expert_peers(int e, bool valid) {
+// Bits that tell expert ids 0 .. E-1 apart (E <= 256).
+__host__ __device__ inline int expert_id_bits(int E) {
+  int b = 0;
+  while (b < 8 && (1 << b) < E) ++b;
+  return b;
+}
+
+// The lanes of this wave that hold a valid slot of the same expert as this
+// lane: one ballot per id bit (nbits = expert_id_bits(E); valid ids have no
+// higher bits).  Each bit costs several vector instructions per wave, so
+// only the bits E needs are tested.
+__device__ __forceinline__ uint64_t expert_peers(int e, bool valid, int nbits) {
   uint64_t peers = __ballot(valid);
 #pragma unroll
   for (int b = 0; b < 8; ++b) {
+    if (b >= nbits) break;
     const bool bit = (e >> b) & 1;
     const uint64_t bb = __ballot(bit);
     peers &= bit ? bb : ~bb;
@@ -56,6 +68,7 @@ __device__ inline void permute_one_workgroup(
   __shared__ int pmt[256];
   __shared__ int pbase[257];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int nbits = expert_id_bits(E);
   if (n <= 64) {
     // a decode batch: wave 0 alone ranks, counts, scans and places the <= 64
     // slots (lane l holds the l-th visited slot), without workgroup barriers;
@@ -65,7 +78,7 @@ __device__ inline void permute_one_workgroup(
       const int sa = lane < n ? slot_of(lane, tslot, k) : 0;
       const int e = lane < n ? idx[sa] : -1;
       const bool valid = lane < n && e >= 0 && e < E;
-      const uint64_t peers = expert_peers(e, valid);
+      const uint64_t peers = expert_peers(e, valid, nbits);
       const int rank = __popcll(peers & lt0);
       for (int x = lane; x < 256; x += 64) sk[x] = 0;
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -142,18 +155,24 @@ __device__ inline void permute_one_workgroup(
     ev[i] = (i * 64 < per && a < n) ? idx[slot_of(a, tslot, k)] : -1;
   }
   __syncthreads();
-  // pass 1: per-wave counts
+  // pass 1: per-wave counts; each group's peer mask is kept for pass 2
+  uint64_t pk[FUSED_IT];
 #pragma unroll
   for (int i = 0; i < FUSED_IT; ++i) {
+    pk[i] = 0;
     if (i * 64 >= per) break;
     const int a = lo + i * 64 + lane;
     const int e = ev[i];
     const bool valid = a < n && e >= 0 && e < E;
-    const uint64_t peers = expert_peers(e, valid);
-    if (valid && (peers & lt) == 0) run[w][e] += __popcll(peers);
+    pk[i] = expert_peers(e, valid, nbits);
+    if (valid && (pk[i] & lt) == 0) run[w][e] += __popcll(pk[i]);
   }
   __syncthreads();
-  // per expert: exclusive prefix over waves, counts, capacity
+  // per expert: exclusive prefix over waves, counts, capacity; then the
+  // inclusive scans of kept and dropped over the experts (4 waves of 64:
+  // shuffles within a wave, then the earlier waves' totals)
+  __shared__ int wtot[2][4];
+  int kept = 0, drop = 0;
   if (tid < 256) {
     const int e = tid;
     int tot = 0;
@@ -162,25 +181,32 @@ __device__ inline void permute_one_workgroup(
       run[v][e] = tot;
       tot += c;
     }
-    const int kept = e < E ? (cap < 0 ? tot : (int)(tot < cap ? tot : cap)) : 0;
-    sk[e] = kept;
-    sdrop[e] = e < E ? tot - kept : 0;
+    kept = e < E ? (cap < 0 ? tot : (int)(tot < cap ? tot : cap)) : 0;
+    drop = e < E ? tot - kept : 0;
     if (e < E && counts) counts[e] = tot;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int y = __shfl_up(kept, off, 64), z = __shfl_up(drop, off, 64);
+      if (lane >= off) {
+        kept += y;
+        drop += z;
+      }
+    }
+    if (lane == 63) {
+      wtot[0][w] = kept;
+      wtot[1][w] = drop;
+    }
   }
   __syncthreads();
-  for (int off = 1; off < 256; off <<= 1) {
-    int v = 0, u = 0;
-    if (tid < 256 && tid >= off) {
-      v = sk[tid - off];
-      u = sdrop[tid - off];
+  if (tid < 256) {
+    for (int v = 0; v < w; ++v) {
+      kept += wtot[0][v];
+      drop += wtot[1][v];
     }
-    __syncthreads();
-    if (tid < 256) {
-      sk[tid] += v;
-      sdrop[tid] += u;
-    }
-    __syncthreads();
+    sk[tid] = kept;
+    sdrop[tid] = drop;
   }
+  __syncthreads();
   if (tid < 256) soff[tid] = tid == 0 ? 0 : sk[tid - 1];
   if (tid < E) offsets[tid + 1] = sk[tid];
   if (tid == 0) {
@@ -204,7 +230,7 @@ __device__ inline void permute_one_workgroup(
     const int sa = a < n ? slot_of(a, tslot, k) : 0;   // physical slot
     const int e = ev[i];
     const bool valid = a < n && e >= 0 && e < E;
-    const uint64_t peers = expert_peers(e, valid);
+    const uint64_t peers = pk[i];
     int r = 0;
     if (valid) r = run[w][e] + __popcll(peers & lt);
     __builtin_amdgcn_wave_barrier();
