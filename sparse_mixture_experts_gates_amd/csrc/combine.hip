@@ -14,61 +14,74 @@ namespace moe {
 
 namespace {
 
-// One wave per (token, 512-column group): every lane owns 8 columns (one
-// 16-byte load per source row); the loads of all k rows are issued before
-// the sums so that each wave waits for memory once.
-constexpr int CB_COLS = 512;
+// One wave per (token, 512 NC-column group): every lane owns NC chunks of 8
+// columns, 512 columns apart (one 16-byte load per chunk and source row);
+// the loads of all k rows are issued before the sums so that each wave waits
+// for memory once.  NC is chosen so that about CB_LOADS loads per lane are in
+// flight whatever k is.
+constexpr int CB_LOADS = 8;
 
-template <int KMAX>
+template <int KMAX, int NC>
 __global__ __launch_bounds__(256) void combine_bf16_kernel(CombineArgs a) {
+  constexpr int CB_NC = NC, CB_COLS = 512 * NC;
   const int ncg = (a.d + CB_COLS - 1) / CB_COLS;
   const int64_t wid = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   const int64_t t = wid / ncg;
   if (t >= a.T) return;
   const int cg = (int)(wid - t * ncg);
   const int lane = threadIdx.x & 63, k = a.k, d = a.d;
-  const int c = cg * CB_COLS + lane * 8;
-  if (c >= d) return;
+  const int c0 = cg * CB_COLS + lane * 8;
+  if (c0 >= d) return;
   const uint16_t* eo = static_cast<const uint16_t*>(a.expert_out);
   const uint16_t* so = static_cast<const uint16_t*>(a.shared_out);
-  u32x4_t v[KMAX];
+  int sp[KMAX];
   float g[KMAX];
-  bool on[KMAX];
 #pragma unroll
   for (int j = 0; j < KMAX; ++j) {
-    const int sp = j < k ? a.slot_pos[t * k + j] : -1;
-    on[j] = sp >= 0;
-    g[j] = on[j] ? a.gate[t * k + j] : 0.f;
-    v[j] = on[j] ? *reinterpret_cast<const u32x4_t*>(eo + (int64_t)sp * d + c)
-                 : u32x4_t{0u, 0u, 0u, 0u};
+    sp[j] = j < k ? a.slot_pos[t * k + j] : -1;
+    g[j] = sp[j] >= 0 ? a.gate[t * k + j] : 0.f;
   }
-  float acc[8];
+  u32x4_t v[KMAX][CB_NC];
 #pragma unroll
-  for (int q = 0; q < 8; ++q) acc[q] = 0.f;
+  for (int j = 0; j < KMAX; ++j)
 #pragma unroll
-  for (int j = 0; j < KMAX; ++j) {
-    if (!on[j]) continue;   // dropped or absent slots add nothing
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      acc[2 * q] = fmaf(g[j], bf16_to_f32(v[j][q] & 0xffffu), acc[2 * q]);
-      acc[2 * q + 1] = fmaf(g[j], bf16_to_f32(v[j][q] >> 16), acc[2 * q + 1]);
+    for (int u = 0; u < CB_NC; ++u) {
+      const int c = c0 + u * 512;
+      v[j][u] = sp[j] >= 0 && c < d ? *reinterpret_cast<const u32x4_t*>(eo + (int64_t)sp[j] * d + c)
+                                    : u32x4_t{0u, 0u, 0u, 0u};
     }
-  }
-  for (int s = 0; s < a.S; ++s) {
-    const u32x4_t w = *reinterpret_cast<const u32x4_t*>(so + ((int64_t)s * a.T + t) * d + c);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      acc[2 * q] += bf16_to_f32(w[q] & 0xffffu);
-      acc[2 * q + 1] += bf16_to_f32(w[q] >> 16);
-    }
-  }
   uint16_t* y = static_cast<uint16_t*>(a.y);
-  u32x4_t o;
-  o[0] = pack_bf16x2(acc[0], acc[1]);
-  o[1] = pack_bf16x2(acc[2], acc[3]);
-  o[2] = pack_bf16x2(acc[4], acc[5]);
-  o[3] = pack_bf16x2(acc[6], acc[7]);
-  *reinterpret_cast<u32x4_t*>(y + t * d + c) = o;
+#pragma unroll
+  for (int u = 0; u < CB_NC; ++u) {
+    const int c = c0 + u * 512;
+    if (c >= d) break;
+    float acc[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) acc[q] = 0.f;
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j) {
+      if (sp[j] < 0) continue;   // dropped or absent slots add nothing
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        acc[2 * q] = fmaf(g[j], bf16_to_f32(v[j][u][q] & 0xffffu), acc[2 * q]);
+        acc[2 * q + 1] = fmaf(g[j], bf16_to_f32(v[j][u][q] >> 16), acc[2 * q + 1]);
+      }
+    }
+    for (int s = 0; s < a.S; ++s) {
+      const u32x4_t w = *reinterpret_cast<const u32x4_t*>(so + ((int64_t)s * a.T + t) * d + c);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        acc[2 * q] += bf16_to_f32(w[q] & 0xffffu);
+        acc[2 * q + 1] += bf16_to_f32(w[q] >> 16);
+      }
+    }
+    u32x4_t o;
+    o[0] = pack_bf16x2(acc[0], acc[1]);
+    o[1] = pack_bf16x2(acc[2], acc[3]);
+    o[2] = pack_bf16x2(acc[4], acc[5]);
+    o[3] = pack_bf16x2(acc[6], acc[7]);
+    *reinterpret_cast<u32x4_t*>(y + t * d + c) = o;
+  }
 }
 
 // fp32: 4 columns per lane, 256 per wave.
@@ -104,19 +117,30 @@ __global__ __launch_bounds__(256) void combine_f32_kernel(CombineArgs a) {
 
 }  // namespace
 
+namespace {
+constexpr int cb_nc(int kmax) {
+  return CB_LOADS / kmax < 1 ? 1 : (CB_LOADS / kmax > 4 ? 4 : CB_LOADS / kmax);
+}
+template <int KMAX>
+void launch_combine_bf16(const CombineArgs& a, hipStream_t s) {
+  constexpr int NC = cb_nc(KMAX);
+  const int64_t ncg = (a.d + 512 * NC - 1) / (512 * NC);
+  combine_bf16_kernel<KMAX, NC><<<(unsigned)((a.T * ncg + 3) / 4), 256, 0, s>>>(a);
+}
+}  // namespace
+
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s) {
   if (a.T == 0) return hipSuccess;
-  const int64_t ncg = a.dtype == MOE_BF16 ? (a.d + CB_COLS - 1) / CB_COLS : (a.d + 255) / 256;
-  const unsigned grid = (unsigned)((a.T * ncg + 3) / 4);
   const int64_t prof_rec = prof_before("combine", s);
   if (a.dtype == MOE_BF16) {
-    if (a.k <= 2) combine_bf16_kernel<2><<<grid, 256, 0, s>>>(a);
-    else if (a.k <= 4) combine_bf16_kernel<4><<<grid, 256, 0, s>>>(a);
-    else if (a.k <= 8) combine_bf16_kernel<8><<<grid, 256, 0, s>>>(a);
-    else combine_bf16_kernel<16><<<grid, 256, 0, s>>>(a);
+    if (a.k <= 2) launch_combine_bf16<2>(a, s);
+    else if (a.k <= 4) launch_combine_bf16<4>(a, s);
+    else if (a.k <= 8) launch_combine_bf16<8>(a, s);
+    else launch_combine_bf16<16>(a, s);
+  } else {
+    const int64_t ncg = (a.d + 255) / 256;
+    combine_f32_kernel<<<(unsigned)((a.T * ncg + 3) / 4), 256, 0, s>>>(a);
   }
-  else
-    combine_f32_kernel<<<grid, 256, 0, s>>>(a);
   prof_after(prof_rec, s);
   return hipGetLastError();
 }
