@@ -103,6 +103,16 @@ EDGES = {
                                 d_ff_shared=64, E=16, k=4),
     "decode_threshold_in": small(T=32, k=2),      # 64 rows: small-batch path
     "decode_threshold_out": small(T=33, k=2),     # 66 rows: prefill path
+    # decode batches run the second GEMM and the combine in one kernel: with
+    # shared experts and drops, an expert with more than 16 rows, 256
+    # experts, every slot dropped, and a K that is not a whole number of
+    # the kernel's 8-step load batches
+    "decode_shared_capacity": small(T=12, k=4, E=16, num_shared=2, d_ff_shared=64,
+                                    capacity_factor=0.5, offset=("normal", 0.5)),
+    "decode_rows_over_16": small(T=64, k=1, E=4, offset=("normal", 2.0)),
+    "decode_max_E_k": small(E=256, k=16, T=4, d=64, d_ff=64),
+    "decode_all_dropped": small(T=16, k=2, capacity_factor=1e-6),
+    "decode_relu_odd_batches": small(T=8, k=2, act="relu", d=320, d_ff=1088),
     "max_E_k": small(E=256, k=16, T=300, d=64, d_ff=64),
     "ragged_many_tiles": small(T=1111, d=320, d_ff=704, E=5, k=3),
     # enough tiles for the persistent prefill GEMMs (256 x 256 tiles in the
@@ -121,9 +131,9 @@ EDGES = {
 }
 
 
-# Larger shapes checked on a seeded token sample: a second GEMM with fewer
-# than three rounds of 256 x 256 tiles and K = 4096 runs split over K, its
-# parts added by the combine (moe_forward) or by a reduce (moe_expert_ffn).
+# Larger shapes checked on a seeded token sample: a second GEMM on 256 x 256
+# tiles with K = 4096 and a partial last round of tiles runs that round's
+# tiles in K parts, added in order by the tail reduce.
 SAMPLED_EDGES = {
     "split_k_second_gemm": small(T=4096, d=4096, E=8, k=2, d_ff=4096),
 }
