@@ -12,8 +12,9 @@
 //   dH GEMM       dH = dO . W2_e over each expert's rows; the epilogue applies
 //                 the activation's derivative with the saved pre-activations
 //                 (SwiGLU: dG = dH u silu'(g), dU = dH silu(g))
-//   dX GEMM       dX = dG . W1_e (+ dU . W3_e) over each expert's rows, in K
-//                 parts (fp32 partials) when it has few row tiles
+//   dX GEMM       dX = dG . W1_e (+ dU . W3_e) over each expert's rows; with
+//                 only a few rounds of tiles, the partial last round's tiles
+//                 in K parts (fp32 partials, added by the tail reduce)
 //   dW GEMMs      dW2_e = dO_e^T H_e, dW1_e = dG_e^T X_e, dW3_e = dU_e^T X_e:
 //                 the contraction runs over the expert's rows (ragged K)
 //   dx kernel     dx_t = sum over kept slots of dX rows + shared experts'
@@ -132,9 +133,7 @@ struct GemmArgs {
   int K, N, M;                // dH/dX: K per operand pair; N output cols; dW: M output rows
   int nk1;                    // dX: slabs of the first operand pair
   int G, MT, NT;              // dW tile grid
-  int split;                  // dX: K parts (plan entries carry the part)
-  float* part;                // dX with split > 1: fp32 partials [split][rows, N]
-  int64_t part_stride;
+  float* part;                // dX tail entries: fp32 partial tiles [kTailParts][256][256]
 };
 
 __device__ __forceinline__ float sigm(float z) { return 1.0f / (1.0f + __expf(-z)); }
@@ -244,6 +243,7 @@ __global__ __launch_bounds__(64 * GB_NW) void bwd_gemm_kernel(GemmArgs a) {
   static_assert(KSP % 4 == 0 && KSQ % 4 == 0, "swizzle must repeat across instructions");
   int lane = 0;
   int g = 0, m0 = 0, m1 = 0, n0 = 0, nk = 0, ks = 0, kb0 = 0, klen32 = 0, pk0 = 0, qk0 = 0;
+  int tail = -1;                 // dX tail entry: its partial-tile slot
   int64_t q_off[QMN ? 1 : DQ];   // K-major Q: element offset of this lane's row and chunk
   const uint16_t* pb = nullptr;  // P at k-row pk0 of slab 0
   const uint16_t* pb2 = nullptr;
@@ -294,13 +294,16 @@ __global__ __launch_bounds__(64 * GB_NW) void bwd_gemm_kernel(GemmArgs a) {
       g = pe.g;
       m0 = pe.m0;
       m1 = pe.m1;
-      n0 = (pe.nt & ((1 << 24) - 1)) * BN;
-      ks = pe.nt >> 24;
+      n0 = entry_tile(pe.nt) * BN;
+      ks = entry_part(pe.nt);
+      // a tail entry: part ks of nks, its partial tile in slot e - Vq
+      const int nks = entry_parts(pe.nt);
+      tail = nks > 1 ? e - a.count[1] : -1;
       qrow0 = (int64_t)g * a.q_row_seg;
-      // the slabs of this entry: all of them, or part ks of a split pass
+      // the slabs of this entry: all of them, or part ks of a tail entry
       const int nk_all = KIND == BG_DX && EPI == 1 ? 2 * a.nk1 : a.K / BK;
-      kb0 = (int)((int64_t)nk_all * ks / a.split);
-      nk = (int)((int64_t)nk_all * (ks + 1) / a.split) - kb0;
+      kb0 = (int)((int64_t)nk_all * ks / nks);
+      nk = (int)((int64_t)nk_all * (ks + 1) / nks) - kb0;
     }
     klen32 = (int)klen;
     pk0 = wave * (8 / NLP) + (lane >> 3) / NLP;
@@ -461,7 +464,7 @@ __global__ __launch_bounds__(64 * GB_NW) void bwd_gemm_kernel(GemmArgs a) {
 
     // this tile's output block; then (persistent) the next tile's slabs are
     // requested before the stores
-    const int cg = g, cm0 = m0, cm1 = m1, cn0 = n0, cks = ks;
+    const int cg = g, cm0 = m0, cm1 = m1, cn0 = n0, ctail = tail;
     bool more = false;
     // Weight gradients: the block leaves through LDS.  In registers lane
     // (r, c) = (lane % 16, lane / 16) holds columns 16 j + 4 c .. +3 of row r;
@@ -550,9 +553,9 @@ __global__ __launch_bounds__(64 * GB_NW) void bwd_gemm_kernel(GemmArgs a) {
         if (col >= N) continue;
         float v[4] = {acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]};
         if constexpr (KIND == BG_DX) {
-          if (a.part) {   // split pass: fp32 partial of part ks, added by the dx kernel
-            *reinterpret_cast<f32x4_t*>(a.part + cks * a.part_stride + row + col) =
-                f32x4_t{v[0], v[1], v[2], v[3]};
+          if (ctail >= 0) {   // a tail entry: its fp32 partial, added in order by the tail reduce
+            *reinterpret_cast<f32x4_t*>(a.part + ((int64_t)ctail * 256 + (m - cm0)) * 256 +
+                                        (col - cn0)) = f32x4_t{v[0], v[1], v[2], v[3]};
             continue;
           }
         }
@@ -758,19 +761,6 @@ __global__ __launch_bounds__(256) void dx_kernel(DxArgs a) {
     for (int j = 0; j < k; ++j) {
       const int r = a.slot_pos[t * k + j];
       if (r < 0) continue;
-      if (a.part) {   // the dX GEMM ran in K parts: add them in order
-        for (int p = 0; p < a.nparts; ++p) {
-          const float* src = a.part + p * a.part_stride + (int64_t)r * d + c * 8;
-          const f32x4_t u0 = *reinterpret_cast<const f32x4_t*>(src);
-          const f32x4_t u1 = *reinterpret_cast<const f32x4_t*>(src + 4);
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            acc[q] += u0[q];
-            acc[4 + q] += u1[q];
-          }
-        }
-        continue;
-      }
       const u32x4_t v = *reinterpret_cast<const u32x4_t*>(a.dxp + (int64_t)r * d + c * 8);
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
@@ -940,27 +930,16 @@ int64_t bwd_dw_blocks(int G, int M, int N) {
   return (int64_t)G * ((M + GB_BM - 1) / GB_BM) * ((N + GB_BN - 1) / GB_BN);
 }
 
-// K parts of a routed dX pass: the plan has about (ceil(rows / BM) + G / 2)
-// row tiles per column tile; with few rounds over the CUs the last round runs
-// mostly empty, so split K into S parts (fp32 partials, added by the dx
-// kernel) where ceil(V S / CUs) / S, with 3 % per extra part for the partials'
-// traffic, is smallest.  Each part keeps at least 16 slabs.
+// Tail split of a routed dX pass: the plan has about (ceil(rows / BM) + G / 2)
+// row tiles per column tile; with fewer than 8 rounds of tiles over the CUs,
+// the tiles of the partial last round run in K parts (the plan kernel picks
+// the parts from the real tile count: as many as fill the idle CUs, at most
+// 8), written as fp32 partials that the tail reduce adds in order; the other
+// tiles write bf16 rows.  K must hold at least 32 slabs.
 int bwd_dx_split(int64_t rows, int G, int N, int K_all) {
   const int64_t NT = (N + GB_BN - 1) / GB_BN;
   const int64_t V = ((rows + GB_BM - 1) / GB_BM + G / 2) * NT;
-  const int CUs = 256;
-  if (V <= 0 || V >= 4 * CUs) return 1;
-  int best = 1;
-  double best_cost = 1e30;
-  for (int S = 1; S <= 4; ++S) {
-    if (K_all / BK / S < 16) break;
-    const double cost = (double)((V * S + CUs - 1) / CUs) / S * (1.0 + 0.03 * (S - 1));
-    if (cost < best_cost * 0.999) {
-      best_cost = cost;
-      best = S;
-    }
-  }
-  return best;
+  return V > 0 && V < 8 * 256 && K_all / BK >= 32 ? 2 : 1;   // MI355X: 256 CUs
 }
 
 
@@ -1003,10 +982,8 @@ hipError_t launch_bwd_gemm(const BwdGemm& b, hipStream_t s) {
   a.N = b.N;
   a.M = b.M;
   a.nk1 = b.K / BK;
-  a.split = b.split > 1 ? b.split : 1;
-  a.part = a.split > 1 ? b.part : nullptr;
-  a.part_stride = b.part_stride;
-  if (a.split > 1 && (b.kind != BG_DX || !b.part)) return hipErrorInvalidValue;
+  a.part = b.part;
+  if (b.part && b.kind != BG_DX) return hipErrorInvalidValue;
   a.G = b.G;
   a.MT = (b.M + GB_BM - 1) / GB_BM;
   a.NT = (b.N + GB_BN - 1) / GB_BN;

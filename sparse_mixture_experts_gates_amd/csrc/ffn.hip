@@ -59,15 +59,6 @@ struct KArgs {
   uint16_t* save2;                 // SAVE, SwiGLU: W3 x
 };
 
-// A plan entry's column field: the column tile in the low 24 bits, the K
-// part of a split entry in bits 24-27 and, for a tail entry, its number of K
-// parts in bits 28-31 (0: one).
-constexpr int kNtBits = 24;
-__device__ __forceinline__ int entry_part(int nt) { return (int)(((unsigned)nt >> 24) & 15u); }
-__device__ __forceinline__ int entry_parts(int nt) {
-  const int n = (int)((unsigned)nt >> 28);
-  return n ? n : 1;
-}
 
 // Plan: one workgroup; G <= 1024 segments (offsets seg[G+1], or G dense
 // segments of dense_rows rows).
@@ -223,7 +214,7 @@ void ffn_bf16_kernel(KArgs a) {
   const PlanEntry pe = a.plan[e];
   const int ks = SPLIT ? entry_part(pe.nt) : 0;
   const int nks = SPLIT ? entry_parts(pe.nt) : 1;
-  const int n0 = (pe.nt & ((1 << kNtBits) - 1)) * BNOUT;
+  const int n0 = entry_tile(pe.nt) * BNOUT;
   const int64_t arow0 = (int64_t)pe.g * a.a_seg_rows;
   const int64_t wbase = (int64_t)pe.g * N * K;
 
@@ -523,7 +514,7 @@ __global__ __launch_bounds__(256) void ffn_f32_kernel(KArgs a) {
   const float* Wu = reinterpret_cast<const float*>(a.Wu);
   float* C = reinterpret_cast<float*>(a.C);
   const int K = a.K, N = a.N;
-  const int n0 = (pe.nt & ((1 << kNtBits) - 1)) * TB;
+  const int n0 = entry_tile(pe.nt) * TB;
   const int64_t arow0 = (int64_t)pe.g * a.a_seg_rows;
   const int64_t wbase = (int64_t)pe.g * N * K;
   const int tid = threadIdx.x, tr = tid >> 4, tc = tid & 15;
@@ -805,7 +796,7 @@ __global__ __launch_bounds__(256) void tail_reduce_kernel(const int32_t* __restr
   const int tt = blockIdx.x / kReduceStrips, strip = blockIdx.x % kReduceStrips;
   if (tt >= ntiles) return;
   const PlanEntry pe = plan[Vq + tt * St];
-  const int n0 = (pe.nt & ((1 << kNtBits) - 1)) * 256;
+  const int n0 = entry_tile(pe.nt) * 256;
   const int rows = pe.m1 - pe.m0;
   const float* base = part + (int64_t)tt * St * 65536;
 #pragma unroll
@@ -840,17 +831,22 @@ __global__ __launch_bounds__(256) void tail_reduce_kernel(const int32_t* __restr
 }
 }  // namespace
 
-hipError_t launch_ffn_tail_reduce(const FfnPassArgs& p, hipStream_t s) {
-  if (p.split <= 1) return hipSuccess;
-  int32_t* count = static_cast<int32_t*>(p.plan);
-  const PlanEntry* plan = reinterpret_cast<const PlanEntry*>(static_cast<char*>(p.plan) + kPlanHeader);
-  const int64_t prof_rec = prof_before("ffn2_tail_reduce", s);
+hipError_t launch_tail_reduce(const void* plan_buf, const float* part, void* C, int N,
+                              int64_t c_seg_rows, const char* name, hipStream_t s) {
+  const int32_t* count = static_cast<const int32_t*>(plan_buf);
+  const PlanEntry* plan =
+      reinterpret_cast<const PlanEntry*>(static_cast<const char*>(plan_buf) + kPlanHeader);
+  const int64_t prof_rec = prof_before(name, s);
   // at most kTailParts / 2 tail tiles (each has at least two parts)
-  tail_reduce_kernel<<<kTailParts / 2 * kReduceStrips, 256, 0, s>>>(count, plan, p.part,
-                                                    static_cast<uint16_t*>(p.C), p.N,
-                                                    p.c_seg_rows);
+  tail_reduce_kernel<<<kTailParts / 2 * kReduceStrips, 256, 0, s>>>(
+      count, plan, part, static_cast<uint16_t*>(C), N, c_seg_rows);
   prof_after(prof_rec, s);
   return hipGetLastError();
+}
+
+hipError_t launch_ffn_tail_reduce(const FfnPassArgs& p, hipStream_t s) {
+  if (p.split <= 1) return hipSuccess;
+  return launch_tail_reduce(p.plan, p.part, p.C, p.N, p.c_seg_rows, "ffn2_tail_reduce", s);
 }
 
 }  // namespace moe

@@ -121,6 +121,11 @@ hipError_t launch_plan_kernel(const int32_t* seg, int G, int64_t dense_rows, con
 int ffn_split(int64_t max_rows, int G, int N, int K, bool small, int dtype);
 // For a split pass: C = bf16(sum of the K parts, in order) on the tail tiles.
 hipError_t launch_ffn_tail_reduce(const FfnPassArgs& p, hipStream_t s);
+// The same for any pass on 256 x 256 tiles whose plan (header + entries) has
+// a tail split: C[g * c_seg_rows + row, col] with row pitch N, from the fp32
+// partial tiles part[kTailParts][256][256].
+hipError_t launch_tail_reduce(const void* plan, const float* part, void* C, int N,
+                              int64_t c_seg_rows, const char* name, hipStream_t s);
 // The plan layout of the two passes of one expert FFN; false if there is
 // nothing to plan (no rows).
 bool ffn_plan_spec(const FfnPassArgs& p1, const FfnPassArgs& p2, PlanSpec* ps);
@@ -193,11 +198,12 @@ struct BwdGemm {
   int64_t dense_rows;
   const void* zero;        // BG_DW: >= 64 zero bf16 elements (16-byte aligned)
   int K, N, M, G;
-  int split;               // BG_DX: K parts (the plan lists each row tile per part)
-  float* part;             // BG_DX with split > 1: fp32 partials [split][rows, N]
-  int64_t part_stride;     // rows * N
+  float* part;             // BG_DX whose plan has a tail split: the tail entries'
+                           // fp32 partial tiles [kTailParts][256][256]
 };
-// K parts of a routed dX pass of this shape (K_all = both operand pairs).
+// 2 when a routed dX pass of this shape (K_all = both operand pairs) splits
+// the tiles of its partial last round over K (the plan kernel decides from
+// the real tile count), else 1.
 int bwd_dx_split(int64_t rows, int G, int N, int K_all);
 int bwd_tile_rows();
 int bwd_tile_cols();
@@ -232,9 +238,6 @@ struct DxArgs {
   int64_t T;
   int d, k, E, S;
   int sparse_ds;            // ds is zero outside the selected experts
-  const float* part;        // or: per-row dX as nparts fp32 K parts (stride part_stride)
-  int nparts;
-  int64_t part_stride;
 };
 hipError_t launch_dx(const DxArgs& a, hipStream_t s);
 

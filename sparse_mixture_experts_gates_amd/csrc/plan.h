@@ -24,6 +24,21 @@ struct PlanEntry {
 
 constexpr int kPlanHeader = 128, kPlanHeads = 4;
 
+// The column field's parts: the column tile in the low 24 bits, the K part
+// of a split entry in bits 24-27 and, for a tail entry, its number of K parts
+// in bits 28-31 (0: one).  Bit 31 is set for 8 parts, so the field is read
+// as unsigned.
+constexpr int kNtBits = 24;
+__host__ __device__ constexpr int entry_tile(int nt) { return (int)((unsigned)nt & ((1u << kNtBits) - 1u)); }
+__host__ __device__ constexpr int entry_part(int nt) { return (int)(((unsigned)nt >> 24) & 15u); }
+__host__ __device__ constexpr int entry_parts(int nt) {
+  return (int)((unsigned)nt >> 28) ? (int)((unsigned)nt >> 28) : 1;
+}
+static_assert(entry_parts((int)(5u | (7u << 24) | (8u << 28))) == 8 &&
+                  entry_part((int)(5u | (7u << 24) | (8u << 28))) == 7 &&
+                  entry_tile((int)(5u | (7u << 24) | (8u << 28))) == 5 && entry_parts(3) == 1,
+              "plan entry column field");
+
 // Row tile height of a segment of `rows` rows: BM, or with balanced tiles
 // the rows split evenly over ceil(rows / BM) tiles and rounded up to 16.
 // Equal tiles take equal time, so the workgroups that share a weight slab

@@ -66,7 +66,8 @@ CASES = {
                                                        d_ff_shared=128, capacity_factor=0.01),
     # the largest routing the library takes: E = 256 experts, k = 16 slots
     "max_E256_k16": small(T=96, d=128, E=256, k=16, d_ff=64, gating="softmax_full"),
-    # few row tiles and a long K: the dX GEMM runs in 4 K parts (fp32 partials)
+    # few row tiles and a long K: every dX tile is in the partial last round,
+    # so each runs in K parts (fp32 partials added in order by the tail reduce)
     "split_k_dx": small(T=300, d=256, d_ff=2048),
     "split_k_dx_gelu": small(T=300, d=320, d_ff=4096, act="gelu", E=4),
     # more weight-gradient tiles than CUs, so each persistent block runs
